@@ -1,0 +1,255 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each pin takes the oracle module as an argument so that the same checks can be
+run against deliberately broken copies (tests/test_oracle_mutations.py): every
+plausible mistake in the oracle must make at least one pin fail.
+
+What fixes each pin:
+  * scipy.linalg.hadamard -- an independent library construction of Sylvester H
+  * integer identities    -- H H^T = n I, the involution H (H v) = n v
+  * brute force           -- the fast transform equals the dense product on integers
+  * closed forms          -- a signed Hadamard row rotates to sqrt(n) e_k (E3);
+                             hand-derived worked examples E1 (n = 4) and E2 (n = 4096)
+  * textbook rounding     -- round-half-even on INT4 and E2M1 ties
+  * library casts         -- torch.float8_e4m3fn on in-range values, numpy float16
+  * invariants            -- Parseval, round trip (QuaRot reviews, review 2 Summary:
+                             the RHT is invertible up to machine precision)
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.linalg
+
+
+def _check(cond, msg):
+    if not cond:
+        raise AssertionError(msg)
+
+
+def pin_sylvester_matches_scipy(O):
+    for k in range(0, 11):
+        n = 1 << k
+        _check(np.array_equal(O.sylvester(n), scipy.linalg.hadamard(n)), f"Sylvester H_{n} != scipy")
+
+
+def pin_orthogonality(O):
+    H12 = O.h12()
+    _check(H12.shape == (12, 12) and set(np.unique(H12)) == {-1, 1}, "H12 entries must be +-1")
+    _check(np.array_equal(H12 @ H12.T, 12 * np.eye(12, dtype=np.int64)), "H12 H12^T != 12 I")
+    for n in [1, 2, 4, 64, 512, 12, 24, 48, 12 * 64, 12 * 128]:
+        H = O.hadamard(n)
+        _check(np.array_equal(H @ H.T, n * np.eye(n, dtype=np.int64)), f"H_{n} H^T != n I")
+
+
+def pin_fwht_equals_dense(O):
+    rng = np.random.default_rng(11)
+    for n in [1, 2, 4, 8, 16, 32, 64, 128, 256, 1024, 4096]:
+        v = rng.integers(-1000, 1000, size=(3, n)).astype(np.float64)
+        ref = v @ scipy.linalg.hadamard(n).T.astype(np.float64)
+        _check(np.array_equal(O.fwht(v), ref), f"fwht != dense at n={n}")
+        _check(np.array_equal(O.fwht(O.fwht(v)), n * v), f"fwht involution fails at n={n}")
+    for m in [1, 2, 4, 16, 64, 256]:
+        n = 12 * m
+        v = rng.integers(-1000, 1000, size=(2, n)).astype(np.float64)
+        s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+        fast = O.rotate(v, s) * math.sqrt(n)
+        dense = (v * s) @ O.hadamard(n).T.astype(np.float64)
+        _check(np.allclose(fast, dense, rtol=0, atol=1e-9 * np.abs(dense).max()),
+               f"fast 12x rotation != dense at n={n}")
+
+
+def pin_rotate_matches_scipy_definition(O):
+    rng = np.random.default_rng(12)
+    for n in [16, 128, 1024]:
+        x = rng.standard_normal((4, n))
+        s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+        ref = scipy.linalg.hadamard(n).astype(np.float64) @ (x * s).T / math.sqrt(n)
+        _check(np.allclose(O.rotate(x, s), ref.T, rtol=0, atol=1e-12), f"rotate != H D x / sqrt(n), n={n}")
+
+
+def pin_parseval_and_roundtrip(O):
+    rng = np.random.default_rng(13)
+    for n in [16, 128, 4096, 12288, 3072]:
+        x = rng.standard_normal((3, n)) * np.exp(rng.standard_normal(n))
+        s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+        y = O.rotate(x, s)
+        _check(np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12),
+               f"Parseval fails at n={n}")
+        back = O.inverse_rotate(y, s)
+        _check(np.max(np.abs(back - x)) <= 1e-12 * np.max(np.abs(x)), f"round trip fails at n={n}")
+
+
+def _signed_row(O, n, k, s):
+    """x_j = s_j * H_n[k][j] built from one row of the oracle's dense H."""
+    f, m = O.split_width(n)
+    if f == 1:
+        i = np.arange(n)
+        a = k & i
+        pc = np.array([bin(int(t)).count("1") for t in a])
+        row = np.where(pc & 1, -1.0, 1.0)
+    else:
+        row = np.kron(O.h12()[k // m].astype(np.float64), _signed_row(O, m, k % m, np.ones(m)))
+    return row * s
+
+
+def pin_e3_closed_form(O):
+    """x = s * H_n[k] rotates to sqrt(n) e_k; its quantisation is fully determined."""
+    rng = np.random.default_rng(14)
+    for n, k in [(16, 5), (128, 77), (4096, 1234), (12288, 7000), (3072, 2049)]:
+        s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+        x = _signed_row(O, n, k, s)[None, :]
+        y = O.rotate(x, s)
+        e = np.zeros((1, n)); e[0, k] = math.sqrt(n)
+        _check(np.max(np.abs(y - e)) <= 1e-9, f"E3 rotation at n={n}")
+        # per-token INT4, fp32 scale: scale sqrt(n)/7, code 7 at k
+        q, sc, _ = O.quantize_int4(y, 0, "f32")
+        _check(sc[0, 0] == np.float32(math.sqrt(n) / 7.0), f"E3 per-token scale at n={n}")
+        _check(q[0, k] == 7 and np.count_nonzero(q) == 1, f"E3 per-token codes at n={n}")
+        # INT4 g128 fp16: only k's group has a (fp16-rounded) scale
+        if n % 128 == 0:
+            q, sc, _ = O.quantize_int4(y, 128, "f16")
+            gk = k // 128
+            _check(sc[0, gk] == np.float16(math.sqrt(n) / 7.0), f"E3 g128 scale at n={n}")
+            _check(np.count_nonzero(sc) == 1 and q[0, k] == 7 and np.count_nonzero(q) == 1,
+                   f"E3 g128 codes at n={n}")
+        # NVFP4: the block of k has E4M3 448 (0x7E) and E2M1 6 (0b0111)
+        c, bs, g, _ = O.quantize_nvfp4(y)
+        _check(g == np.float32(math.sqrt(n) / 2688.0), f"E3 tensor scale at n={n}")
+        _check(bs[0, k // 16] == 0x7E and np.count_nonzero(bs) == 1, f"E3 block scale at n={n}")
+        _check(c[0, k] == 0b0111 and np.count_nonzero(c) == 1, f"E3 E2M1 code at n={n}")
+    # n = 12288 group scale printed as a number: fp16(sqrt(12288)/7) = 15.8359375
+    _check(float(np.float16(math.sqrt(12288) / 7.0)) == 15.8359375, "fp16 rounding of 110.85/7")
+
+
+def pin_e1_worked_example(O):
+    """n = 4, s = (+,-,+,+), x = (4.25, -1.25, 5.25, 3.25):
+    s*x = (4.25, 1.25, 5.25, 3.25); H4 (s*x) = (14, 5, -3, 1); / 2 -> y = (7, 2.5, -1.5, 0.5).
+    Per-token scale 7/7 = 1; RNE codes (7, 2, -2, 0); bytes 0x27, 0x0E."""
+    x = np.array([[4.25, -1.25, 5.25, 3.25]])
+    s = np.array([1, -1, 1, 1], dtype=np.int8)
+    out = O.forward(x, s, "int4", 0, "f32")
+    _check(np.array_equal(out["y"], [[7.0, 2.5, -1.5, 0.5]]), "E1 rotation")
+    _check(out["scales"][0, 0] == 1.0, "E1 scale")
+    _check(np.array_equal(out["codes"], [[7, 2, -2, 0]]), "E1 codes")
+    _check(np.array_equal(out["packed"], [[0x27, 0x0E]]), "E1 packed bytes")
+
+
+def e2_input(n: int = 4096, seed: int = 0):
+    """E2: y* = (7, 2.5, -1.5, 0.5, 0, ...), x = s * (H y*) / sqrt(n).  For the
+    Sylvester H, (H y*)_i = 7 + 2.5 (-1)^{i0} - 1.5 (-1)^{i1} + 0.5 (-1)^{i0+i1}
+    takes the values 8.5, 2.5, 10.5, 6.5 for (i1 i0) = 00, 01, 10, 11; divided by
+    sqrt(4096) = 64 they are exact in bf16."""
+    i = np.arange(n)
+    b0 = np.where(i & 1, -1.0, 1.0)
+    b1 = np.where(i & 2, -1.0, 1.0)
+    hy = 7.0 + 2.5 * b0 - 1.5 * b1 + 0.5 * b0 * b1
+    rng = np.random.default_rng(seed)
+    s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+    return (s * hy / math.sqrt(n))[None, :], s
+
+
+def pin_e2_worked_example(O):
+    x, s = e2_input()
+    out = O.forward(x, s, "int4", 0, "f32")
+    want = np.zeros((1, 4096)); want[0, :4] = [7.0, 2.5, -1.5, 0.5]
+    _check(np.array_equal(out["y"], want), "E2 rotation")
+    _check(out["scales"][0, 0] == 1.0, "E2 scale")
+    _check(np.array_equal(out["codes"][0, :4], [7, 2, -2, 0]) and
+           np.count_nonzero(out["codes"]) == 3, "E2 codes")
+    _check(out["packed"][0, 0] == 0x27 and out["packed"][0, 1] == 0x0E and
+           not np.any(out["packed"][0, 2:]), "E2 packed row")
+
+
+def pin_int4_rounding(O):
+    y = np.array([[0.5, 1.5, 2.5, -1.5, -2.5, -0.5, 3.49, 7.0]])
+    # scale fixed to 1 through amax 7
+    q, s, _ = O.quantize_int4(y, 0, "f32")
+    _check(s[0, 0] == 1.0, "scale 7/7")
+    _check(np.array_equal(q, [[0, 2, 2, -2, -2, 0, 3, 7]]), f"RNE ties: {q}")
+    rng = np.random.default_rng(15)
+    y = rng.standard_normal((50, 256)) * np.exp(rng.standard_normal((50, 1)))
+    for group, sd in [(0, "f32"), (16, "f16"), (128, "f16"), (64, "f32")]:
+        q, s, _ = O.quantize_int4(y, group, sd)
+        _check(np.all(np.abs(q) <= 7), "-8 or beyond produced")
+        g = y.shape[1] if group == 0 else group
+        yhat = O.dequantize(O.pack_nibbles(q), s, "int4", group)
+        step = np.repeat(s.astype(np.float64), g, axis=1)
+        _check(np.all(np.abs(yhat - y) <= 0.5 * step * (1 + 1e-12)), "dequant error > s/2")
+        amax_pos = np.argmax(np.abs(y.reshape(50, -1, g)), axis=-1)
+        qa = np.take_along_axis(q.reshape(50, -1, g), amax_pos[..., None], axis=-1)
+        if sd == "f32":
+            _check(np.all(np.abs(qa) == 7), "group amax element must map to +-7")
+
+
+def pin_fp16_storage(O):
+    rng = np.random.default_rng(16)
+    a = rng.random(1000) * 1e4
+    _check(np.array_equal(O.int4_scale_store(a, "f16"), (a / 7.0).astype(np.float16)),
+           "fp16 storage != numpy float16 RNE")
+    _check(O.int4_scale_store(np.array([1e7]), "f16")[0] == np.float16(65504), "fp16 saturation")
+
+
+def pin_e2m1(O):
+    ties = {0.25: 0b0000, 0.75: 0b0010, 1.25: 0b0010, 1.75: 0b0100, 2.5: 0b0100,
+            3.5: 0b0110, 5.0: 0b0110, 7.0: 0b0111, 100.0: 0b0111, -0.1: 0b1000,
+            0.0: 0b0000, -6.0: 0b1111, 0.5: 0b0001, 2.9: 0b0101, -3.1: 0b1101}
+    for v, c in ties.items():
+        got = int(O.e2m1_encode(np.array([v]))[0])
+        _check(got == c, f"E2M1({v}) = {got:#06b}, want {c:#06b}")
+    for c in range(16):
+        if c == 8:
+            continue  # -0 decodes to 0 and re-encodes as +0
+        _check(int(O.e2m1_encode(O.e2m1_decode(np.array([c])))[0]) == c, f"E2M1 enc(dec({c}))")
+    # brute force: nearest grid point, ties to even code
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    for v in np.linspace(0, 7, 2801):
+        d = np.abs(grid - v)
+        cands = np.flatnonzero(d == d.min())
+        want = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        _check(int(O.e2m1_encode(np.array([v]))[0]) == want, f"E2M1 brute force at {v}")
+
+
+def pin_e4m3(O):
+    import torch
+    codes = np.arange(127, dtype=np.uint8)
+    _check(np.array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes), "E4M3 enc(dec(c)) != c")
+    _check(O.e4m3_decode(np.array([0x7E]))[0] == 448.0, "E4M3 max is 448")
+    _check(O.e4m3_decode(np.array([0x01]))[0] == 2.0 ** -9, "E4M3 min subnormal")
+    rng = np.random.default_rng(17)
+    vals = np.concatenate([rng.random(4000) * 448.0, np.exp(rng.uniform(-14, 6, 4000)),
+                           O.e4m3_values(),
+                           0.5 * (O.e4m3_values()[1:] + O.e4m3_values()[:-1])])
+    vals = vals[vals <= 448.0]
+    ref = torch.tensor(vals, dtype=torch.float64).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    _check(np.array_equal(O.e4m3_encode(vals), ref), "E4M3 encode != torch float8_e4m3fn")
+    _check(O.e4m3_encode(np.array([1e6]))[0] == 0x7E, "E4M3 saturates at 448")
+    _check(O.e4m3_encode(np.array([1.01 * 2.0 ** -10]))[0] == 0x01, "E4M3 subnormal rounding")
+
+
+def pin_nvfp4_invariants(O):
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((8, 256)) * np.exp(rng.standard_normal((8, 1)))
+    s = np.where(rng.random(256) < 0.5, -1, 1).astype(np.int8)
+    out = O.forward(x, s, "nvfp4", 16)
+    y = out["y"]
+    g = out["tensor_scale"]
+    _check(g == np.float32(np.max(np.abs(y)) / 2688.0), "g = fl32(amax / (6 * 448))")
+    t, j = np.unravel_index(np.argmax(np.abs(y)), y.shape)
+    _check(out["scales"][t, j // 16] == 0x7E, "amax block must take E4M3 448")
+    _check(out["codes"][t, j] & 7 == 7, "amax element must take E2M1 6")
+    yhat = O.dequantize(out["packed"], out["scales"], "nvfp4", 16, g)
+    seff = np.repeat(O.e4m3_decode(out["scales"]) * np.float64(g), 16, axis=1)
+    av = np.abs(y) / np.where(seff > 0, seff, 1)
+    half_step = np.where(av < 2, 0.25, np.where(av < 4, 0.5, 1.0))
+    half_step = np.where(av > 6, av - 6 + 0.0, half_step)
+    _check(np.all(np.abs(yhat - y) <= half_step * seff * (1 + 1e-9) + 1e-300), "E2M1 dequant bound")
+
+
+ALL_PINS = [
+    pin_sylvester_matches_scipy, pin_orthogonality, pin_fwht_equals_dense,
+    pin_rotate_matches_scipy_definition, pin_parseval_and_roundtrip, pin_e3_closed_form,
+    pin_e1_worked_example, pin_e2_worked_example, pin_int4_rounding, pin_fp16_storage,
+    pin_e2m1, pin_e4m3, pin_nvfp4_invariants,
+]

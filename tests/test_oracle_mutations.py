@@ -1,0 +1,157 @@
+"""CPU: plant plausible mistakes in copies of the oracle and require that a pin fails.
+
+This guards the pins themselves: an oracle that dropped the normalisation, applied
+the signs after H, transposed H12, used round-half-away, swapped nibbles, or got a
+format constant wrong must not pass tests/oracle_pins.py.
+"""
+import importlib.util
+import math
+import os
+
+import numpy as np
+import pytest
+
+from tests import oracle_pins as P
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "rht_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("rht_oracle_mut", ORACLE_SRC)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _no_norm(O):
+    orig = O.rotate
+    O.rotate = lambda x, signs=None: orig(x, signs) * math.sqrt(np.shape(x)[-1])
+
+
+def _signs_after(O):
+    orig_rot = O.rotate
+
+    def rot(x, signs=None):
+        y = orig_rot(x, None)
+        return y if signs is None else y * np.asarray(signs, dtype=np.float64)
+    O.rotate = rot
+
+
+def _h12_transposed_in_rotate(O):
+    """rotate() applies H12^T while the dense definition keeps H12.  (Transposing the
+    table everywhere is a different but equally valid convention, not a mistake.)"""
+    def rot(x, signs=None):
+        x = O._as_f64(x)
+        n = x.shape[-1]
+        u = x * O._signs(signs, n)
+        f, m = O.split_width(n)
+        if f == 1:
+            return O.fwht(u) / np.sqrt(n)
+        u = O.fwht(u.reshape(*u.shape[:-1], 12, m))
+        return np.einsum("ba,...bj->...aj", O.h12().astype(np.float64), u).reshape(x.shape) / np.sqrt(n)
+    O.rotate = rot
+
+
+def _h12_typo(O):
+    orig = O.h12
+
+    def bad():
+        h = orig().copy()
+        h[4, 7] *= -1
+        return h
+    O.h12 = bad
+
+
+def _round_half_away(O):
+    class NP:
+        def __getattr__(self, k):
+            return getattr(np, k)
+    fake = NP()
+    fake.rint = lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5)
+    O.np = fake
+
+
+def _swap_nibbles(O):
+    orig = O.pack_nibbles
+    O.pack_nibbles = lambda q: ((orig(q) >> 4) | (orig(q) << 4)).astype(np.uint8)
+
+
+def _scale_over_8(O):
+    orig = O.int4_scale_store
+    O.int4_scale_store = lambda a, sd: orig(np.asarray(a) * 7.0 / 8.0, sd)
+
+
+def _fp16_truncation(O):
+    orig = O.int4_scale_store
+
+    def trunc(a, sd):
+        if sd != "f16":
+            return orig(a, sd)
+        s = np.asarray(a, dtype=np.float64) / 7.0
+        r = s.astype(np.float16)
+        return np.where(r.astype(np.float64) > s, np.nextafter(r, np.float16(0)), r).astype(np.float16)
+    O.int4_scale_store = trunc
+
+
+def _nvfp4_wrong_constant(O):
+    O.nvfp4_tensor_scale = lambda y: np.float32(np.max(np.abs(np.asarray(y))) / (6.0 * 256.0))
+
+
+def _e2m1_ties_up(O):
+    orig = O.e2m1_encode
+    O.e2m1_encode = lambda v: orig(np.asarray(v, dtype=np.float64) * (1 + 1e-12))
+
+
+def _e4m3_truncate(O):
+    vals = O.e4m3_values()
+
+    def enc(x):
+        x = np.asarray(x, dtype=np.float64)
+        return np.clip(np.searchsorted(vals, x, side="right") - 1, 0, 126).astype(np.uint8)
+    O.e4m3_encode = enc
+
+
+def _fwht_skip_stage(O):
+    orig = O.fwht
+
+    def bad(v):
+        v = np.asarray(v, dtype=np.float64)
+        n = v.shape[-1]
+        if n < 4:
+            return orig(v)
+        w = v.reshape(*v.shape[:-1], n // 2, 2).copy()
+        # drop the first butterfly stage: run H over the other bits only
+        out = orig(w.swapaxes(-1, -2)).swapaxes(-1, -2)
+        return out.reshape(v.shape) if False else np.concatenate([out[..., 0], out[..., 1]], -1)
+    O.fwht = bad
+
+
+def _inverse_without_transpose(O):
+    def inv(y, signs=None):
+        y = np.asarray(y, dtype=np.float64)
+        n = y.shape[-1]
+        f, m = O.split_width(n)
+        v = y.reshape(*y.shape[:-1], f, m)
+        v = np.einsum("ab,...bj->...aj", O.h12().astype(np.float64), v) if f == 12 else v
+        u = O.fwht(v).reshape(y.shape)
+        return u * O._signs(signs, n) / np.sqrt(n)
+    O.inverse_rotate = inv
+
+
+MUTATIONS = [_no_norm, _signs_after, _h12_transposed_in_rotate, _h12_typo, _round_half_away,
+             _swap_nibbles, _scale_over_8, _fp16_truncation, _nvfp4_wrong_constant,
+             _e2m1_ties_up, _e4m3_truncate, _fwht_skip_stage, _inverse_without_transpose]
+
+
+@pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
+def test_some_pin_catches(mutate):
+    O = fresh_oracle()
+    mutate(O)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(O)
+        except Exception as e:  # noqa: BLE001 -- any failure counts as caught
+            failed.append((pin.__name__, str(e)[:80]))
+    assert failed, f"no pin caught mutation {mutate.__name__}"
