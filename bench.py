@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused randomized Hadamard rotation + 4-bit quantisation on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only]
+
+A step is one rhtq_forward call over one batch of the workload (rotation, scale,
+quantisation and packing of every row; for NVFP4 also the tensor-amax pass).
+Inputs are generated on the device before timing and rotate through enough
+buffer sets (>= 512 MB) that the 256 MB Infinity Cache cannot hold them, so the
+timed region reads HBM.  Timing uses HIP events on the stream the kernels run on.
+
+Prints ONE JSON line (rank 0).  `value` is tokens/s of the headline workload
+(2048 x 4096 bf16, per-token INT4); the d=12288, KV and NVFP4 workloads are
+reported under "also".  The CPU oracle, timed on a bounded sample on the host,
+is reported as "cpu_baseline" (a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RHT+4-bit quant tokens/s & HBM GB/s (% of peak) at d=4096 and d=12288"
+HBM_PEAK_GBS = 8000.0
+CACHE_DEFEAT_BYTES = 512 << 20
+HEADLINE = "llama_4096_int4"
+OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096"]
+KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_generic.hip",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_workload(R, torch, name, steps, warmup):
+    from workloads import WORKLOADS, bytes_per_call, generate
+    w = WORKLOADS[name]
+    x0, signs = generate(w, "cuda")
+    nbytes = bytes_per_call(w)
+    sets = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / nbytes)))
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    s_dev = torch.from_numpy(signs).to("cuda")
+    outs = []
+    for _ in range(sets):
+        packed = torch.empty((w.tokens, w.n // 2), dtype=torch.uint8, device="cuda")
+        sdt = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8}[w.scale_dtype]
+        ng = 1 if w.group == 0 else w.n // w.group
+        scales = torch.empty((w.tokens, ng), dtype=sdt, device="cuda")
+        ts = torch.zeros(1, dtype=torch.float32, device="cuda") if w.fmt == "nvfp4" else None
+        outs.append((packed, scales, ts))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        packed, scales, ts = outs[i % sets]
+        R.rhtq_forward(xs[i % sets], s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype,
+                       tensor_scale=ts, packed=packed, scales=scales, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    tokens = w.tokens * w.tokens_per_row
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": name, "tokens": int(tokens), "rows": w.tokens, "n": w.n,
+        "in_dtype": w.in_dtype, "fmt": w.fmt, "group": w.group, "scale_dtype": w.scale_dtype,
+        "buffer_sets": sets, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+        "rows_per_s": w.tokens / (ms * 1e-3), "bytes_per_call": nbytes, "achieved_gbs": gbs,
+        "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+        "launches_per_step": 4 if w.fmt == "nvfp4" else 1,
+    }
+
+
+def cpu_baseline(name, budget_s=10.0):
+    """The oracle, untouched, on the host: repeat the full workload input until the
+    budget is spent (single process; numpy's elementwise kernels use one thread)."""
+    import numpy as np
+    import oracle as O
+    from workloads import WORKLOADS, generate
+    w = WORKLOADS[name]
+    x, s = generate(w, "cpu")
+    xr = x.float().numpy().astype(np.float64)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.forward(xr, s, w.fmt, w.group, w.scale_dtype)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": reps * w.tokens * w.tokens_per_row / el, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} x full {w.tokens}x{w.n} {w.in_dtype} input of {name} "
+                      f"({el:.1f} s, numpy fp64, one process)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--only", action="store_true", help="time only --workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: rows are independent, so the path shards "
+              "by rows with no exchange; multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import randomized_hadamard_rotation_amd as R
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    head = time_workload(R, torch, args.workload, args.steps, args.warmup)
+    also = []
+    if not args.only:
+        for name in OTHERS:
+            if name != args.workload:
+                also.append(time_workload(R, torch, name, args.steps, args.warmup))
+
+    per_launch_ms = head["ms_per_step"] / head["launches_per_step"]
+    traffic = traffic_for(args.workload)
+    roofline = {"bound": "hbm", "achieved": head["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": head["achieved_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel_ms": per_launch_ms, "algorithmic_bytes_per_launch": head["bytes_per_call"]}
+    out = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": head["tokens"], "n": head["n"],
+                   "in_dtype": head["in_dtype"], "fmt": head["fmt"], "group": head["group"],
+                   "scale_dtype": head["scale_dtype"], "buffer_sets": head["buffer_sets"]},
+        "hbm_gbs": head["achieved_gbs"],
+        "roofline": roofline,
+        "also": also,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * rhtq.h -- randomized Hadamard rotation fused with 4-bit quantisation (gfx950).
+ *
+ * C ABI of librhtq.so.  What the calls compute comes from these pages:
+ *
+ *  - "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (reviews page):
+ *      review 1, Summary ..... Hadamard rotations that cannot be folded into the
+ *                              weights are applied online with the Walsh-Hadamard
+ *                              fast algorithm; combined with grouped quantisation.
+ *      review 2, Summary ..... the random Hadamard transform is invertible up to
+ *                              machine precision; activations are quantised to INT4.
+ *      review 3, Strengths ... the online Hadamard is applied to activations and to
+ *                              the KV cache.
+ *      review 3, Questions ... the Hadamard block computes Y = X H^T.
+ *      reviewer 2 follow-up .. activations use nearest rounding; per-batch RHT is
+ *                              data parallelism.
+ *  - "incoh_rotate=true degrades W4 PPL on Qwen3-8B" (KronQ issue #2), Model
+ *    Details table: 12288 = 12 x 1024 is Hadamard-compatible.
+ *  - "Methodology checks for NVFP4 W4A4 on Qwen3-8B", the NVFP4 results and the
+ *    block-Hadamard comment: E2M1 codes with E4M3 block scales, INT4-g128.
+ *
+ * Per row x of width n (rows contiguous, row-major [tokens][n]):
+ *
+ *     y = H_n * diag(s) * x / sqrt(n)          (row form Y = X D H^T / sqrt(n))
+ *
+ * H_n is the Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i&j)) for
+ * n = 2^k, and H12 (x) H_m with index j = j1*m + j2 for n = 12*m, where H12 is
+ * the Williamson array [[A,B,B,B],[-B,A,-B,B],[-B,B,A,-B],[-B,-B,B,A]] with
+ * A = J3 (all ones) and B = J3 - 2*I3.  s is a +-1 vector shared by all rows.
+ *
+ * Conventions shared by every call:
+ *  - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *    allocates nothing and keeps no state between calls.  Calls are thread-safe.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *    the call returns once it is enqueued.  A fault inside a kernel surfaces at
+ *    the caller's next synchronisation, as usual for HIP.
+ *  - Arguments are checked on the host before any HIP call; on error nothing is
+ *    enqueued and the status says why.  tokens == 0 is a valid no-op.
+ *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *  - Alignment: x, y_out, packed_out and x_out must be 16-byte aligned; scale
+ *    buffers aligned to their element size.
+ *  - Supported widths: n = 2^k with 16 <= n <= 16384, and n = 12 * 2^k with
+ *    256 <= 2^k <= 2048 (3072, 6144, 12288, 24576).
+ *  - signs: device int8 [n] with values +1 / -1, or NULL for all +1 (plain
+ *    Hadamard).  Other values are undefined behaviour.
+ */
+#ifndef RHTQ_H
+#define RHTQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RHTQ_ABI_VERSION 1
+
+/* Status codes. */
+#define RHTQ_OK           0   /* enqueued (or nothing to do)                       */
+#define RHTQ_EINVAL       1   /* bad argument: null pointer, negative size, alignment */
+#define RHTQ_EUNSUPPORTED 2   /* valid but unsupported width / format / group combo */
+#define RHTQ_EHIP         3   /* a HIP runtime call failed while enqueueing         */
+
+/* Input element types. */
+#define RHTQ_IN_BF16 0
+#define RHTQ_IN_F32  1
+
+/* 4-bit formats. */
+#define RHTQ_FMT_INT4  0      /* symmetric absmax INT4, two's complement nibbles     */
+#define RHTQ_FMT_NVFP4 1      /* E2M1 codes, E4M3 block-16 scales, fp32 tensor scale */
+
+/* Scale storage types. */
+#define RHTQ_SCALE_F32  0
+#define RHTQ_SCALE_F16  1
+#define RHTQ_SCALE_E4M3 2
+
+/* NVFP4 tensor-scale handling. */
+#define RHTQ_TENSOR_SCALE_DYNAMIC 0   /* g = fl32(max|y| / (6*448)) computed and written */
+#define RHTQ_TENSOR_SCALE_GIVEN   1   /* g is read from *tensor_scale                   */
+
+typedef void* rhtq_stream_t;  /* a hipStream_t */
+
+/* Returns RHTQ_ABI_VERSION of the loaded library. */
+int rhtq_abi_version(void);
+
+/* Static text for a status code ("ok", "invalid argument", ...). */
+const char* rhtq_status_str(int status);
+
+/* 1 if (n, fmt, group) is supported, else 0.  INT4: group 0 (one group per row) or
+ * a power of two >= 16 dividing n.  NVFP4: group 16. */
+int rhtq_supported(int32_t n, int fmt, int32_t group);
+
+/*
+ * Rotation only:  y_out[t][i] = (H_n diag(s) x[t])[i] / sqrt(n), fp32.
+ *   x       [tokens][n] bf16 (RHTQ_IN_BF16) or fp32 (RHTQ_IN_F32)
+ *   signs   [n] int8 or NULL
+ *   y_out   [tokens][n] fp32
+ * Cite: QuaRot reviews, review 1 Summary (Walsh-Hadamard algorithm) and review 2
+ * Summary (randomised, invertible); review 3 Questions (Y = X H^T).
+ */
+int rhtq_rotate(const void* x, int in_dtype, int64_t tokens, int32_t n,
+                const int8_t* signs, float* y_out, rhtq_stream_t stream);
+
+/*
+ * Rotation fused with 4-bit quantisation and nibble packing.
+ *   packed_out  [tokens][n/2] bytes: element 2k in the low nibble, 2k+1 in the high.
+ *
+ * INT4 (fmt RHTQ_FMT_INT4; QuaRot reviews, review 2 Summary and reviewer 2
+ * follow-up: INT4, nearest rounding; review 1 Summary: grouped quantisation):
+ *   group       0 (one group per row) or a power of two >= 16 dividing n
+ *   scale_dtype RHTQ_SCALE_F32 or RHTQ_SCALE_F16
+ *   scales_out  [tokens][n/group] (group 0: [tokens][1]); s = max|y|/7 over the group,
+ *               rounded to the storage type (nearest even; fp16 saturates at 65504)
+ *   codes       q = clamp(round_half_even(y / s_stored), -8, 7); a zero group stores
+ *               s = 0 and codes 0.  Codes never reach -8 (|y| <= 7 s).
+ *   tensor_scale, tensor_scale_mode: ignored (may be NULL / 0)
+ *
+ * NVFP4-style (fmt RHTQ_FMT_NVFP4; NVFP4 methodology thread):
+ *   group 16, scale_dtype RHTQ_SCALE_E4M3
+ *   tensor_scale  device float: DYNAMIC -> written with g = fl32(max|y| / 2688) over the
+ *                 whole call (two passes over x); GIVEN -> g is read (one pass)
+ *   scales_out    [tokens][n/16] E4M3FN codes of max|y_block| / (6 g), nearest even,
+ *                 saturating at 448, never NaN
+ *   codes         bit 3 = sign of y, bits 0-2 = E2M1 magnitude of |y| / (dec(s_b) g)
+ *                 ({0,.5,1,1.5,2,3,4,6}, nearest even, saturating at 6); a block whose
+ *                 scale decodes to 0 stores code 0.
+ */
+int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n,
+                 const int8_t* signs, int fmt, int32_t group, int scale_dtype,
+                 uint8_t* packed_out, void* scales_out, float* tensor_scale,
+                 int tensor_scale_mode, rhtq_stream_t stream);
+
+/*
+ * Inverse of rhtq_forward: unpack, dequantise with the stored scales (INT4 q*s;
+ * NVFP4 e2m1(c) * dec(s_b) * g) and undo the rotation, x_out = diag(s) H_n^T y / sqrt(n)
+ * (fp32 [tokens][n]).  Arguments mirror rhtq_forward; tensor_scale is read for NVFP4.
+ * Cite: QuaRot reviews, review 2 Summary (the RHT is invertible).
+ */
+int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_scale,
+                 int64_t tokens, int32_t n, const int8_t* signs, int fmt, int32_t group,
+                 int scale_dtype, float* x_out, rhtq_stream_t stream);
+
+/*
+ * Host helper: a random sign vector from a seed with splitmix64 (Steele, Lea and
+ * Flood, OOPSLA 2014): output i = mix(seed + (i+1) * 0x9E3779B97F4A7C15); the sign is
+ * -1 when its top bit is set.  host_out is HOST memory [n].  The pages draw the
+ * rotation at random and leave the generator open (NVFP4 methodology thread:
+ * results vary with the transform seed).
+ */
+int rhtq_signs_from_seed(uint64_t seed, int32_t n, int8_t* host_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RHTQ_H */

@@ -1,0 +1,47 @@
+// Internal interfaces between the host entry points (rhtq_api.cpp) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rhtq {
+
+enum Op : int {
+  OP_ROTATE = 0,   // y fp32
+  OP_INT4 = 1,     // packed INT4 + scales
+  OP_NVFP4 = 2,    // packed E2M1 + E4M3 scales, reads the tensor scale g
+  OP_AMAX = 3,     // atomic max of |y| bits into tensor_scale (NVFP4 dynamic pre-pass)
+  OP_INVERSE = 4,  // packed + scales -> x fp32
+};
+
+struct KernelArgs {
+  const void* x;            // forward input [rows][n] (bf16 or fp32)
+  const int8_t* signs;      // [n] or null
+  int64_t rows;
+  int32_t n;
+  int32_t group;            // elements per scale group (n for per-token)
+  int32_t scale_dtype;      // RHTQ_SCALE_*
+  float* y;                 // OP_ROTATE / OP_INVERSE output
+  uint8_t* packed;          // OP_INT4 / OP_NVFP4 output
+  void* scales;             // OP_INT4 / OP_NVFP4 output
+  float* tensor_scale;      // OP_NVFP4 input g, OP_AMAX accumulator (as uint bits)
+  const uint8_t* in_packed; // OP_INVERSE input
+  const void* in_scales;    // OP_INVERSE input
+  const float* in_tensor_scale;  // OP_INVERSE input (NVFP4)
+  int32_t inv_fmt;          // OP_INVERSE: RHTQ_FMT_*
+};
+
+// Generic LDS-staged path: every width, both input types, every op.
+// Returns hipSuccess or the launch error.
+hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t s);
+
+// Register-resident fast path (bf16 input).  Returns hipErrorNotSupported when the
+// (op, n, group) combination has no fast kernel; the caller then uses the generic one.
+hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
+
+// Tiny helper kernels for the dynamic NVFP4 tensor scale.
+hipError_t launch_zero_word(float* p, hipStream_t s);
+hipError_t launch_finalize_tensor_scale(float* p, hipStream_t s);
+
+}  // namespace rhtq

@@ -1,0 +1,101 @@
+"""CPU: the C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def R():
+    import randomized_hadamard_rotation_amd as R
+    return R
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "rhtq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(rhtq_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(R):
+    decl = declared_functions()
+    assert len(decl) == 7
+    lib = ctypes.CDLL(R.LIB_PATH)
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(R.EXPORTED) == decl
+
+
+def test_abi_version_and_status_strings(R):
+    assert R.rhtq_abi_version() == 1
+    assert R.rhtq_status_str(0) == "ok"
+    assert "invalid" in R.rhtq_status_str(1)
+    assert "unsupported" in R.rhtq_status_str(2)
+    assert "HIP" in R.rhtq_status_str(3)
+
+
+def test_supported_matrix(R):
+    for k in range(4, 15):
+        assert R.rhtq_supported(1 << k, "int4", 0)
+        assert R.rhtq_supported(1 << k, "nvfp4", 16)
+    for m in (256, 512, 1024, 2048):
+        assert R.rhtq_supported(12 * m, "int4", 128)
+    for bad in (0, 8, 32768, 100, 12 * 128, 12 * 4096, 11008):
+        assert not R.rhtq_supported(bad, "int4", 0)
+    assert not R.rhtq_supported(4096, "int4", 96)      # not a power of two
+    assert not R.rhtq_supported(4096, "int4", 8)       # below 16
+    assert not R.rhtq_supported(4096, "nvfp4", 32)
+
+
+def test_signs_from_seed_matches_generator(R):
+    from workloads import splitmix64_signs
+    for seed in (0, 1, 12345, 2**63 + 7):
+        for n in (1, 128, 4096, 12288):
+            assert np.array_equal(R.rhtq_signs_from_seed(seed, n), splitmix64_signs(seed, n))
+
+
+def test_host_validation(R):
+    lib = R.lib
+    fake = ctypes.c_void_p(0x100000)          # never dereferenced: every call below fails validation
+    mis = ctypes.c_void_p(0x100004)           # not 16-byte aligned
+    s = ctypes.c_void_p(0)
+    # rotate
+    assert lib.rhtq_rotate(fake, 0, -1, 4096, None, fake, s) == R.RHTQ_EINVAL
+    assert lib.rhtq_rotate(fake, 7, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
+    assert lib.rhtq_rotate(fake, 0, 4, 100, None, fake, s) == R.RHTQ_EUNSUPPORTED
+    assert lib.rhtq_rotate(None, 0, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
+    assert lib.rhtq_rotate(mis, 0, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
+    assert lib.rhtq_rotate(None, 0, 0, 4096, None, None, s) == R.RHTQ_OK   # empty: no-op
+    # forward
+    F = lambda *a: lib.rhtq_forward(*a)
+    assert F(fake, 0, -2, 4096, None, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EINVAL
+    assert F(fake, 0, 4, 4096, None, 0, 96, 0, fake, fake, None, 0, s) == R.RHTQ_EUNSUPPORTED
+    assert F(fake, 0, 4, 4096, None, 0, 0, 2, fake, fake, None, 0, s) == R.RHTQ_EUNSUPPORTED
+    assert F(fake, 0, 4, 4096, None, 1, 16, 1, fake, fake, fake, 0, s) == R.RHTQ_EUNSUPPORTED
+    assert F(fake, 0, 4, 4096, None, 1, 16, 2, fake, fake, None, 0, s) == R.RHTQ_EINVAL
+    assert F(fake, 0, 4, 4096, None, 1, 16, 2, fake, fake, fake, 9, s) == R.RHTQ_EINVAL
+    assert F(fake, 0, 4, 4096, None, 9, 16, 2, fake, fake, fake, 0, s) == R.RHTQ_EINVAL
+    assert F(None, 0, 4, 4096, None, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EINVAL
+    assert F(fake, 0, 4, 4096, None, 0, 0, 0, mis, fake, None, 0, s) == R.RHTQ_EINVAL
+    assert F(fake, 0, 4, 4096, None, 0, 0, 0, fake, ctypes.c_void_p(0x100002), None, 0, s) == R.RHTQ_EINVAL
+    assert F(None, 0, 0, 4096, None, 0, 0, 0, None, None, None, 0, s) == R.RHTQ_OK
+    # inverse
+    I = lambda *a: lib.rhtq_inverse(*a)
+    assert I(fake, fake, None, -1, 4096, None, 0, 0, 0, fake, s) == R.RHTQ_EINVAL
+    assert I(fake, fake, None, 4, 4097, None, 0, 0, 0, fake, s) == R.RHTQ_EUNSUPPORTED
+    assert I(fake, fake, None, 4, 4096, None, 1, 16, 2, fake, s) == R.RHTQ_EINVAL   # no tensor scale
+    assert I(None, fake, None, 4, 4096, None, 0, 0, 0, fake, s) == R.RHTQ_EINVAL
+    assert I(None, None, None, 0, 4096, None, 0, 0, 0, None, s) == R.RHTQ_OK
+    assert lib.rhtq_signs_from_seed(1, -1, None) == R.RHTQ_EINVAL
+
+
+def test_python_binding_refuses_cpu_tensors(R):
+    import torch
+    with pytest.raises(ValueError):
+        R.rhtq_rotate(torch.zeros(2, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        R.rhtq_forward(torch.zeros(2, 128, dtype=torch.bfloat16))

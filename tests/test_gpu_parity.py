@@ -1,0 +1,303 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Each case prints what it runs before touching the GPU, so a failing run names it.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle import check as C
+from tests import oracle_pins as P
+from workloads import WORKLOADS, generate, special_rows, splitmix64_signs
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tiny_128_int4.txt")
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def R():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import randomized_hadamard_rotation_amd as R
+    return R
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def to_np(t):
+    import torch
+    t = t.detach().to("cpu")
+    if t.dtype == torch.bfloat16:
+        return t.to(torch.float64).numpy()
+    return t.numpy()
+
+
+def run_forward(R, x, s, fmt, group, scale_dtype, **kw):
+    import torch
+    packed, scales, ts = R.rhtq_forward(x, s, fmt=fmt, group=group, scale_dtype=scale_dtype, **kw)
+    torch.cuda.synchronize()
+    return to_np(packed), to_np(scales), (None if ts is None else float(ts.item()))
+
+
+def check_forward(R, x, s, fmt, group, scale_dtype, rows=None, y_ref=None, g_ref=None):
+    """Device forward of all rows of x; oracle on `rows` (all by default)."""
+    packed, scales, g = run_forward(R, x, s, fmt, group, scale_dtype)
+    if rows is None:
+        rows = np.arange(x.shape[0])
+    if y_ref is None:
+        y_ref = O.rotate(x[rows].cpu(), s)
+    if fmt == "int4":
+        return C.check_int4(packed[rows], scales[rows], y_ref, group, scale_dtype)
+    return C.check_nvfp4(packed[rows], scales[rows], g, y_ref, g_ref)
+
+
+def x_to(w, tokens=None):
+    w = w if tokens is None else w.with_tokens(tokens)
+    x, s = generate(w, "cpu")
+    return x.to(dev()), s
+
+
+# ----------------------------------------------------------------------------
+# worked examples and closed forms
+# ----------------------------------------------------------------------------
+
+def test_tiny_fp32_matches_golden_fixture(R):
+    say("tiny_128_int4 vs tests/golden/tiny_128_int4.txt")
+    w = WORKLOADS["tiny_128_int4"]
+    x, s = x_to(w)
+    packed, scales, _ = run_forward(R, x, s, "int4", 0, "f32")
+    rows = [ln.split() for ln in open(GOLDEN) if not ln.startswith("#")]
+    gold_s = np.array([int(r[0], 16) for r in rows], dtype=np.uint32).view(np.float32)
+    gold_p = np.array([list(bytes.fromhex(r[1])) for r in rows], dtype=np.uint8)
+    y_ref = O.rotate(x.cpu(), s)
+    rep = C.check_int4(packed, scales, y_ref, 0, "f32")
+    assert np.abs(scales[:, 0] - gold_s).max() <= 1e-6 * np.abs(gold_s).max()
+    mism = int(np.sum(packed != gold_p))
+    assert mism <= rep["code_mismatches"], (mism, rep)
+
+
+def test_e2_exact_example(R):
+    say("E2 n=4096 exact")
+    import torch
+    xe, s = P.e2_input(4096)
+    x = torch.tensor(xe, dtype=torch.bfloat16, device=dev())
+    assert np.array_equal(to_np(x), xe)          # bf16-exact input
+    y = to_np(R.rhtq_rotate(x, s))
+    want = np.zeros((1, 4096), np.float32)
+    want[0, :4] = [7.0, 2.5, -1.5, 0.5]
+    assert np.array_equal(y, want)
+    packed, scales, _ = run_forward(R, x, s, "int4", 0, "f32")
+    assert scales[0, 0] == 1.0
+    assert packed[0, 0] == 0x27 and packed[0, 1] == 0x0E and not packed[0, 2:].any()
+
+
+@pytest.mark.parametrize("n,k", [(16, 3), (128, 77), (4096, 1234), (12288, 7000), (3072, 2049),
+                                 (16384, 9999), (24576, 123)])
+def test_e3_closed_form(R, n, k):
+    say(f"E3 n={n} k={k}")
+    import torch
+    s = splitmix64_signs(5, n)
+    xe = P._signed_row(O, n, k, s)[None, :]
+    x = torch.tensor(np.repeat(xe, 3, axis=0), dtype=torch.bfloat16, device=dev())
+    y = to_np(R.rhtq_rotate(x, s))
+    e = np.zeros(n); e[k] = math.sqrt(n)
+    assert np.max(np.abs(y - e)) <= 1e-5 * math.sqrt(n)
+    packed, scales, _ = run_forward(R, x, s, "int4", 0, "f32")
+    q = O.unpack_nibbles(packed)
+    assert np.all(q[:, k] == 7) and np.count_nonzero(q) == 3
+    assert np.all(scales[:, 0] == np.float32(math.sqrt(n) / 7.0)) or \
+        np.allclose(scales[:, 0], math.sqrt(n) / 7.0, rtol=1e-6)
+    if n % 128 == 0:
+        packed, scales, _ = run_forward(R, x, s, "int4", 128, "f16")
+        assert np.count_nonzero(scales) == 3
+        assert np.all(scales[:, k // 128] == np.float16(math.sqrt(n) / 7.0))
+    packed, scales, g = run_forward(R, x, s, "nvfp4", 16, "e4m3")
+    c = O.unpack_nibbles(packed, signed=False)
+    assert np.all(scales[:, k // 16] == 0x7E) and np.count_nonzero(scales) == 3
+    assert np.all(c[:, k] == 0b0111)
+    assert np.count_nonzero(c & 7) == 3
+
+
+# ----------------------------------------------------------------------------
+# the five workloads: reduced row counts (whole oracle) and full size (sampled rows)
+# ----------------------------------------------------------------------------
+
+REDUCED = [("tiny_128_int4", 64), ("llama_4096_int4", 203), ("downproj_12288_int4g128", 37),
+           ("kv_128_int4g128", 4099), ("nvfp4_4096", 131)]
+
+
+@pytest.mark.parametrize("name,tokens", REDUCED)
+def test_workload_reduced(R, name, tokens):
+    w = WORKLOADS[name]
+    say(f"{name} reduced to {tokens} rows")
+    x, s = x_to(w, tokens)
+    rep = check_forward(R, x, s, w.fmt, w.group, w.scale_dtype)
+    print(rep)
+
+
+@pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
+                                  "nvfp4_4096"])
+def test_workload_full_size_sampled(R, name):
+    """Full-size input on the device in the same launch shape as the benchmark;
+    the oracle checks sampled rows (first, last, every sink row it can find, random)."""
+    import torch
+    w = WORKLOADS[name]
+    say(f"{name} full size {w.tokens} x {w.n}")
+    x, s = generate(w, dev())
+    T = w.tokens
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.choice(T, 60, replace=False)]))
+    xr = x.float().abs().amax(dim=1)
+    big = torch.topk(xr, 4).indices.cpu().numpy()
+    rows = np.unique(np.concatenate([rows, big]))
+    g_ref = None
+    if w.fmt == "nvfp4":
+        # the tensor scale needs the amax over every row: oracle in chunks
+        amax = 0.0
+        for r0 in range(0, T, 2048):
+            amax = max(amax, float(np.max(np.abs(O.rotate(x[r0:r0 + 2048].cpu(), s)))))
+        g_ref = np.float32(amax / 2688.0)
+    rep = check_forward(R, x, s, w.fmt, w.group, w.scale_dtype, rows=rows, g_ref=g_ref)
+    print(rep)
+    # properties over the whole output: INT4 codes never -8
+    if w.fmt == "int4":
+        packed, _, _ = R.rhtq_forward(x, s, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype)
+        lo = (packed & 0xF)
+        hi = (packed >> 4)
+        assert not bool(((lo == 8) | (hi == 8)).any())
+
+
+# ----------------------------------------------------------------------------
+# sweeps: every width, several token counts, signs on / off, fp32 input
+# ----------------------------------------------------------------------------
+
+WIDTHS = [16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 3072, 6144, 12288, 24576]
+
+
+@pytest.mark.parametrize("n", WIDTHS)
+def test_rotate_every_width(R, n):
+    import torch
+    for tokens in (1, 3, 33):
+        for seed in (None, 1):
+            say(f"rotate n={n} tokens={tokens} signs={seed}")
+            g = torch.Generator().manual_seed(n + tokens)
+            xc = torch.randn(tokens, n, generator=g) * torch.exp(torch.randn(n, generator=g))
+            s = None if seed is None else splitmix64_signs(seed, n)
+            for dt in (torch.bfloat16, torch.float32):
+                x = xc.to(dt).to(dev())
+                y = to_np(R.rhtq_rotate(x, s))
+                C.check_rotation(y, O.rotate(x.cpu(), s))
+
+
+@pytest.mark.parametrize("n", WIDTHS)
+def test_quantise_every_width(R, n):
+    import torch
+    g = torch.Generator().manual_seed(3 * n)
+    xc = torch.randn(35, n, generator=g) * torch.exp(torch.randn(n, generator=g))
+    s = splitmix64_signs(2, n)
+    for dt in (torch.bfloat16, torch.float32):
+        x = xc.to(dt).to(dev())
+        y_ref = O.rotate(x.cpu(), s)
+        groups = [0, 16, 128] if n >= 128 else [0, 16]
+        for group in groups:
+            for sd in ("f32", "f16"):
+                say(f"int4 n={n} group={group} scale={sd} dtype={dt}")
+                check_forward(R, x, s, "int4", group, sd, y_ref=y_ref)
+        say(f"nvfp4 n={n} dtype={dt}")
+        check_forward(R, x, s, "nvfp4", 16, "e4m3", y_ref=y_ref)
+
+
+def test_nvfp4_given_tensor_scale(R):
+    import torch
+    w = WORKLOADS["nvfp4_4096"].with_tokens(77)
+    x, s = x_to(w)
+    say("nvfp4 given tensor scale")
+    y_ref = O.rotate(x.cpu(), s)
+    g = torch.tensor([0.37], dtype=torch.float32, device=dev())
+    packed, scales, ts = R.rhtq_forward(x, s, fmt="nvfp4", tensor_scale=g, tensor_scale_mode="given")
+    torch.cuda.synchronize()
+    assert float(ts.item()) == np.float32(0.37)       # read, not overwritten
+    C.check_nvfp4(to_np(packed), to_np(scales), np.float32(0.37), y_ref, g_ref=np.float32(0.37))
+
+
+# ----------------------------------------------------------------------------
+# edge cases
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["zeros", "constant", "tiny", "huge"])
+def test_special_inputs(R, kind):
+    for n in (128, 4096, 12288):
+        say(f"special {kind} n={n}")
+        x = special_rows(kind, n, 5, device=dev())
+        s = splitmix64_signs(3, n)
+        y_ref = O.rotate(x.cpu(), s)
+        C.check_rotation(to_np(R.rhtq_rotate(x, s)), y_ref)
+        check_forward(R, x, s, "int4", 0, "f32", y_ref=y_ref)
+        check_forward(R, x, s, "int4", 128, "f16", y_ref=y_ref)
+        check_forward(R, x, s, "nvfp4", 16, "e4m3", y_ref=y_ref)
+
+
+def test_zero_tokens_is_noop(R):
+    import torch
+    say("tokens = 0")
+    x = torch.empty((0, 4096), dtype=torch.bfloat16, device=dev())
+    R.rhtq_rotate(x)
+    R.rhtq_forward(x)
+    torch.cuda.synchronize()
+
+
+def test_deterministic(R):
+    import torch
+    for name in ("llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096"):
+        w = WORKLOADS[name]
+        say(f"determinism {name}")
+        x, s = x_to(w, min(w.tokens, 512))
+        a = run_forward(R, x, s, w.fmt, w.group, w.scale_dtype)
+        b = run_forward(R, x, s, w.fmt, w.group, w.scale_dtype)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+# ----------------------------------------------------------------------------
+# inverse
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
+                                  "nvfp4_4096"])
+def test_inverse_round_trip(R, name):
+    import torch
+    w = WORKLOADS[name]
+    say(f"inverse {name}")
+    x, s = x_to(w, 41)
+    packed, scales, ts = R.rhtq_forward(x, s, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype)
+    xh = R.rhtq_inverse(packed, scales, w.n, s, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype,
+                        tensor_scale=ts)
+    torch.cuda.synchronize()
+    g = None if ts is None else float(ts.item())
+    ref = O.inverse(to_np(packed), to_np(scales), s, w.fmt, w.group, g)
+    err = np.max(np.abs(to_np(xh) - ref), axis=1)
+    assert np.all(err <= 1e-5 * np.max(np.abs(ref), axis=1) + 1e-30)
+    # round trip bound: ||x - x_hat|| <= sqrt(sum over groups |G| (s_G/2)^2) for INT4
+    xr = to_np(x)
+    if w.fmt == "int4":
+        sc = to_np(scales).astype(np.float64)
+        gsz = w.n if w.group == 0 else w.group
+        bound = np.sqrt(np.sum(gsz * (sc / 2) ** 2, axis=1))
+        assert np.all(np.linalg.norm(to_np(xh) - xr, axis=1) <= bound * (1 + 1e-4))
+    # the rotation alone inverts to fp32 precision
+    y = R.rhtq_rotate(x, s)
+    torch.cuda.synchronize()
+    assert np.allclose(O.inverse_rotate(to_np(y), s), xr, rtol=0, atol=1e-5 * np.abs(xr).max())
