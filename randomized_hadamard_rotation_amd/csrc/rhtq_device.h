@@ -1,0 +1,101 @@
+// Device helpers shared by the HIP kernels (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rhtq {
+
+// (a, b) -> (a + b, a - b): one Walsh-Hadamard butterfly.
+__device__ __forceinline__ void bfly(float& a, float& b) {
+  const float s = a + b;
+  b = a - b;
+  a = s;
+}
+
+// Order-12 Williamson Hadamard array
+//   [[ A,  B,  B,  B],
+//    [-B,  A, -B,  B],
+//    [-B,  B,  A, -B],
+//    [-B, -B,  B,  A]]      A = J3 (all ones), B = J3 - 2 I3,
+// entry (r, c) as +1 / -1.  Block (bi, bj) is negated when bit 4*bi + bj of 0x3950 is set.
+__host__ __device__ constexpr int h12_entry(int r, int c) {
+  const int bi = r / 3, bj = c / 3;
+  const int bsign = ((0x3950 >> (4 * bi + bj)) & 1) ? -1 : 1;
+  const int e = (bi == bj) ? 1 : ((r % 3) == (c % 3) ? -1 : 1);
+  return bsign * e;
+}
+
+// w <- H12 w using the array's structure: with v1..v4 the four 3-blocks, sk = sum(vk),
+// A v = sk * 1 and B v = sk * 1 - 2 v, so block k of the result is
+// T_k * 1 + 2 (+-vi +-vj +-vl) with T_k = +-s1 +-s2 +-s3 +-s4 (52 adds/FMAs per 12 values).
+__device__ __forceinline__ void h12_forward(float* w) {
+  const float s1 = w[0] + w[1] + w[2];
+  const float s2 = w[3] + w[4] + w[5];
+  const float s3 = w[6] + w[7] + w[8];
+  const float s4 = w[9] + w[10] + w[11];
+  const float pa = s1 + s3, pb = s2 + s4, pc = s2 - s4, pd = s3 - s1;
+  const float t1 = pa + pb, t2 = pb - pa, t3 = pc + pd, t4 = pd - pc;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const float v1 = w[k], v2 = w[3 + k], v3 = w[6 + k], v4 = w[9 + k];
+    const float s34 = v3 + v4, d34 = v3 - v4, d24 = v2 - v4, s12 = v1 + v2;
+    w[k] = __builtin_fmaf(-2.0f, v2 + s34, t1);       // -2 (v2 + v3 + v4)
+    w[3 + k] = __builtin_fmaf(2.0f, v1 + d34, t2);    // +2 (v1 + v3 - v4)
+    w[6 + k] = __builtin_fmaf(2.0f, v1 - d24, t3);    // +2 (v1 - v2 + v4)
+    w[9 + k] = __builtin_fmaf(2.0f, s12 - v3, t4);    // +2 (v1 + v2 - v3)
+  }
+}
+
+// Maximum over aligned groups of G lanes (G a power of two, 1..64); every lane of the
+// group receives it.  Within 16 lanes by DPP; across rows by the gfx950 lane swaps.
+__device__ __forceinline__ float group_max(float v, int G) {
+  if (G >= 2) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  if (G >= 4) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  if (G >= 8) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  if (G >= 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  if (G >= 32) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  }
+  if (G >= 64) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  }
+  return v;
+}
+
+// E4M3FN (OCP FP8) code of s >= 0: nearest value, ties to even mantissa, saturating at
+// 448 (0x7E); NaN never produced.
+__device__ __forceinline__ uint32_t e4m3_code(float s) {
+  if (!(s > 0.0f)) return 0u;
+  if (s >= 448.0f) return 0x7Eu;
+  const uint32_t bits = __float_as_uint(s);
+  const int ex = (int)((bits >> 23) & 0xFF) - 127;
+  if (ex < -6) return (uint32_t)__builtin_rintf(s * 512.0f);   // subnormal steps of 2^-9
+  uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);          // round mantissa to 3 bits
+  r &= ~0xFFFFFu;
+  const int e2 = (int)((r >> 23) & 0xFF) - 127;
+  const uint32_t code = (uint32_t)((e2 + 7) << 3) | ((r >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * (1.0f / 512.0f);
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Eight INT4 codes -> one dword, element k in nibble k.  q[k] holds the bits of
+// fma(y, 1/s, 1.5 * 2^23): its low 4 bits are the two's-complement code.
+__device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t* q) {
+  const uint32_t e_lo = __builtin_amdgcn_perm(q[2], q[0], 0x0C0C0400u);
+  const uint32_t e_hi = __builtin_amdgcn_perm(q[6], q[4], 0x0C0C0400u);
+  const uint32_t o_lo = __builtin_amdgcn_perm(q[3], q[1], 0x0C0C0400u);
+  const uint32_t o_hi = __builtin_amdgcn_perm(q[7], q[5], 0x0C0C0400u);
+  const uint32_t ev = __builtin_amdgcn_perm(e_hi, e_lo, 0x05040100u);   // bytes q0 q2 q4 q6
+  const uint32_t od = __builtin_amdgcn_perm(o_hi, o_lo, 0x05040100u);   // bytes q1 q3 q5 q7
+  return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+}
+
+}  // namespace rhtq

@@ -1,12 +1,406 @@
-// Register-resident kernels for bf16 input (filled in below as they are written).
+// Register-resident kernels for bf16 input on gfx950.
+//
+// One wavefront owns one row (rows of >= 512 elements) or one 512-element block of
+// consecutive rows (128- and 256-wide rows) at a time and loops over rows
+// (persistent grid).  Per row:
+//
+//  1. Coalesced 16-byte loads in the MFMA A-operand layout: lane l loads the 8
+//     elements j = 512 f + 32 (l & 15) + 8 (l >> 4) + e of fragment f, so one load
+//     instruction covers 512 consecutive elements.  The random signs are applied by
+//     XOR-ing bf16 sign bits with masks kept in LDS.
+//  2. The first five index bits (0..4) are transformed by v_mfma_f32_16x16x32_bf16
+//     against a constant +-1 Sylvester H32 operand.  The input is exact bf16 and the
+//     matrix is +-1, so every product is exact and the sums are fp32 accumulations,
+//     the same arithmetic as the first five butterfly stages.
+//  3. The remaining bits run as fp32 butterflies in registers: bits 5-6 and the
+//     fragment bits (9..) are register indices; bits 7-8 sit in lane bits 4-5 and are
+//     brought into registers with v_permlane16_swap / v_permlane32_swap.
+//  4. n = 12 m: the order-12 Williamson factor is applied in registers across the
+//     twelve sub-rows (KronQ issue #2, Model Details: 12288 = 12 x 1024).
+//  5. Epilogue: 512/1024-element chunks go through a per-wave LDS buffer so that each
+//     lane holds 8 or 16 consecutive elements; then group maxima (DPP), scales,
+//     quantisation (INT4 by the round-to-nearest-even magic-constant FMA; E2M1 by
+//     v_cvt_scalef32_pk_fp4_f32 with unit scale), nibble packing and 8-byte stores.
+//
+// QuaRot reviews, review 1 Summary: the online Hadamard uses the Walsh-Hadamard fast
+// algorithm; review 2 Summary: random Hadamard transform then INT4; reviewer 2
+// follow-up: nearest rounding.  NVFP4 methodology thread: E2M1 + E4M3 block scales.
+#include <hip/hip_fp16.h>
+
 #include "rhtq.h"
+#include "rhtq_device.h"
 #include "rhtq_internal.h"
 
 namespace rhtq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+template <int F, int LOGM>
+struct Shape {
+  static constexpr int M = 1 << LOGM;                  // power-of-two factor
+  static constexpr int N = F * M;                      // row width
+  static constexpr int UNIT = N >= 512 ? N : 512;      // elements per wave iteration
+  static constexpr int RPU = UNIT / N;                 // rows per unit (1, 2 or 4)
+  static constexpr int NF = UNIT / 512;                // MFMA fragments per unit
+  static constexpr int FPJ = (F == 12) ? M / 512 : NF; // fragments per power-of-two sub-row
+  static constexpr int LOG_FPJ = FPJ == 1 ? 0 : (FPJ == 2 ? 1 : (FPJ == 4 ? 2 : (FPJ == 8 ? 3 : 4)));
+  static constexpr int CHUNK = M >= 1024 ? 1024 : 512; // epilogue transpose unit
+  static constexpr int NCH = UNIT / CHUNK;
+  static constexpr int FPC = CHUNK / 512;              // fragments per chunk
+  static constexpr int V = CHUNK / 64;                 // consecutive elements per lane after transpose
+  static constexpr int TBUF = CHUNK + CHUNK / 4;       // padded chunk buffer (floats)
+  static constexpr bool BIT7 = (F == 12) || LOGM >= 8; // bit 7 inside the row
+  static constexpr bool BIT8 = (F == 12) || LOGM >= 9; // bit 8 inside the row
+};
+
+// padded LDS index of a chunk-local element: 4 extra floats after every 16
+__device__ __forceinline__ int tpad(int j) { return j + ((j >> 4) << 2); }
+
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int F, int LOGM, int OP>
+__global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
+  using S = Shape<F, LOGM>;
+  extern __shared__ uint32_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t* sign_tab = smem;                                            // N/2 dwords
+  float* tbuf = reinterpret_cast<float*>(smem + S::N / 2) + wave * S::TBUF;
+
+  // sign-bit masks of bf16 pairs: dword d covers elements 2d, 2d+1
+  for (int d = threadIdx.x; d < S::N / 2; d += kThreads) {
+    uint32_t m = 0;
+    if (a.signs) m = (a.signs[2 * d] < 0 ? 0x8000u : 0u) | (a.signs[2 * d + 1] < 0 ? 0x80000000u : 0u);
+    sign_tab[d] = m;
+  }
+  // constant MFMA B operands: B_t[x][n] = H32[x][2n + t], x = 8 (l >> 4) + e, n = l & 15
+  bf16x8 hb[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    uint16_t bits[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int x = 8 * (lane >> 4) + e;
+      const int o = 2 * (lane & 15) + t;
+      bits[e] = (__builtin_popcount(x & o) & 1) ? 0xBF80 : 0x3F80;
+    }
+    __builtin_memcpy(&hb[t], bits, 16);
+  }
+  __syncthreads();
+
+  const float cnorm = (float)(1.0 / __builtin_sqrt((double)S::N));
+  const int64_t units = (a.rows + S::RPU - 1) / S::RPU;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  float run_max = 0.0f;
+  float gts = 0.0f, inv6g = 0.0f;
+  if constexpr (OP == OP_NVFP4) {
+    gts = a.tensor_scale[0];
+    inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
+  }
+
+  for (int64_t u = (int64_t)blockIdx.x * kWaves + wave; u < units; u += (int64_t)gridDim.x * kWaves) {
+    const int64_t ubase = u * S::UNIT;                 // element index of the unit start
+    const int64_t valid = (a.rows - u * S::RPU) * S::N;  // elements of the unit that exist (may exceed UNIT)
+
+    // ---------------- load, sign, MFMA ----------------
+    float v[S::NF][2][4];
+#pragma unroll
+    for (int f = 0; f < S::NF; ++f) {
+      const int off = 512 * f + 32 * (lane & 15) + 8 * (lane >> 4);
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (S::RPU == 1 || off < valid) raw = *reinterpret_cast<const uint4*>(x + ubase + off);
+      const uint4 m = *reinterpret_cast<const uint4*>(sign_tab + ((off % S::N) >> 1));
+      raw.x ^= m.x; raw.y ^= m.y; raw.z ^= m.z; raw.w ^= m.w;
+      bf16x8 av;
+      __builtin_memcpy(&av, &raw, 16);
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
+      const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[f][0][i] = d0[i]; v[f][1][i] = d1[i]; }
+    }
+
+    // ---------------- butterflies on register bits ----------------
+    // bits 5, 6: register index i
+#pragma unroll
+    for (int f = 0; f < S::NF; ++f)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bfly(v[f][t][0], v[f][t][1]);
+        bfly(v[f][t][2], v[f][t][3]);
+        bfly(v[f][t][0], v[f][t][2]);
+        bfly(v[f][t][1], v[f][t][3]);
+      }
+    // bits 9.. inside each power-of-two sub-row: fragment index
+#pragma unroll
+    for (int b = 0; b < S::LOG_FPJ; ++b)
+#pragma unroll
+      for (int f = 0; f < S::NF; ++f)
+        if (((f % S::FPJ) & (1 << b)) == 0)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bfly(v[f][t][i], v[f + (1 << b)][t][i]);
+    // order-12 factor across the twelve sub-rows
+    if constexpr (F == 12) {
+#pragma unroll
+      for (int fl = 0; fl < S::FPJ; ++fl)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float w[12];
+#pragma unroll
+            for (int j1 = 0; j1 < 12; ++j1) w[j1] = v[j1 * S::FPJ + fl][t][i];
+            h12_forward(w);
+#pragma unroll
+            for (int j1 = 0; j1 < 12; ++j1) v[j1 * S::FPJ + fl][t][i] = w[j1];
+          }
+    }
+    // bit 7 (lane bit 4) and bit 8 (lane bit 5): exchange with register bits 5 / 6
+    if constexpr (S::BIT7) {
+#pragma unroll
+      for (int f = 0; f < S::NF; ++f)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[f][t][i]),
+                                                      __float_as_uint(v[f][t][i + 1]), false, false);
+            v[f][t][i] = __uint_as_float(p[0]);
+            v[f][t][i + 1] = __uint_as_float(p[1]);
+            bfly(v[f][t][i], v[f][t][i + 1]);
+          }
+    }
+    if constexpr (S::BIT8) {
+#pragma unroll
+      for (int f = 0; f < S::NF; ++f)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[f][t][i]),
+                                                      __float_as_uint(v[f][t][i + 2]), false, false);
+            v[f][t][i] = __uint_as_float(p[0]);
+            v[f][t][i + 2] = __uint_as_float(p[1]);
+            bfly(v[f][t][i], v[f][t][i + 2]);
+          }
+    }
+    // Element held by (f, t, i) at this lane, within the unit (rows >= 512 wide):
+    //   j = 512 f + 128 i + 32 (lane >> 4) + 2 (lane & 15) + t
+    // 256-wide rows (bit 8 = row):  j = 256 (lane >> 5) + 128 (i & 1) + 64 (i >> 1) + 32 ((lane >> 4) & 1) + 2 (lane & 15) + t
+    // 128-wide rows (bits 7-8 = row): j = 128 (lane >> 4) + 32 i + 2 (lane & 15) + t
+
+    if constexpr (OP == OP_AMAX) {
+#pragma unroll
+      for (int f = 0; f < S::NF; ++f)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) run_max = fmaxf(run_max, fabsf(v[f][t][i]));
+      continue;
+    }
+
+    // per-token groups wider than a chunk: row maximum now (whole unit is one row)
+    float row_amax = 0.0f;
+    const bool row_group = (OP == OP_INT4) && (a.group > S::CHUNK);
+    if (row_group) {
+#pragma unroll
+      for (int f = 0; f < S::NF; ++f)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) row_amax = fmaxf(row_amax, fabsf(v[f][t][i]));
+      row_amax = group_max(row_amax, 64);
+    }
+
+    // ---------------- epilogue, one chunk at a time ----------------
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c) {
+      // registers of chunk c -> LDS in element order
+#pragma unroll
+      for (int fc = 0; fc < S::FPC; ++fc) {
+        const int f = c * S::FPC + fc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int jl;
+          if constexpr (S::N >= 512 || F == 12)
+            jl = 512 * fc + 128 * i + 32 * (lane >> 4) + 2 * (lane & 15);
+          else if constexpr (S::N == 256)
+            jl = 256 * (lane >> 5) + 128 * (i & 1) + 64 * (i >> 1) + 32 * ((lane >> 4) & 1) + 2 * (lane & 15);
+          else
+            jl = 128 * (lane >> 4) + 32 * i + 2 * (lane & 15);
+          *reinterpret_cast<float2*>(tbuf + tpad(jl)) = make_float2(v[f][0][i], v[f][1][i]);
+        }
+      }
+      lds_fence();
+      float y[S::V];
+#pragma unroll
+      for (int q = 0; q < S::V / 4; ++q) {
+        const float4 r = *reinterpret_cast<const float4*>(tbuf + tpad(S::V * lane + 4 * q));
+        y[4 * q + 0] = r.x; y[4 * q + 1] = r.y; y[4 * q + 2] = r.z; y[4 * q + 3] = r.w;
+      }
+      lds_fence();
+
+      const int64_t g0 = ubase + (int64_t)c * S::CHUNK + S::V * lane;   // first element of this lane
+      const bool live = (S::RPU == 1) || ((int64_t)c * S::CHUNK + S::V * lane < valid);
+
+      if constexpr (OP == OP_ROTATE) {
+        if (live) {
+          float4* dst = reinterpret_cast<float4*>(a.y + g0);
+#pragma unroll
+          for (int q = 0; q < S::V / 4; ++q)
+            dst[q] = make_float4(y[4 * q] * cnorm, y[4 * q + 1] * cnorm, y[4 * q + 2] * cnorm, y[4 * q + 3] * cnorm);
+        }
+      } else if constexpr (OP == OP_INT4) {
+        float amax;
+        int lanes_per_group;
+        if (row_group) {
+          amax = row_amax;
+          lanes_per_group = 64;  // unused
+        } else {
+          float m = 0.0f;
+#pragma unroll
+          for (int r = 0; r < S::V; ++r) m = fmaxf(m, fabsf(y[r]));
+          lanes_per_group = a.group / S::V;
+          amax = group_max(m, lanes_per_group);
+        }
+        const float amax_y = amax * cnorm;
+        const float s = amax_y / 7.0f;
+        float sq;
+        if (a.scale_dtype == RHTQ_SCALE_F32) {
+          sq = s;
+        } else {
+          sq = __half2float(__float2half_rn(fminf(s, 65504.0f)));
+        }
+        const float inv = sq > 0.0f ? cnorm * __builtin_amdgcn_rcpf(sq) : 0.0f;
+        // codes leave [-7, 7] only when the stored scale is far below amax / 7 (fp16 saturation
+        // or a subnormal scale); clamp in that rare case
+        const bool clamp = __builtin_amdgcn_ballot_w64(amax * inv > 7.25f) != 0;
+        uint32_t qb[S::V];
+        if (!clamp) {
+#pragma unroll
+          for (int r = 0; r < S::V; ++r) qb[r] = __float_as_uint(__builtin_fmaf(y[r], inv, 12582912.0f));
+        } else {
+#pragma unroll
+          for (int r = 0; r < S::V; ++r)
+            qb[r] = __float_as_uint(__builtin_amdgcn_fmed3f(y[r] * inv, -8.0f, 7.0f) + 12582912.0f);
+        }
+        if (live) {
+          if constexpr (S::V == 16) {
+            const uint2 w = make_uint2(pack8_nibbles(qb), pack8_nibbles(qb + 8));
+            *reinterpret_cast<uint2*>(a.packed + (g0 >> 1)) = w;
+          } else {
+            *reinterpret_cast<uint32_t*>(a.packed + (g0 >> 1)) = pack8_nibbles(qb);
+          }
+          const bool writer = row_group ? (c == 0 && lane == 0) : ((lane & (lanes_per_group - 1)) == 0);
+          if (writer) {
+            const int64_t gi = g0 / a.group;
+            if (a.scale_dtype == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[gi] = s;
+            else static_cast<__half*>(a.scales)[gi] = __float2half_rn(fminf(s, 65504.0f));
+          }
+        }
+      } else if constexpr (OP == OP_NVFP4) {
+        // 16-element blocks: one lane (V = 16) or two lanes (V = 8)
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < S::V; ++r) m = fmaxf(m, fabsf(y[r]));
+        m = group_max(m, 16 / S::V);
+        const uint32_t code = e4m3_code((m * cnorm) * inv6g);
+        const float seff = e4m3_value(code) * gts;
+        const float inv = seff > 0.0f ? cnorm * __builtin_amdgcn_rcpf(seff) : 0.0f;
+        uint32_t words[S::V / 8];
+#pragma unroll
+        for (int w = 0; w < S::V / 8; ++w) {
+          uint32_t acc = 0;
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * w + 0] * inv, y[8 * w + 1] * inv, 1.0f, 0);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * w + 2] * inv, y[8 * w + 3] * inv, 1.0f, 1);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * w + 4] * inv, y[8 * w + 5] * inv, 1.0f, 2);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * w + 6] * inv, y[8 * w + 7] * inv, 1.0f, 3);
+          words[w] = seff > 0.0f ? acc : 0u;     // a block whose scale decodes to 0 stores code 0
+        }
+        if (live) {
+          if constexpr (S::V == 16)
+            *reinterpret_cast<uint2*>(a.packed + (g0 >> 1)) = make_uint2(words[0], words[1]);
+          else
+            *reinterpret_cast<uint32_t*>(a.packed + (g0 >> 1)) = words[0];
+          if (S::V == 16 || (lane & 1) == 0) static_cast<uint8_t*>(a.scales)[g0 >> 4] = (uint8_t)code;
+        }
+      }
+    }
+  }
+
+  if constexpr (OP == OP_AMAX) {
+    run_max = group_max(run_max, 64);
+    __shared__ float wmax[kWaves];
+    if (lane == 0) wmax[wave] = run_max;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = wmax[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) m = fmaxf(m, wmax[w]);
+      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(m * cnorm));
+    }
+  }
+}
+
+template <int F, int LOGM, int OP>
+hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
+  using S = Shape<F, LOGM>;
+  if constexpr (OP == OP_INT4) {
+    if (!(a.group == S::N || a.group <= S::CHUNK)) return hipErrorNotSupported;
+  }
+  auto kern = fast_kernel<F, LOGM, OP>;
+  const size_t lds = (size_t)(S::N / 2) * 4 + (size_t)kWaves * S::TBUF * 4;
+  static int max_blocks = 0;   // resident blocks per CU x CUs, computed once per instantiation
+  if (max_blocks == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorNotSupported;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kThreads, lds) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    max_blocks = cus * per_cu;
+  }
+  const int64_t units = (a.rows + S::RPU - 1) / S::RPU;
+  const int64_t want = (units + kWaves - 1) / kWaves;
+  const int grid = (int)(want < max_blocks ? want : max_blocks);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int OP>
+hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
+  switch (a.n) {
+    case 128: return launch_one<1, 7, OP>(a, s);
+    case 256: return launch_one<1, 8, OP>(a, s);
+    case 512: return launch_one<1, 9, OP>(a, s);
+    case 1024: return launch_one<1, 10, OP>(a, s);
+    case 2048: return launch_one<1, 11, OP>(a, s);
+    case 4096: return launch_one<1, 12, OP>(a, s);
+    case 8192: return launch_one<1, 13, OP>(a, s);
+    case 6144: return launch_one<12, 9, OP>(a, s);
+    case 12288: return launch_one<12, 10, OP>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace
 
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s) {
-  (void)op; (void)a; (void)s;
-  return hipErrorNotSupported;
+  if (getenv_fast_disabled()) return hipErrorNotSupported;
+  switch (op) {
+    case OP_ROTATE: return dispatch<OP_ROTATE>(a, s);
+    case OP_INT4: return dispatch<OP_INT4>(a, s);
+    case OP_NVFP4: return dispatch<OP_NVFP4>(a, s);
+    case OP_AMAX: return dispatch<OP_AMAX>(a, s);
+    default: return hipErrorNotSupported;
+  }
 }
 
 }  // namespace rhtq

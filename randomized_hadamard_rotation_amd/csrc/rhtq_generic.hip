@@ -10,6 +10,7 @@
 #include <hip/hip_fp16.h>
 
 #include "rhtq.h"
+#include "rhtq_device.h"
 #include "rhtq_internal.h"
 
 namespace rhtq {
@@ -20,45 +21,8 @@ constexpr int kTileTarget = 4096;
 
 __host__ __device__ constexpr int lds_idx(int j) { return j + (j >> 5); }
 
-// Williamson array of order 12: 4 x 4 blocks of 3 x 3, A = J3 on the block
-// diagonal, B = J3 - 2 I3 elsewhere, block signs
-//   + + + +
-//   - + - +
-//   - + + -
-//   - - + +
-__host__ __device__ constexpr int h12(int r, int c) {
-  const int bi = r / 3, bj = c / 3;
-  const bool diag_block = bi == bj;
-  const int sign_tab = 0x3950;  // bit (4*bi+bj) set => block negated
-  const int bsign = ((sign_tab >> (4 * bi + bj)) & 1) ? -1 : 1;
-  const int e = diag_block ? 1 : ((r % 3) == (c % 3) ? -1 : 1);
-  return bsign * e;
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// E4M3FN code of s >= 0: nearest even, saturating at 448 (0x7E), never NaN.
-__device__ __forceinline__ uint32_t e4m3_code(float s) {
-  if (!(s > 0.0f)) return 0u;
-  if (s >= 448.0f) return 0x7Eu;
-  const uint32_t bits = __float_as_uint(s);
-  const int ex = (int)((bits >> 23) & 0xFF) - 127;
-  if (ex < -6) {                      // subnormal range: steps of 2^-9
-    return (uint32_t)__builtin_rintf(s * 512.0f);   // 8 -> 0x08 = 2^-6 (exact)
-  }
-  uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);   // round mantissa to 3 bits
-  r &= ~0xFFFFFu;
-  const int e2 = (int)((r >> 23) & 0xFF) - 127;
-  uint32_t code = (uint32_t)((e2 + 7) << 3) | ((r >> 20) & 7u);
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 0) return (float)m * (1.0f / 512.0f);
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
 
 // 3-bit E2M1 magnitude of a >= 0, nearest even, saturating at 6.
 __device__ __forceinline__ uint32_t e2m1_mag(float a) {
@@ -193,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(KernelArgs a) {
           float acc = 0.0f;
 #pragma unroll
           for (int j = 0; j < 12; ++j) {
-            const int h = (OP == OP_INVERSE) ? h12(j, i) : h12(i, j);
+            const int h = (OP == OP_INVERSE) ? h12_entry(j, i) : h12_entry(i, j);
             acc = h > 0 ? acc + v[j] : acc - v[j];
           }
           o[i] = acc;

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace rhtq {
 
@@ -39,6 +40,15 @@ hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t
 // Register-resident fast path (bf16 input).  Returns hipErrorNotSupported when the
 // (op, n, group) combination has no fast kernel; the caller then uses the generic one.
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
+
+// RHTQ_FORCE_GENERIC=1 routes every call to the generic kernels (read once).
+inline bool getenv_fast_disabled() {
+  static const bool v = [] {
+    const char* e = getenv("RHTQ_FORCE_GENERIC");
+    return e != nullptr && e[0] == '1';
+  }();
+  return v;
+}
 
 // Tiny helper kernels for the dynamic NVFP4 tensor scale.
 hipError_t launch_zero_word(float* p, hipStream_t s);
