@@ -37,8 +37,8 @@
  *  - Arguments are checked on the host before any HIP call; on error nothing is
  *    enqueued and the status says why.  tokens == 0 is a valid no-op.
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.
- *  - Alignment: x, y_out, packed_out and x_out must be 16-byte aligned; scale
- *    buffers aligned to their element size.
+ *  - Alignment: x, y_out, packed_out, x_out and signs must be 16-byte aligned;
+ *    scale buffers aligned to their element size.
  *  - Supported widths: n = 2^k with 16 <= n <= 16384, and n = 12 * 2^k with
  *    256 <= 2^k <= 2048 (3072, 6144, 12288, 24576).
  *  - signs: device int8 [n] with values +1 / -1, or NULL for all +1 (plain

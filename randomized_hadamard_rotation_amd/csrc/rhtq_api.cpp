@@ -71,7 +71,7 @@ int rhtq_rotate(const void* x, int in_dtype, int64_t tokens, int32_t n, const in
   if (!width_ok(n)) return RHTQ_EUNSUPPORTED;
   if (tokens == 0) return RHTQ_OK;
   if (!x || !y_out) return RHTQ_EINVAL;
-  if (!aligned(x, 16) || !aligned(y_out, 16)) return RHTQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(y_out, 16) || !aligned(signs, 16)) return RHTQ_EINVAL;
   rhtq::KernelArgs a{};
   a.x = x;
   a.signs = signs;
@@ -99,7 +99,8 @@ int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n, const i
   if (tokens == 0) return RHTQ_OK;
   if (!x || !packed_out || !scales_out) return RHTQ_EINVAL;
   if (fmt == RHTQ_FMT_NVFP4 && !tensor_scale) return RHTQ_EINVAL;
-  if (!aligned(x, 16) || !aligned(packed_out, 16) || !aligned(scales_out, scale_align(scale_dtype)))
+  if (!aligned(x, 16) || !aligned(packed_out, 16) || !aligned(scales_out, scale_align(scale_dtype)) ||
+      !aligned(signs, 16))
     return RHTQ_EINVAL;
   if (fmt == RHTQ_FMT_NVFP4 && !aligned(tensor_scale, 4)) return RHTQ_EINVAL;
 
@@ -141,7 +142,8 @@ int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_
   if (tokens == 0) return RHTQ_OK;
   if (!packed || !scales || !x_out) return RHTQ_EINVAL;
   if (fmt == RHTQ_FMT_NVFP4 && !tensor_scale) return RHTQ_EINVAL;
-  if (!aligned(packed, 4) || !aligned(x_out, 16) || !aligned(scales, scale_align(scale_dtype)))
+  if (!aligned(packed, 4) || !aligned(x_out, 16) || !aligned(scales, scale_align(scale_dtype)) ||
+      !aligned(signs, 16))
     return RHTQ_EINVAL;
   rhtq::KernelArgs a{};
   a.signs = signs;

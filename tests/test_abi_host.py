@@ -69,6 +69,7 @@ def test_host_validation(R):
     assert lib.rhtq_rotate(fake, 0, 4, 100, None, fake, s) == R.RHTQ_EUNSUPPORTED
     assert lib.rhtq_rotate(None, 0, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
     assert lib.rhtq_rotate(mis, 0, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
+    assert lib.rhtq_rotate(fake, 0, 4, 4096, mis, fake, s) == R.RHTQ_EINVAL     # signs misaligned
     assert lib.rhtq_rotate(None, 0, 0, 4096, None, None, s) == R.RHTQ_OK   # empty: no-op
     # forward
     F = lambda *a: lib.rhtq_forward(*a)
@@ -82,6 +83,7 @@ def test_host_validation(R):
     assert F(None, 0, 4, 4096, None, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EINVAL
     assert F(fake, 0, 4, 4096, None, 0, 0, 0, mis, fake, None, 0, s) == R.RHTQ_EINVAL
     assert F(fake, 0, 4, 4096, None, 0, 0, 0, fake, ctypes.c_void_p(0x100002), None, 0, s) == R.RHTQ_EINVAL
+    assert F(fake, 0, 4, 4096, mis, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EINVAL
     assert F(None, 0, 0, 4096, None, 0, 0, 0, None, None, None, 0, s) == R.RHTQ_OK
     # inverse
     I = lambda *a: lib.rhtq_inverse(*a)
