@@ -2,9 +2,71 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include "rhtq.h"
+
 namespace rhtq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming accesses: each input and output byte is touched once, so the loads and
+// stores carry the non-temporal hint (measured ~10% more HBM throughput on gfx950).
+__device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st_stream(uint8_t* p, uint32_t a, uint32_t b) {
+  const u32x2 t = {a, b};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_stream(uint8_t* p, uint32_t a) {
+  __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void st_stream(float* p, float a, float b, float c, float d) {
+  const f32x4 t = {a, b, c, d};
+  __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(p));
+}
+
+// INT4 group scale from the group maximum of the unnormalised values:
+// s = amax * cnorm * fl(1/7) stored as fp32 or fp16 (nearest even, saturating); inv maps an
+// unnormalised value to scale units (0 for a zero group); clamp flags a stored scale far
+// below amax / 7 (fp16 saturation, subnormal scale) where codes must be clamped to [-8, 7].
+struct Int4Scale {
+  float s;
+  float inv;
+  bool clamp;
+};
+
+__device__ __forceinline__ Int4Scale int4_scale(float amax, float cnorm, int scale_dtype) {
+  Int4Scale r;
+  r.s = (amax * cnorm) * (1.0f / 7.0f);   // within 2 ulp of the exact quotient
+  const float sq = scale_dtype == RHTQ_SCALE_F32 ? r.s : __half2float(__float2half_rn(fminf(r.s, 65504.0f)));
+  r.inv = sq > 0.0f ? cnorm * __builtin_amdgcn_rcpf(sq) : 0.0f;
+  r.clamp = amax * r.inv > 7.25f;
+  return r;
+}
+
+// Constant MFMA B operand of v_mfma_f32_16x16x32_bf16 for a 32-point Sylvester
+// Hadamard: B_t[x][n] = H32[x][2n + t] with x = 8 (lane >> 4) + e and n = lane & 15, so
+// output column n of N-tile t is element 2n + t of the transformed 32-vector.
+__device__ __forceinline__ bf16x8 h32_operand(int lane, int t) {
+  uint16_t bits[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int xk = 8 * (lane >> 4) + e;
+    const int o = 2 * (lane & 15) + t;
+    bits[e] = (__builtin_popcount(xk & o) & 1) ? 0xBF80 : 0x3F80;
+  }
+  bf16x8 r;
+  __builtin_memcpy(&r, bits, 16);
+  return r;
+}
+
 
 // (a, b) -> (a + b, a - b): one Walsh-Hadamard butterfly.
 __device__ __forceinline__ void bfly(float& a, float& b) {

@@ -34,29 +34,6 @@
 namespace rhtq {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-// Streaming accesses: each input and output byte is touched once, so the loads and
-// stores carry the non-temporal hint (measured ~10% more HBM throughput on gfx950).
-__device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
-  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-__device__ __forceinline__ void st_stream(uint8_t* p, uint32_t a, uint32_t b) {
-  const u32x2 t = {a, b};
-  __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
-}
-__device__ __forceinline__ void st_stream(uint8_t* p, uint32_t a) {
-  __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
-}
-__device__ __forceinline__ void st_stream(float* p, float a, float b, float c, float d) {
-  const f32x4 t = {a, b, c, d};
-  __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(p));
-}
-
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
@@ -73,34 +50,19 @@ struct Shape {
   static constexpr int NCH = UNIT / CHUNK;
   static constexpr int FPC = CHUNK / 512;              // fragments per chunk
   static constexpr int V = CHUNK / 64;                 // consecutive elements per lane after transpose
-  static constexpr int TBUF = CHUNK + CHUNK / 4;       // padded chunk buffer (floats)
+  static constexpr int TBUF = CHUNK + CHUNK / 8;       // padded chunk buffer (floats)
   static constexpr bool BIT7 = (F == 12) || LOGM >= 8; // bit 7 inside the row
   static constexpr bool BIT8 = (F == 12) || LOGM >= 9; // bit 8 inside the row
+  // loads of the next unit overlap this unit's work when the registers allow it
+  static constexpr bool PREFETCH = NF <= 8;
 };
 
-// padded LDS index of a chunk-local element: 4 extra floats after every 16
-__device__ __forceinline__ int tpad(int j) { return j + ((j >> 4) << 2); }
+// padded LDS index of a chunk-local element: 4 extra floats after every 32, so the
+// 8-byte pair stores and the 16-byte reads of 8 or 16 consecutive floats per lane touch
+// distinct banks
+__device__ __forceinline__ int tpad(int j) { return j + ((j >> 5) << 2); }
 
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// INT4 group scale from the group maximum of the unnormalised values:
-// s = (amax * cnorm) / 7 stored as fp32 or fp16 (nearest even, saturating); inv maps an
-// unnormalised value to scale units (0 for a zero group); clamp flags a stored scale far
-// below amax / 7 (fp16 saturation, subnormal scale) where codes must be clamped to [-8, 7].
-struct Int4Scale {
-  float s;
-  float inv;
-  bool clamp;
-};
-
-__device__ __forceinline__ Int4Scale int4_scale(float amax, float cnorm, int scale_dtype) {
-  Int4Scale r;
-  r.s = (amax * cnorm) / 7.0f;
-  const float sq = scale_dtype == RHTQ_SCALE_F32 ? r.s : __half2float(__float2half_rn(fminf(r.s, 65504.0f)));
-  r.inv = sq > 0.0f ? cnorm * __builtin_amdgcn_rcpf(sq) : 0.0f;
-  r.clamp = amax * r.inv > 7.25f;
-  return r;
-}
 
 // Issue the 16-byte loads of unit u (fragment f at element 512 f + 32 (l & 15) + 8 (l >> 4));
 // elements past the last row read as zero.
@@ -123,8 +85,7 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   extern __shared__ uint32_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t* sign_tab = smem;                                            // N/2 dwords
-  float* tbuf = reinterpret_cast<float*>(smem + S::N / 2) + wave * S::TBUF;
+  float* tbuf = reinterpret_cast<float*>(smem + S::NF * 256) + wave * S::TBUF;
 
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)S::N));
   const int64_t units = (a.rows + S::RPU - 1) / S::RPU;
@@ -136,38 +97,23 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   uint4 raw[S::NF];
   load_unit<S>(x, u, units, a.rows, lane, raw);
 
-  // sign-bit masks of bf16 pairs: dword d covers elements 2d, 2d+1 (bit 15 / bit 31).
-  // Each thread turns 16 int8 signs (one 16-byte load) into 8 mask dwords.
-  for (int d0 = 8 * threadIdx.x; d0 < S::N / 2; d0 += 8 * kThreads) {
-    uint4 m0 = make_uint4(0, 0, 0, 0), m1 = make_uint4(0, 0, 0, 0);
+  // bf16 sign-bit masks in load order: entry f * 64 + lane holds the four mask dwords
+  // (bit 15 / bit 31 of each bf16 pair) of the 8 elements that lane loads for fragment f
+  uint4* sign_tab = reinterpret_cast<uint4*>(smem);
+  for (int k = threadIdx.x; k < S::NF * 64; k += kThreads) {
+    uint4 m = make_uint4(0, 0, 0, 0);
     if (a.signs) {
-      const uint4 sv = *reinterpret_cast<const uint4*>(a.signs + 2 * d0);
-      // byte 2k -> byte 1, byte 2k+1 -> byte 3; keep the sign bits
-      m0.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
-      m0.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
-      m0.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
-      m0.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
-      m1.x = __builtin_amdgcn_perm(0u, sv.z, 0x010C000Cu) & 0x80008000u;
-      m1.y = __builtin_amdgcn_perm(0u, sv.z, 0x030C020Cu) & 0x80008000u;
-      m1.z = __builtin_amdgcn_perm(0u, sv.w, 0x010C000Cu) & 0x80008000u;
-      m1.w = __builtin_amdgcn_perm(0u, sv.w, 0x030C020Cu) & 0x80008000u;
+      const int kl = k & 63;
+      const int col = (512 * (k >> 6) + 32 * (kl & 15) + 8 * (kl >> 4)) % S::N;
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + col);
+      m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
+      m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
+      m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
+      m.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
     }
-    *reinterpret_cast<uint4*>(sign_tab + d0) = m0;
-    *reinterpret_cast<uint4*>(sign_tab + d0 + 4) = m1;
+    sign_tab[k] = m;
   }
-  // constant MFMA B operands: B_t[x][n] = H32[x][2n + t], x = 8 (l >> 4) + e, n = l & 15
-  bf16x8 hb[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    uint16_t bits[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int xk = 8 * (lane >> 4) + e;
-      const int o = 2 * (lane & 15) + t;
-      bits[e] = (__builtin_popcount(xk & o) & 1) ? 0xBF80 : 0x3F80;
-    }
-    __builtin_memcpy(&hb[t], bits, 16);
-  }
+  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
   __syncthreads();
   float run_max = 0.0f;
   float gts = 0.0f, inv6g = 0.0f;
@@ -177,6 +123,8 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   }
 
   for (; u < units; u += ustride) {
+    if constexpr (!S::PREFETCH)
+      if (u != (int64_t)blockIdx.x * kWaves + wave) load_unit<S>(x, u, units, a.rows, lane, raw);
     const int64_t ubase = u * S::UNIT;                 // element index of the unit start
     const int64_t valid = (a.rows - u * S::RPU) * S::N;  // elements of the unit that exist (may exceed UNIT)
 
@@ -185,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
 #pragma unroll
     for (int f = 0; f < S::NF; ++f) {
       const int off = 512 * f + 32 * (lane & 15) + 8 * (lane >> 4);
-      const uint4 m = *reinterpret_cast<const uint4*>(sign_tab + ((off % S::N) >> 1));
+      const uint4 m = sign_tab[f * 64 + lane];
       uint4 r = raw[f];
       r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
       bf16x8 av;
@@ -198,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     }
     // raw[] is consumed: its registers now receive the next unit, whose loads run while
     // this unit's butterflies and epilogue execute
-    load_unit<S>(x, u + ustride, units, a.rows, lane, raw);
+    if constexpr (S::PREFETCH) load_unit<S>(x, u + ustride, units, a.rows, lane, raw);
 
     // ---------------- butterflies on register bits ----------------
     // bits 5, 6: register index i
@@ -420,7 +368,7 @@ hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
     if (!(a.group == S::N || a.group <= S::CHUNK)) return hipErrorNotSupported;
   }
   auto kern = fast_kernel<F, LOGM, OP>;
-  const size_t lds = (size_t)(S::N / 2) * 4 + (size_t)kWaves * S::TBUF * 4;
+  const size_t lds = (size_t)S::NF * 64 * 16 + (size_t)kWaves * S::TBUF * 4;
   static int max_blocks = 0;   // resident blocks per CU x CUs, computed once per instantiation
   if (max_blocks == 0) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -449,7 +397,6 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
     case 4096: return launch_one<1, 12, OP>(a, s);
     case 8192: return launch_one<1, 13, OP>(a, s);
     case 6144: return launch_one<12, 9, OP>(a, s);
-    case 12288: return launch_one<12, 10, OP>(a, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -458,6 +405,7 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
 
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s) {
   if (getenv_fast_disabled()) return hipErrorNotSupported;
+  if (a.n == 12288) return launch_fast12(op, a, s);
   switch (op) {
     case OP_ROTATE: return dispatch<OP_ROTATE>(a, s);
     case OP_INT4: return dispatch<OP_INT4>(a, s);

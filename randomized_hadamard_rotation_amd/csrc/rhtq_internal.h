@@ -41,6 +41,9 @@ hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t
 // (op, n, group) combination has no fast kernel; the caller then uses the generic one.
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
 
+// Two-wave kernel for 12288-wide rows (called by launch_fast).
+hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s);
+
 // RHTQ_FORCE_GENERIC=1 routes every call to the generic kernels (read once).
 inline bool getenv_fast_disabled() {
   static const bool v = [] {
