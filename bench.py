@@ -128,6 +128,43 @@ def cpu_baseline(name, budget_s=10.0):
                       f"({el:.1f} s, numpy fp64, one process)"}
 
 
+def copy_calibration(torch, nbytes=1 << 30, reps=8):
+    """A plain device copy of known size (torch's elementwise negation of fp32, which reads
+    and writes nbytes each): the HBM counters read under it give the factor that turns
+    FETCH_SIZE / WRITE_SIZE into bytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"read_bytes": nbytes, "write_bytes": nbytes, "reps": reps}}),
+          flush=True)
+
+
+def rocprof_summary(root, pattern):
+    """Compact text summary of rocprofv3 CSV output under root: per kernel whose name
+    contains pattern, the mean of each counter per dispatch and the kernel-trace stats."""
+    import collections
+    import csv
+    import glob
+    for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
+        acc = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if pattern in r.get("Kernel_Name", ""):
+                    acc[r["Kernel_Name"]][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for k, cs in acc.items():
+            for c, per in cs.items():
+                xs = list(per.values())
+                print(f"PMC {c} mean_per_dispatch {sum(xs) / len(xs):.6g} dispatches {len(xs)} kernel {k}")
+    for f in sorted(glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if pattern in r["Name"]:
+                    print(f"STATS calls {r['Calls']} avg_ns {float(r['AverageNs']):.1f} min_ns {r['MinNs']} "
+                          f"max_ns {r['MaxNs']} total_ns {r.get('TotalDurationNs', '?')} kernel {r['Name']}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,7 +173,17 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--only", action="store_true", help="time only --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="summarise rocprofv3 CSV output under DIR and exit (no GPU use)")
+    ap.add_argument("--kernel-pattern", default="",
+                    help="with --rocprof-summary: only kernels whose name contains this")
     args = ap.parse_args()
+
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary, args.kernel_pattern)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: rows are independent, so the path shards "
@@ -149,6 +196,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     head = time_workload(R, torch, args.workload, args.steps, args.warmup)
     also = []
