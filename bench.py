@@ -34,6 +34,7 @@ HEADLINE = "llama_4096_int4"
 OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096"]
 KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_fast2.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_device.h",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_generic.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_api.cpp"]

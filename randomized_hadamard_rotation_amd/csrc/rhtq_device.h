@@ -13,6 +13,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Streaming accesses: each input and output byte is touched once, so the loads and
 // stores carry the non-temporal hint (measured ~10% more HBM throughput on gfx950).
@@ -109,22 +110,116 @@ __device__ __forceinline__ void h12_forward(float* w) {
   }
 }
 
-// Maximum over aligned groups of G lanes (G a power of two, 1..64); every lane of the
-// group receives it.  Within 16 lanes by DPP; across rows by the gfx950 lane swaps.
+// Maximum of non-negative values over aligned groups of G lanes (G a power of two,
+// 1..64); every lane of the group receives it.  Non-negative floats order like their
+// bit patterns, so the comparisons are unsigned integer maxima, which fold the DPP lane
+// moves into the max.  Within 16 lanes by DPP; across rows by the gfx950 lane swaps.
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ float group_max(float v, int G) {
-  if (G >= 2) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  if (G >= 4) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  if (G >= 8) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  if (G >= 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  uint32_t u = __float_as_uint(v);
+  if (G >= 2) u = umax(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));
+  if (G >= 4) u = umax(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));
+  if (G >= 8) u = umax(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));
+  if (G >= 16) u = umax(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));
   if (G >= 32) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    u = umax(p[0], p[1]);
   }
   if (G >= 64) {
-    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    u = umax(p[0], p[1]);
   }
-  return v;
+  return __uint_as_float(u);
+}
+
+// ---- two-stage matrix-core transform helpers ----
+
+// Stage-2 B operand of v_mfma_f32_16x16x32_f16: the +-1 H32 over element bits 5-9.
+// k = 8 (lane >> 4) + e stands for bits 5,6 = e & 3, bits 7,8 = lane >> 4, bit 9 = e >> 2;
+// column n = lane & 15 stands for output bits 5-8 and tile t2 for output bit 9.
+__device__ __forceinline__ f16x8 h32_stage2_operand(int lane, int t2) {
+  uint16_t bits[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = (e & 3) | ((lane >> 4) << 2) | ((e >> 2) << 4);
+    const int n = (lane & 15) | (t2 << 4);
+    bits[e] = (__builtin_popcount(k & n) & 1) ? 0xBC00 : 0x3C00;
+  }
+  f16x8 r;
+  __builtin_memcpy(&r, bits, 16);
+  return r;
+}
+
+// Maxima of non-negative values compare as unsigned bit patterns (see group_max).
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return __uint_as_float(umax(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false)));
+}
+
+// Pairwise exchange across lane bit 4 (rows of 16 lanes 0<->1, 2<->3) followed by max:
+// the result holds a's maxima in rows 0 and 2 and b's in rows 1 and 3.
+__device__ __forceinline__ float swap16_max(float a, float b) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(umax(p[0], p[1]));
+}
+// Same across lane bit 5 (halves of 32 lanes): a's maxima in rows 0-1, b's in rows 2-3.
+__device__ __forceinline__ float swap32_max(float a, float b) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(umax(p[0], p[1]));
+}
+// Inverse of the compaction: x holds (rows 0, 2 -> a; rows 1, 3 -> b); returns a and b
+// broadcast over the row pairs.
+__device__ __forceinline__ void expand16(float x, float& a, float& b) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(p[0]);
+  b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void expand32(float x, float& a, float& b) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(p[0]);
+  b = __uint_as_float(p[1]);
+}
+
+// Power-of-two split scale for a row whose largest |stage-1 value| has the bits mb:
+// S = 2^(14 - e) with e the exponent of that maximum, so |y S| < 2^15; returned with
+// its inverse, both kept within the normal range.
+__device__ __forceinline__ void split_scale(uint32_t mb, float& S, float& invS) {
+  int be = 268 - (int)((mb >> 23) & 0xFF);   // biased exponent of 2^(14 - e)
+  be = be < 1 ? 1 : (be > 253 ? 253 : be);
+  S = __uint_as_float((uint32_t)be << 23);
+  invS = __uint_as_float((uint32_t)(254 - be) << 23);
+}
+
+// Eight values y scaled by S, split into f16 pairs: hi = f16(y S) and lo = f16(y S - hi),
+// both nearest even; y S - hi is exact in fp32, so hi + lo carries 22 significant bits.
+// Word k of hi / lo holds elements 2k (low half) and 2k + 1 (high half).  Written with
+// v_fma_mixlo/mixhi_f16 so that each half costs one instruction and lo reads hi through
+// op_sel; the order keeps every half-register write at least one instruction away from
+// its reader, and the closing s_nop covers the VALU-write to matrix-core-read distance.
+__device__ __forceinline__ void split8(const float* y, float S, uint32_t* hi, uint32_t* lo) {
+  asm("v_fma_mixlo_f16 %0, %8, %16, 0\n\t"
+      "v_fma_mixlo_f16 %1, %10, %16, 0\n\t"
+      "v_fma_mixlo_f16 %2, %12, %16, 0\n\t"
+      "v_fma_mixlo_f16 %3, %14, %16, 0\n\t"
+      "v_fma_mixhi_f16 %0, %9, %16, 0\n\t"
+      "v_fma_mixhi_f16 %1, %11, %16, 0\n\t"
+      "v_fma_mixhi_f16 %2, %13, %16, 0\n\t"
+      "v_fma_mixhi_f16 %3, %15, %16, 0\n\t"
+      "v_fma_mixlo_f16 %4, %8, %16, -%0 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %5, %10, %16, -%1 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %6, %12, %16, -%2 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %7, %14, %16, -%3 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %4, %9, %16, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %5, %11, %16, -%1 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %6, %13, %16, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %7, %15, %16, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]),
+        "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3])
+      : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]),
+        "v"(S));
 }
 
 // E4M3FN (OCP FP8) code of s >= 0: nearest value, ties to even mantissa, saturating at

@@ -132,7 +132,6 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     float v[S::NF][2][4];
 #pragma unroll
     for (int f = 0; f < S::NF; ++f) {
-      const int off = 512 * f + 32 * (lane & 15) + 8 * (lane >> 4);
       const uint4 m = sign_tab[f * 64 + lane];
       uint4 r = raw[f];
       r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
@@ -406,6 +405,10 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s) {
   if (getenv_fast_disabled()) return hipErrorNotSupported;
   if (a.n == 12288) return launch_fast12(op, a, s);
+  if (!getenv_fast2_disabled()) {
+    const hipError_t e = launch_fast2(op, a, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   switch (op) {
     case OP_ROTATE: return dispatch<OP_ROTATE>(a, s);
     case OP_INT4: return dispatch<OP_INT4>(a, s);

@@ -3,24 +3,26 @@
 // Hadamard-compatible; QuaRot reviews, review 2 Questions: non-power-of-two widths
 // need an extra factor next to the power-of-two transform).
 //
-// Index j = 1024 j1 + j2 (j1 < 12, j2 < 1024); H_12288 = H12 (x) H1024.  The two waves
-// of a workgroup share one row: wave h holds the half j2 bit 9 = h of all twelve
-// sub-rows (96 values per lane), which keeps the per-lane state low enough for two
-// waves per SIMD.  Per row:
+// Index j = 1024 j1 + j2 (j1 < 12, j2 < 1024); H_12288 = H12 (x) H1024 and the factors
+// commute.  The two waves of a workgroup share one row; wave h holds the sub-rows
+// j1 = 6h .. 6h + 5 (96 values per lane).  Per row:
 //
-//  1. 16-byte loads in the MFMA A layout (element 1024 j1 + 512 h + 32 (l & 15) +
-//     8 (l >> 4) + e), random signs by XOR with bf16 sign masks from an LDS table.
-//  2. Bits 0-4 of j2 on v_mfma_f32_16x16x32_bf16 against the +-1 H32 operand.
-//  3. Bits 5-6 in registers; bits 7-8 through v_permlane16/32_swap and registers.
-//  4. The order-12 Williamson factor across the twelve sub-rows, in registers.
-//  5. Bit 9 couples the two waves: each sub-row is exchanged through a double-buffered
-//     LDS chunk; wave h reads the element pairs (j2, j2 + 512) of its own output half
-//     (8 consecutive j2 per lane) and forms a + b (h = 0) or a - b (h = 1).  The same
-//     pass leaves 8 consecutive outputs per lane for the epilogue.
-//  6. Epilogue as in the other fast kernels: group maxima by DPP, INT4 magic-constant
-//     rounding or E2M1 conversion, packed 4-byte stores.
+//  1. 16-byte loads in the MFMA A layout, random signs by XOR of bf16 sign bits.
+//  2. H1024 of each sub-row on the matrix cores, as in the 1024..4096 kernel: bits 0-4 on
+//     v_mfma_f32_16x16x32_bf16, bits 5-9 on v_mfma_f32_16x16x32_f16 with every value
+//     split into two f16 terms under a power-of-two scale S.  Afterwards the lane holds,
+//     per sub-row and per half t2 = j2 bit 9, eight consecutive outputs.
+//  3. Exchange through LDS: wave h keeps the half t2 = h of every sub-row, so it sends
+//     its other half (48 values per lane, in two steps) and receives the other wave's
+//     half t2 = h of the six sub-rows it lacks, rescaled to its own S.
+//  4. The order-12 Williamson factor in registers across the twelve sub-rows.
+//  5. Epilogue on the twelve 512-element chunks 1024 j1 + 512 h + [0, 512): group
+//     maxima, scales, INT4 or E2M1 codes, packed stores straight from registers.
+#include <hip/hip_fp16.h>
+
 #include "rhtq.h"
 #include "rhtq_device.h"
+#include "rhtq_epilogue.h"
 #include "rhtq_internal.h"
 
 namespace rhtq {
@@ -30,240 +32,222 @@ constexpr int kW = 2;              // waves per workgroup (one row)
 constexpr int kT = 64 * kW;
 constexpr int kN = 12288;
 constexpr int kSub = 12;           // sub-rows of 1024
-constexpr int kTB = 1024 + 128;    // padded chunk buffer (floats)
+constexpr int kOwn = 6;            // sub-rows per wave
+constexpr int kX = kOwn * 4;       // values per lane in one exchange step
 
-// 4 padding floats after every 32: the 8-byte pair stores and the 16-byte reads of
-// 8 consecutive floats per lane then touch distinct LDS banks
-__device__ __forceinline__ int tp(int j) { return j + ((j >> 5) << 2); }
-
-// element offset (within a row) of this lane's 8 loaded values of sub-row j1
-__device__ __forceinline__ int load_off(int j1, int h, int lane) {
-  return 1024 * j1 + 512 * h + 32 * (lane & 15) + 8 * (lane >> 4);
+// element offset (within a row) of the 8 values this lane loads for own sub-row jl, fragment f
+__device__ __forceinline__ int load_off(int h, int jl, int f, int lane) {
+  return 1024 * (kOwn * h + jl) + 512 * f + 32 * (lane & 15) + 8 * (lane >> 4);
 }
 
-template <int OP>
-__global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
-  __shared__ float tbuf[2][kTB];
-  __shared__ float rowmax[kW];
-  __shared__ uint4 sign_tab[kSub * kW * 64];   // bf16 sign-bit masks in load order
-  const int lane = threadIdx.x & 63;
-  const int h = threadIdx.x >> 6;
+struct Shared12 {
+  uint4 sign_tab[kW * kOwn * 2 * 64];   // bf16 sign-bit masks in load order
+  float xbuf[kW][kX][64];               // exchange buffer, one step of each wave
+  float xs[kW];                         // inverse split scale of each wave
+  float rmax[kW];                       // per-token row maximum of each wave
+};
+
+// Rows of the workgroup as seen by wave H (a template parameter, so that every register
+// array is indexed by constants).  Both waves pass the same barriers in the same order.
+template <int OP, int H>
+__device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, const bf16x8 (&hb)[2],
+                                            const f16x8 (&hc)[2], const int lane, const float gts,
+                                            const float inv6g, const int G) {
+  constexpr int h = H, other = 1 - H;
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)kN));
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
-
-  // bf16 sign-bit masks in load order: entry (j1 * 2 + h) * 64 + lane covers the 8 elements
-  // that lane loads for sub-row j1 in wave h, so the table reads are conflict-free
-  for (int k = threadIdx.x; k < kSub * kW * 64; k += kT) {
-    uint4 m = make_uint4(0, 0, 0, 0);
-    if (a.signs) {
-      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + load_off(k >> 7, (k >> 6) & 1, k & 63));
-      m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
-      m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
-      m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
-      m.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
-    }
-    sign_tab[k] = m;
-  }
-  __syncthreads();
-  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
-  float gts = 0.0f, inv6g = 0.0f;
-  if constexpr (OP == OP_NVFP4) {
-    gts = a.tensor_scale[0];
-    inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
-  }
-  const int group = a.group;
   float run_max = 0.0f;
+  const int lc = (lane >> 4) | ((lane & 15) << 2);
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-    const int64_t rbase = row * kN;
-    float v[kSub][2][4];
+    const int64_t relem0 = row * kN;
+    // ---------------- H1024 of the own sub-rows ----------------
+    float d1[kOwn][2][2][4];   // [jl][f][t][i]
 #pragma unroll
-    for (int j1 = 0; j1 < kSub; ++j1) {
-      uint4 r = ld_stream(x + rbase + load_off(j1, h, lane));
-      const uint4 mk = sign_tab[(j1 * kW + h) * 64 + lane];
-      r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
-      bf16x8 av;
-      __builtin_memcpy(&av, &r, 16);
-      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
-      const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+    for (int jl = 0; jl < kOwn; ++jl)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { v[j1][0][i] = d0[i]; v[j1][1][i] = d1[i]; }
-    }
-    // bits 5, 6 (register index i)
+      for (int f = 0; f < 2; ++f) {
+        uint4 r = ld_stream(x + relem0 + load_off(h, jl, f, lane));
+        const uint4 mk = sh.sign_tab[((h * kOwn + jl) * 2 + f) * 64 + lane];
+        r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
+        bf16x8 av;
+        __builtin_memcpy(&av, &r, 16);
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
+        const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
 #pragma unroll
-    for (int j1 = 0; j1 < kSub; ++j1)
+        for (int i = 0; i < 4; ++i) { d1[jl][f][0][i] = p0[i]; d1[jl][f][1][i] = p1[i]; }
+      }
+    float m1 = 0.0f;
+#pragma unroll
+    for (int jl = 0; jl < kOwn; ++jl)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fabsf(d1[jl][f][t][i]));
+    m1 = group_max(m1, 64);
+    float S, invS;
+    split_scale(__float_as_uint(m1), S, invS);
+
+    // d2[jl][t][t2][i2]: element 1024 j1 + 512 t2 + 8 lc + t + 2 i2
+    float d2[kOwn][2][2][4];
+#pragma unroll
+    for (int jl = 0; jl < kOwn; ++jl)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        bfly(v[j1][t][0], v[j1][t][1]);
-        bfly(v[j1][t][2], v[j1][t][3]);
-        bfly(v[j1][t][0], v[j1][t][2]);
-        bfly(v[j1][t][1], v[j1][t][3]);
+        float ys[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ys[e] = d1[jl][e >> 2][t][e & 3];
+        uint32_t hw[4], lw[4];
+        split8(ys, S, hw, lw);
+        f16x8 ah, al;
+        __builtin_memcpy(&ah, hw, 16);
+        __builtin_memcpy(&al, lw, 16);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+          f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, hc[t2], z, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, hc[t2], acc, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d2[jl][t][t2][i] = acc[i];
+        }
       }
-    // order-12 factor across the sub-rows
+
+    // ---------------- exchange the halves ----------------
+    // w[j1][t][i2]: the twelve sub-rows at this wave's half t2 = h, in this wave's units
+    float w[kSub][2][4];
+#pragma unroll
+    for (int jl = 0; jl < kOwn; ++jl)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[kOwn * h + jl][t][i] = d2[jl][t][h][i];
+    float rho = 1.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      __syncthreads();   // the other wave has read the previous contents of xbuf
+#pragma unroll
+      for (int jl = 0; jl < kOwn; ++jl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sh.xbuf[h][jl * 4 + i][lane] = d2[jl][t][other][i];
+      if (t == 0 && lane == 0) sh.xs[h] = invS;
+      __syncthreads();
+      if (t == 0) rho = S * sh.xs[other];   // ratio of two powers of two: exact
+#pragma unroll
+      for (int jl = 0; jl < kOwn; ++jl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[kOwn * other + jl][t][i] = sh.xbuf[other][jl * 4 + i][lane] * rho;
+    }
+
+    // ---------------- order-12 factor ----------------
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float w[kSub];
+        float v[kSub];
 #pragma unroll
-        for (int j1 = 0; j1 < kSub; ++j1) w[j1] = v[j1][t][i];
-        h12_forward(w);
+        for (int j1 = 0; j1 < kSub; ++j1) v[j1] = w[j1][t][i];
+        h12_forward(v);
 #pragma unroll
-        for (int j1 = 0; j1 < kSub; ++j1) v[j1][t][i] = w[j1];
+        for (int j1 = 0; j1 < kSub; ++j1) w[j1][t][i] = v[j1];
       }
-    // bits 7, 8 (lane bits 4, 5) exchanged with register bits 5, 6
-#pragma unroll
-    for (int j1 = 0; j1 < kSub; ++j1)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j1][t][i]),
-                                                    __float_as_uint(v[j1][t][i + 1]), false, false);
-          v[j1][t][i] = __uint_as_float(p[0]);
-          v[j1][t][i + 1] = __uint_as_float(p[1]);
-          bfly(v[j1][t][i], v[j1][t][i + 1]);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j1][t][i]),
-                                                    __float_as_uint(v[j1][t][i + 2]), false, false);
-          v[j1][t][i] = __uint_as_float(p[0]);
-          v[j1][t][i + 2] = __uint_as_float(p[1]);
-          bfly(v[j1][t][i], v[j1][t][i + 2]);
-        }
-      }
-    // Element of (j1, t, i) now: j2 = 512 h + 128 i + 32 (lane >> 4) + 2 (lane & 15) + t.
 
-    // bit 9: exchange each sub-row through LDS; this wave keeps j2 = 512 h + 8 lane + r
-    float yo[kSub][8];
-#pragma unroll
-    for (int c = 0; c < kSub; ++c) {
-      float* buf = tbuf[c & 1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int jl = 512 * h + 128 * i + 32 * (lane >> 4) + 2 * (lane & 15);
-        *reinterpret_cast<float2*>(buf + tp(jl)) = make_float2(v[c][0][i], v[c][1][i]);
-      }
-      __syncthreads();
-      const float4 lo0 = *reinterpret_cast<const float4*>(buf + tp(8 * lane));
-      const float4 lo1 = *reinterpret_cast<const float4*>(buf + tp(8 * lane + 4));
-      const float4 up0 = *reinterpret_cast<const float4*>(buf + tp(512 + 8 * lane));
-      const float4 up1 = *reinterpret_cast<const float4*>(buf + tp(512 + 8 * lane + 4));
-      const float sg = h == 0 ? 1.0f : -1.0f;
-      yo[c][0] = __builtin_fmaf(sg, up0.x, lo0.x);
-      yo[c][1] = __builtin_fmaf(sg, up0.y, lo0.y);
-      yo[c][2] = __builtin_fmaf(sg, up0.z, lo0.z);
-      yo[c][3] = __builtin_fmaf(sg, up0.w, lo0.w);
-      yo[c][4] = __builtin_fmaf(sg, up1.x, lo1.x);
-      yo[c][5] = __builtin_fmaf(sg, up1.y, lo1.y);
-      yo[c][6] = __builtin_fmaf(sg, up1.z, lo1.z);
-      yo[c][7] = __builtin_fmaf(sg, up1.w, lo1.w);
-    }
+    // chunk q = j1: elements 1024 q + 512 h + 8 lc + r
+    auto val = [&](int q, int r) -> float { return w[q][r & 1][r >> 1]; };
+    auto cbase = [&](int q) -> int { return 1024 * q + 512 * h; };
 
     if constexpr (OP == OP_AMAX) {
-#pragma unroll
-      for (int c = 0; c < kSub; ++c)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) run_max = fmaxf(run_max, fabsf(yo[c][r]));
-      continue;
-    }
-
-    // per-token INT4: maximum of the whole row across both waves
-    Int4Scale row_sc{0.0f, 0.0f, false};
-    const bool row_group = (OP == OP_INT4) && (group == kN);
-    if (row_group) {
       float m = 0.0f;
 #pragma unroll
-      for (int c = 0; c < kSub; ++c)
+      for (int q = 0; q < kSub; ++q)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(yo[c][r]));
-      m = group_max(m, 64);
-      if (lane == 0) rowmax[h] = m;
-      __syncthreads();
-      row_sc = int4_scale(fmaxf(rowmax[0], rowmax[1]), cnorm, a.scale_dtype);
-    }
-
+        for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(val(q, r)));
+      run_max = fmaxf(run_max, m * invS);
+    } else if constexpr (OP == OP_ROTATE) {
 #pragma unroll
-    for (int c = 0; c < kSub; ++c) {
-      const int64_t g0 = rbase + 1024 * c + 512 * h + 8 * lane;   // first element of this lane
-      if constexpr (OP == OP_ROTATE) {
-        st_stream(a.y + g0, yo[c][0] * cnorm, yo[c][1] * cnorm, yo[c][2] * cnorm, yo[c][3] * cnorm);
-        st_stream(a.y + g0 + 4, yo[c][4] * cnorm, yo[c][5] * cnorm, yo[c][6] * cnorm, yo[c][7] * cnorm);
-      } else if constexpr (OP == OP_INT4) {
-        Int4Scale sc = row_sc;
-        int lpg = 64;
-        if (!row_group) {
-          float m = 0.0f;
+      for (int q = 0; q < kSub; ++q) {
+        float o[8];
 #pragma unroll
-          for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(yo[c][r]));
-          lpg = group >> 3;
-          sc = int4_scale(group_max(m, lpg), cnorm, a.scale_dtype);
-        }
-        uint32_t qb[8];
-        if (__builtin_amdgcn_ballot_w64(sc.clamp) == 0) {
-#pragma unroll
-          for (int r = 0; r < 8; ++r) qb[r] = __float_as_uint(__builtin_fmaf(yo[c][r], sc.inv, 12582912.0f));
-        } else {
-#pragma unroll
-          for (int r = 0; r < 8; ++r)
-            qb[r] = __float_as_uint(__builtin_amdgcn_fmed3f(yo[c][r] * sc.inv, -8.0f, 7.0f) + 12582912.0f);
-        }
-        st_stream(a.packed + (g0 >> 1), pack8_nibbles(qb));
-        const bool writer = row_group ? (c == 0 && h == 0 && lane == 0) : ((lane & (lpg - 1)) == 0);
-        if (writer) {
-          const int64_t gi = row_group ? row : (g0 >> __builtin_ctz((unsigned)group));
-          if (a.scale_dtype == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[gi] = sc.s;
-          else static_cast<__half*>(a.scales)[gi] = __float2half_rn(fminf(sc.s, 65504.0f));
-        }
-      } else if constexpr (OP == OP_NVFP4) {
-        // 16-element blocks over two lanes
-        float m = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(yo[c][r]));
-        m = group_max(m, 2);
-        const uint32_t code = e4m3_code((m * cnorm) * inv6g);
-        const float seff = e4m3_value(code) * gts;
-        const float inv = seff > 0.0f ? cnorm * __builtin_amdgcn_rcpf(seff) : 0.0f;
-        uint32_t w = 0;
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, yo[c][0] * inv, yo[c][1] * inv, 1.0f, 0);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, yo[c][2] * inv, yo[c][3] * inv, 1.0f, 1);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, yo[c][4] * inv, yo[c][5] * inv, 1.0f, 2);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, yo[c][6] * inv, yo[c][7] * inv, 1.0f, 3);
-        st_stream(a.packed + (g0 >> 1), seff > 0.0f ? w : 0u);   // zero-scale block -> code 0
-        if ((lane & 1) == 0) static_cast<uint8_t*>(a.scales)[g0 >> 4] = (uint8_t)code;
+        for (int r = 0; r < 8; ++r) o[r] = (val(q, r) * invS) * cnorm;
+        float* p = a.y + relem0 + cbase(q) + 8 * lc;
+        st_stream(p, o[0], o[1], o[2], o[3]);
+        st_stream(p + 4, o[4], o[5], o[6], o[7]);
       }
+    } else {
+      // per-token INT4: maximum of the whole row across both waves (uniform branch)
+      auto rowmax = [&](float m) -> float {
+        m = group_max(m, 64);
+        if (lane == 0) sh.rmax[h] = m;
+        __syncthreads();
+        return fmaxf(sh.rmax[0], sh.rmax[1]);
+      };
+      quant_epilogue<OP, kSub>(a, row, relem0, G, invS, cnorm, gts, inv6g, lane, lane == 0 && h == 0, val,
+                               cbase, rowmax);
     }
   }
 
   if constexpr (OP == OP_AMAX) {
     run_max = group_max(run_max, 64);
-    if (lane == 0) rowmax[h] = run_max;
+    if (lane == 0) sh.rmax[h] = run_max;
     __syncthreads();
-    if (threadIdx.x == 0)
-      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale),
-                __float_as_uint(fmaxf(rowmax[0], rowmax[1]) * cnorm));
+    if (h == 0 && lane == 0)
+      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(fmaxf(sh.rmax[0], sh.rmax[1]) * cnorm));
   }
+}
+
+
+template <int OP>
+__global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
+  __shared__ Shared12 sh;
+  const int lane = threadIdx.x & 63;
+  const int h = threadIdx.x >> 6;
+
+  for (int k = threadIdx.x; k < kW * kOwn * 2 * 64; k += kT) {
+    uint4 m = make_uint4(0, 0, 0, 0);
+    if (a.signs) {
+      const int kl = k & 63, f = (k >> 6) & 1, jl = (k >> 7) % kOwn, hh = (k >> 7) / kOwn;
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + load_off(hh, jl, f, kl));
+      m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
+      m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
+      m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
+      m.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
+    }
+    sh.sign_tab[k] = m;
+  }
+  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
+  __syncthreads();
+
+  float gts = 0.0f, inv6g = 0.0f;
+  if constexpr (OP == OP_NVFP4) {
+    gts = a.tensor_scale[0];
+    inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
+  }
+  int G = 0;   // log2 of the INT4 group (0: one group per row)
+  if constexpr (OP == OP_INT4) G = a.group == kN ? 0 : __builtin_ctz((unsigned)a.group);
+  if constexpr (OP == OP_NVFP4) G = 4;
+  if (h == 0) fast12_rows<OP, 0>(a, sh, hb, hc, lane, gts, inv6g, G);
+  else fast12_rows<OP, 1>(a, sh, hb, hc, lane, gts, inv6g, G);
 }
 
 template <int OP>
 hipError_t launch12(const KernelArgs& a, hipStream_t s) {
   if constexpr (OP == OP_INT4) {
-    if (!(a.group == kN || a.group <= 512)) return hipErrorNotSupported;
+    if (!(a.group == kN || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
   auto kern = fast12_kernel<OP>;
-  static const int max_blocks = [&] {
-    int dev = 0, cus = 256, per_cu = 1;
-    if (hipGetDevice(&dev) == hipSuccess)
-      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kT, 0) != hipSuccess ||
-        per_cu < 1)
+  static int max_blocks = 0;   // resident blocks per CU x CUs, computed once per instantiation
+  if (max_blocks == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorNotSupported;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kT, 0) != hipSuccess || per_cu < 1)
       per_cu = 1;
-    return cus * per_cu;
-  }();
-  const int64_t want = a.rows;
-  const int grid = (int)(want < max_blocks ? want : max_blocks);
+    max_blocks = cus * per_cu;
+  }
+  const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }

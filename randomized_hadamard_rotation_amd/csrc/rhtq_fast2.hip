@@ -1,0 +1,290 @@
+// Two-stage matrix-core kernel for bf16 rows of 1024, 2048 and 4096 elements.
+//
+// One wavefront owns one row at a time (persistent grid).  Per row:
+//
+//  1. Coalesced 16-byte loads in the MFMA A layout (lane l loads elements
+//     512 f + 32 (l & 15) + 8 (l >> 4) + e of fragment f); random signs by XOR of bf16
+//     sign bits with masks kept in LDS.
+//  2. Stage 1: index bits 0-4 on v_mfma_f32_16x16x32_bf16 against a +-1 H32 operand.
+//     bf16 times +-1 is exact, so this is the first five butterfly stages in fp32.
+//     The result of tile t, register i, holds element
+//         t + 2 (l & 15) + 32 i + 128 (l >> 4) + 512 f.
+//  3. Stage 2: index bits 5-9 on v_mfma_f32_16x16x32_f16.  The stage-1 registers are
+//     already in the A layout of this product (row = element bits 1-4, k = bits 5-9
+//     spread over the register index i, the lane bits 4-5 and the fragment bit 9), so no
+//     data moves between lanes.  fp32 does not fit an f16 operand, so each value y is
+//     split as y S = hi + lo (two f16 terms, S a power of two chosen from the row
+//     maximum so that |y S| < 2^15) and both halves go through the same +-1 operand;
+//     the two products accumulate in fp32.  The split keeps 22 significant bits, and
+//     the row-relative error stays near fp32 rounding.
+//  4. Bits 10 and up (2048, 4096) are register butterflies.  Each lane now holds eight
+//     consecutive outputs (element bits 0-2 in registers) and the 64 lanes cover 512
+//     consecutive elements, so codes and values are stored straight from registers.
+//  5. Epilogue: group maxima within the lane, then across lanes by pairwise
+//     v_permlane16/32_swap + max that also compacts the groups into fewer registers,
+//     so the scale arithmetic runs once per group; INT4 codes by the
+//     round-to-nearest-even magic-constant FMA, E2M1 by v_cvt_scalef32_pk_fp4_f32 with
+//     unit scale; nibble packing and 4-byte stores, 256 contiguous bytes per wave store.
+//
+// QuaRot reviews, review 1 Summary: online Hadamard by the Walsh-Hadamard fast
+// algorithm; review 2 Summary: random Hadamard transform then INT4; reviewer 2
+// follow-up: nearest rounding.  NVFP4 methodology thread: E2M1 codes with E4M3 block
+// scales.
+#include <hip/hip_fp16.h>
+
+#include "rhtq.h"
+#include "rhtq_device.h"
+#include "rhtq_epilogue.h"
+#include "rhtq_internal.h"
+
+namespace rhtq {
+namespace {
+
+constexpr int kWaves2 = 4;
+constexpr int kThreads2 = 64 * kWaves2;
+
+template <int LOGM>
+struct Shape2 {
+  static constexpr int N = 1 << LOGM;
+  static constexpr int NF = N / 512;        // stage-1 fragments (element bits 9..)
+  static constexpr int NG = NF / 2;         // stage-2 output groups (element bits 10..)
+  static constexpr int LOG_NG = LOGM - 10;
+  static constexpr int R = 2 * NG;          // 512-element chunks per row (t2, g)
+};
+
+template <int LOGM>
+__device__ __forceinline__ void load_row(const uint16_t* x, int64_t row, int64_t rows, int lane, uint4* raw) {
+  using S2 = Shape2<LOGM>;
+  if (row < rows) {   // past the last row raw[] is left as is: it is never used
+#pragma unroll
+    for (int f = 0; f < S2::NF; ++f) raw[f] = ld_stream(x + row * S2::N + 512 * f + 32 * (lane & 15) + 8 * (lane >> 4));
+  }
+}
+
+#ifndef RHTQ_FAST2_WAVES
+#define RHTQ_FAST2_WAVES 2
+#endif
+template <int LOGM, int OP, int DEPTH>
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RHTQ_FAST2_WAVES)))
+void fast2_kernel(KernelArgs a) {
+  using S2 = Shape2<LOGM>;
+  constexpr int N = S2::N, NF = S2::NF, NG = S2::NG, R = S2::R;
+  __shared__ uint4 sign_tab[NF * 64];
+  __shared__ float wmax[kWaves2];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const float cnorm = (float)(1.0 / __builtin_sqrt((double)N));
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const int64_t rstride = (int64_t)gridDim.x * kWaves2;
+  int64_t row = (int64_t)blockIdx.x * kWaves2 + wave;
+
+  // DEPTH rows of loads in flight per wave: raw (this row) and raw2 (the next one);
+  // DEPTH 0 loads each row at the top of its own step and relies on occupancy
+  uint4 raw[NF] = {}, raw2[NF] = {};
+  if constexpr (DEPTH >= 1) load_row<LOGM>(x, row, a.rows, lane, raw);
+  if constexpr (DEPTH == 2) load_row<LOGM>(x, row + rstride, a.rows, lane, raw2);
+
+  // bf16 sign-bit masks in load order: entry f * 64 + lane covers the 8 elements that
+  // lane loads for fragment f
+  for (int k = threadIdx.x; k < NF * 64; k += kThreads2) {
+    uint4 m = make_uint4(0, 0, 0, 0);
+    if (a.signs) {
+      const int kl = k & 63;
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + 512 * (k >> 6) + 32 * (kl & 15) + 8 * (kl >> 4));
+      m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
+      m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
+      m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
+      m.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
+    }
+    sign_tab[k] = m;
+  }
+  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
+  __syncthreads();
+
+  float gts = 0.0f, inv6g = 0.0f;
+  if constexpr (OP == OP_NVFP4) {
+    gts = a.tensor_scale[0];
+    inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
+  }
+  int G = 0;   // log2 of the INT4 group (0: one group per row)
+  if constexpr (OP == OP_INT4) G = a.group == N ? 0 : __builtin_ctz((unsigned)a.group);
+  if constexpr (OP == OP_NVFP4) G = 4;
+  float run_max = 0.0f;
+  // lane chunk: element bits 3-4 = lane >> 4, bits 5-8 = lane & 15
+  const int lc = (lane >> 4) | ((lane & 15) << 2);
+
+  auto step = [&](const int64_t row, uint4 (&raw)[NF]) {
+    if constexpr (DEPTH == 0) load_row<LOGM>(x, row, a.rows, lane, raw);
+    // ---------------- stage 1 ----------------
+    float d1[NF][2][4];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint4 m = sign_tab[f * 64 + lane];
+      uint4 r = raw[f];
+      r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
+      bf16x8 av;
+      __builtin_memcpy(&av, &r, 16);
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
+      const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { d1[f][0][i] = p0[i]; d1[f][1][i] = p1[i]; }
+    }
+    // raw[] is consumed: it now receives the row DEPTH steps ahead, whose loads run
+    // during the work of this and the following rows
+    if constexpr (DEPTH >= 1) load_row<LOGM>(x, row + DEPTH * rstride, a.rows, lane, raw);
+
+    // ---------------- split scale ----------------
+    float m1 = 0.0f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fabsf(d1[f][t][i]));
+    m1 = group_max(m1, 64);
+    float S, invS;
+    split_scale(__float_as_uint(m1), S, invS);
+
+    // ---------------- stage 2 ----------------
+    // d2[t][g][t2][i2] holds element t + 2 i2 + 8 lc + 512 t2 + 1024 g
+    float d2[2][NG][2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float ys[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ys[e] = d1[2 * g + (e >> 2)][t][e & 3];
+        uint32_t hw[4], lw[4];
+        split8(ys, S, hw, lw);
+        f16x8 ah, al;
+        __builtin_memcpy(&ah, hw, 16);
+        __builtin_memcpy(&al, lw, 16);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+          f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, hc[t2], z, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, hc[t2], acc, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d2[t][g][t2][i] = acc[i];
+        }
+      }
+    // bits 10..: register butterflies over g
+#pragma unroll
+    for (int b = 0; b < S2::LOG_NG; ++b)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        if ((g & (1 << b)) == 0)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) bfly(d2[t][g][t2][i], d2[t][g | (1 << b)][t2][i]);
+
+    // chunk q = t2 + 2 g: 8 consecutive elements per lane, y8[r] = element 8 lc + r
+    auto val = [&](int q, int r) -> float { return d2[r & 1][q >> 1][q & 1][r >> 1]; };
+
+    if constexpr (OP == OP_AMAX) {
+      float m = 0.0f;
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(val(q, r)));
+      run_max = fmaxf(run_max, m * invS);   // across lanes at the end
+      return;
+    }
+
+    const int64_t ebase = row * N;   // first element of the row
+
+    if constexpr (OP == OP_ROTATE) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        float o[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) o[r] = (val(q, r) * invS) * cnorm;
+        float* p = a.y + ebase + 512 * q + 8 * lc;
+        st_stream(p, o[0], o[1], o[2], o[3]);
+        st_stream(p + 4, o[4], o[5], o[6], o[7]);
+      }
+      return;
+    }
+
+    if constexpr (OP == OP_INT4 || OP == OP_NVFP4)
+      quant_epilogue<OP, R>(a, row, ebase, G, invS, cnorm, gts, inv6g, lane, lane == 0, val,
+                            [](int q) { return 512 * q; }, [](float m) { return group_max(m, 64); });
+  };
+  if constexpr (DEPTH <= 1) {
+    for (; row < a.rows; row += rstride) step(row, raw);
+  } else {
+    for (; row < a.rows; row += 2 * rstride) {
+      step(row, raw);
+      if (row + rstride < a.rows) step(row + rstride, raw2);
+    }
+  }
+
+  if constexpr (OP == OP_AMAX) {
+    run_max = group_max(run_max, 64);
+    if (lane == 0) wmax[wave] = run_max;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = wmax[0];
+#pragma unroll
+      for (int w = 1; w < kWaves2; ++w) m = fmaxf(m, wmax[w]);
+      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(m * cnorm));
+    }
+  }
+}
+
+template <int LOGM, int OP>
+hipError_t launch2(const KernelArgs& a, hipStream_t s) {
+  using S2 = Shape2<LOGM>;
+  if constexpr (OP == OP_INT4) {
+    if (!(a.group == S2::N || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
+  }
+#ifdef RHTQ_FAST2_DEPTH
+  auto kern = fast2_kernel<LOGM, OP, RHTQ_FAST2_DEPTH>;
+#else
+  auto kern = fast2_kernel<LOGM, OP, 2>;
+#endif
+  static int max_blocks = 0;   // resident blocks per CU x CUs, computed once per instantiation
+  if (max_blocks == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorNotSupported;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kThreads2, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    max_blocks = cus * per_cu;
+  }
+  const int64_t want = (a.rows + kWaves2 - 1) / kWaves2;
+  const int grid = (int)(want < max_blocks ? want : max_blocks);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads2), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int OP>
+hipError_t dispatch2(const KernelArgs& a, hipStream_t s) {
+  switch (a.n) {
+    case 1024: return launch2<10, OP>(a, s);
+    case 2048: return launch2<11, OP>(a, s);
+    case 4096: return launch2<12, OP>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s) {
+  switch (op) {
+    case OP_ROTATE: return dispatch2<OP_ROTATE>(a, s);
+    case OP_INT4: return dispatch2<OP_INT4>(a, s);
+    case OP_NVFP4: return dispatch2<OP_NVFP4>(a, s);
+    case OP_AMAX: return dispatch2<OP_AMAX>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace rhtq

@@ -44,10 +44,22 @@ hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
 // Two-wave kernel for 12288-wide rows (called by launch_fast).
 hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s);
 
+// Two-stage matrix-core kernel for 1024-, 2048- and 4096-wide rows (called by launch_fast).
+hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s);
+
 // RHTQ_FORCE_GENERIC=1 routes every call to the generic kernels (read once).
 inline bool getenv_fast_disabled() {
   static const bool v = [] {
     const char* e = getenv("RHTQ_FORCE_GENERIC");
+    return e != nullptr && e[0] == '1';
+  }();
+  return v;
+}
+
+// RHTQ_DISABLE_FAST2=1 keeps 1024..4096-wide rows on the single-stage kernel (read once).
+inline bool getenv_fast2_disabled() {
+  static const bool v = [] {
+    const char* e = getenv("RHTQ_DISABLE_FAST2");
     return e != nullptr && e[0] == '1';
   }();
   return v;
