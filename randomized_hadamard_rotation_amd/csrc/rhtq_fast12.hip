@@ -59,6 +59,19 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
   float run_max = 0.0f;
   const int lc = (lane >> 4) | ((lane & 15) << 2);
 
+  // loads of one row (12 x 16 bytes per lane); the next row's go out as soon as stage 1
+  // has consumed these registers, so they run during this row's work
+  uint4 raw[kOwn][2] = {};
+  auto load = [&](int64_t r) {
+    if (r < a.rows) {
+#pragma unroll
+      for (int jl = 0; jl < kOwn; ++jl)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) raw[jl][f] = ld_stream(x + r * kN + load_off(h, jl, f, lane));
+    }
+  };
+  load(blockIdx.x);
+
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const int64_t relem0 = row * kN;
     // ---------------- H1024 of the own sub-rows ----------------
@@ -67,7 +80,7 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
     for (int jl = 0; jl < kOwn; ++jl)
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        uint4 r = ld_stream(x + relem0 + load_off(h, jl, f, lane));
+        uint4 r = raw[jl][f];
         const uint4 mk = sh.sign_tab[((h * kOwn + jl) * 2 + f) * 64 + lane];
         r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
         bf16x8 av;
@@ -78,6 +91,7 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) { d1[jl][f][0][i] = p0[i]; d1[jl][f][1][i] = p1[i]; }
       }
+    load(row + gridDim.x);
     float m1 = 0.0f;
 #pragma unroll
     for (int jl = 0; jl < kOwn; ++jl)
