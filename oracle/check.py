@@ -14,6 +14,9 @@ R3  codes: compared with the oracle's codes recomputed from the device's stored
     such codes may make up at most 1e-4 of all codes.
 R4  invariants of the device output, in groups whose stored scale is a normal number of
     its storage type: INT4 codes in [-7, 7]; dequantisation error within half a step.
+MXFP4 scales (E8M0 bytes) are exponents: equal, except adjacent where the oracle's block
+maximum lies within 1e-6 relative of a power of two (the floor of log2 is a boundary case
+there); codes then follow R3 under the device's stored scales.
 """
 from __future__ import annotations
 
@@ -155,6 +158,36 @@ def check_nvfp4(packed_dev, sc_dev, g_dev, y_ref, g_ref=None) -> dict:
     same_sign = (c_dev & 8) == (c_ref & 8)
     one_step = same_sign & (np.abs(mag_dev - mag_ref) == 1)
     # +-0: both magnitudes zero, only the sign differs, |v| tiny
+    signed_zero = (mag_dev == 0) & (mag_ref == 0) & (av < INT4_BOUNDARY_BAND)
+    dist = np.where(signed_zero, 0.0, dist)
+    rep["code_mismatches"] = _code_mismatch_check(c_dev, c_ref, v, dist, one_step | signed_zero,
+                                                  "E2M1")
+    return rep
+
+
+def check_mxfp4(packed_dev, sb_dev, y_ref) -> dict:
+    rep = {}
+    T, n = y_ref.shape
+    bmax = np.max(np.abs(y_ref.reshape(T, n // 32, 32)), axis=-1)
+    sb_ref = (O.mxfp4_scale_exponent(bmax) + 127).astype(np.uint8)
+    sb_dev = np.asarray(sb_dev, dtype=np.uint8).reshape(sb_ref.shape)
+    diff = sb_dev != sb_ref
+    adjacent = np.abs(sb_dev.astype(int) - sb_ref.astype(int)) == 1
+    # distance of bmax to the power of two between the two candidate exponents
+    p2 = np.ldexp(1.0, np.maximum(sb_dev, sb_ref).astype(np.int64) - 127 + 2)
+    near = np.abs(bmax - p2) <= SCALE_REL * p2
+    bad = diff & ~(adjacent & near)
+    if np.any(bad):
+        i = tuple(np.argwhere(bad)[0])
+        raise ParityError(f"R2: E8M0 scale at {i}: {sb_dev[i]} vs {sb_ref[i]} (block max {bmax[i]!r})")
+    rep["scale_boundary_cases"] = int(np.sum(diff))
+    c_dev = O.unpack_nibbles(packed_dev, signed=False).astype(np.uint8)
+    c_ref, v = O.mxfp4_codes_from_scales(y_ref, sb_dev)
+    av = np.abs(v)
+    dist = np.min(np.abs(av[..., None] - _E2M1_BOUNDS), axis=-1)
+    mag_dev, mag_ref = (c_dev & 7).astype(int), (c_ref & 7).astype(int)
+    same_sign = (c_dev & 8) == (c_ref & 8)
+    one_step = same_sign & (np.abs(mag_dev - mag_ref) == 1)
     signed_zero = (mag_dev == 0) & (mag_ref == 0) & (av < INT4_BOUNDARY_BAND)
     dist = np.where(signed_zero, 0.0, dist)
     rep["code_mismatches"] = _code_mismatch_check(c_dev, c_ref, v, dist, one_step | signed_zero,

@@ -25,7 +25,11 @@ Sources (web pages on the subject; cited by title and section):
   is Hadamard-compatible.
 * "Methodology checks for NVFP4 W4A4 on Qwen3-8B" (rstation thread), the
   NVFP4 results and the block-Hadamard comment: NVFP4 = E2M1 codes with FP8
-  E4M3 block scales (16-wide blocks) plus a tensor scale; INT4-g128.
+  E4M3 block scales (16-wide blocks) plus a tensor scale; INT4-g128; MXFP4 is
+  compared against both after block-Hadamard rotation.
+* The pages name MXFP4 but do not define it; its definition is the public OCP
+  Microscaling Formats (MX) v1.0 specification: blocks of 32 elements share
+  one power-of-two scale stored as E8M0, elements are E2M1.
 
 Where the pages are silent the oracle takes these readings:
   R-norm   the transform is orthonormal: y = H_n D x / sqrt(n)
@@ -42,6 +46,11 @@ Where the pages are silent the oracle takes these readings:
            |y| / (dec(s_b) g), ties to even; sign kept on values that round to 0
   R-e4m3   OCP FP8 E4M3FN: bias 7, max 448, subnormals, NaN never produced
   R-e2m1   OCP MX E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} <-> codes 0..7
+  R-mxfp4  per 32-block X = 2^(floor(log2(blockmax)) - 2) (2 = exponent of the
+           largest E2M1 normal, 6 = 1.5 * 2^2), exponent clamped to [-127, 127]
+           and stored as the E8M0 byte exponent + 127; codes = sign bit | E2M1 of
+           |y| / X (ties to even, saturating at 6); an all-zero block stores
+           exponent -127 and codes 0
 
 Parity of the H12 choice, the sign generator, the nibble order, the +-0 rule
 and the NVFP4 amax source is by convention: the pages fix none of them
@@ -57,7 +66,8 @@ __all__ = [
     "inverse_rotate", "int4_scale_store", "int4_codes", "quantize_int4", "pack_nibbles",
     "unpack_nibbles", "e4m3_values", "e4m3_encode", "e4m3_decode", "e2m1_values",
     "e2m1_encode", "e2m1_decode", "nvfp4_tensor_scale", "quantize_nvfp4",
-    "nvfp4_codes_from_scales", "forward", "dequantize", "inverse",
+    "nvfp4_codes_from_scales", "mxfp4_scale_exponent", "mxfp4_codes_from_scales",
+    "quantize_mxfp4", "forward", "dequantize", "inverse",
 ]
 
 
@@ -365,6 +375,41 @@ def quantize_nvfp4(y, tensor_scale=None):
     return codes, sc, g, v
 
 
+def mxfp4_scale_exponent(bmax) -> np.ndarray:
+    """Shared exponent of MX blocks with maxima bmax (OCP MX v1.0, shared scale):
+    floor(log2(bmax)) - 2, clamped to [-127, 127]; -127 for an all-zero block.
+    floor(log2) is read off frexp, which is exact for every positive double."""
+    bmax = np.asarray(bmax, dtype=np.float64)
+    _, ex = np.frexp(np.where(bmax > 0, bmax, 1.0))   # bmax = m * 2^ex, 0.5 <= m < 1
+    e = np.where(bmax > 0, ex - 1 - 2, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def mxfp4_codes_from_scales(y, scale_bytes):
+    """E2M1 codes of 32-blocks for given E8M0 scale bytes (exponent + 127).
+    Returns (codes uint8 [T][n], v fp64 = y / X).  Blocks whose maximum is zero store
+    code 0 (their values are all zero)."""
+    y = np.asarray(y, dtype=np.float64)
+    T, n = y.shape
+    yb = y.reshape(T, n // 32, 32)
+    X = np.ldexp(1.0, np.asarray(scale_bytes, dtype=np.int64) - 127).reshape(T, n // 32, 1)
+    v = yb / X
+    codes = e2m1_encode(v)
+    zero = np.max(np.abs(yb), axis=-1, keepdims=True) == 0
+    codes = np.where(zero, 0, codes).astype(np.uint8)
+    return codes.reshape(T, n), v.reshape(T, n)
+
+
+def quantize_mxfp4(y):
+    """Returns (codes uint8 [T][n], scale bytes uint8 [T][n/32], v)."""
+    y = np.asarray(y, dtype=np.float64)
+    T, n = y.shape
+    bmax = np.max(np.abs(y.reshape(T, n // 32, 32)), axis=-1)
+    sb = (mxfp4_scale_exponent(bmax) + 127).astype(np.uint8)
+    codes, v = mxfp4_codes_from_scales(y, sb)
+    return codes, sb, v
+
+
 # ---------------------------------------------------------------------------
 # Whole forward / inverse
 # ---------------------------------------------------------------------------
@@ -383,17 +428,28 @@ def forward(x, signs, fmt: str, group: int = 0, scale_dtype: str = "f32", tensor
         c, sc, g, v = quantize_nvfp4(y, tensor_scale)
         return {"y": y, "codes": c, "packed": pack_nibbles(c), "scales": sc,
                 "tensor_scale": g, "v": v}
+    if fmt == "mxfp4":
+        if group != 32:
+            raise ValueError("MXFP4 uses 32-wide blocks")
+        c, sb, v = quantize_mxfp4(y)
+        return {"y": y, "codes": c, "packed": pack_nibbles(c), "scales": sb,
+                "tensor_scale": None, "v": v}
     raise ValueError(fmt)
 
 
 def dequantize(packed, scales, fmt: str, group: int = 0, tensor_scale=None) -> np.ndarray:
-    """y_hat from packed codes: INT4 q * s; NVFP4 e2m1(code) * dec(s_b) * g."""
+    """y_hat from packed codes: INT4 q * s; NVFP4 e2m1(code) * dec(s_b) * g;
+    MXFP4 e2m1(code) * 2^(scale byte - 127)."""
     if fmt == "int4":
         q = unpack_nibbles(packed, signed=True).astype(np.float64)
         T, n = q.shape
         s = np.asarray(scales, dtype=np.float64).reshape(T, -1, 1)
         return (_group_view(q, group) * s).reshape(T, n)
     c = unpack_nibbles(packed, signed=False)
+    if fmt == "mxfp4":
+        T, n = c.shape
+        X = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127).reshape(T, n // 32, 1)
+        return (e2m1_decode(c).reshape(T, n // 32, 32) * X).reshape(T, n)
     T, n = c.shape
     seff = (e4m3_decode(scales) * np.float64(np.float32(tensor_scale))).reshape(T, n // 16, 1)
     return (e2m1_decode(c).reshape(T, n // 16, 16) * seff).reshape(T, n)

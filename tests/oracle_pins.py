@@ -247,9 +247,75 @@ def pin_nvfp4_invariants(O):
     _check(np.all(np.abs(yhat - y) <= half_step * seff * (1 + 1e-9) + 1e-300), "E2M1 dequant bound")
 
 
+def pin_mxfp4_closed_form(O):
+    """E3 for MXFP4: y = sqrt(n) e_k, so only k's 32-block is non-zero.  Its shared
+    exponent is floor(log2(sqrt(n))) - 2 (OCP MX v1.0: the largest E2M1 normal is
+    1.5 * 2^2); every other block stores exponent -127 (byte 0) and codes 0."""
+    rng = np.random.default_rng(19)
+    # (n, k, expected scale byte, expected E2M1 code at k)
+    cases = [(128, 77, 127 + 1, 0b0111),      # 11.31 / 2 = 5.66 -> 6
+             (4096, 1234, 127 + 4, 0b0110),   # 64 / 16 = 4
+             (12288, 7000, 127 + 4, 0b0111),  # 110.85 / 16 = 6.93 -> saturates at 6
+             (3072, 2049, 127 + 3, 0b0111)]   # 55.43 / 8 = 6.93 -> 6
+    for n, k, sbyte, code in cases:
+        s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+        x = _signed_row(O, n, k, s)[None, :]
+        out = O.forward(x, s, "mxfp4", 32)
+        sb = out["scales"]
+        _check(sb[0, k // 32] == sbyte, f"MXFP4 E3 scale byte at n={n}")
+        _check(np.count_nonzero(sb) == 1, f"MXFP4 E3 other blocks at n={n}")
+        _check(out["codes"][0, k] == code and np.count_nonzero(out["codes"]) == 1, f"MXFP4 E3 codes at n={n}")
+
+
+def pin_mxfp4_worked_block(O):
+    """A hand-made 32-block: maximum 7 * 2^3 = 56, so X = 2^(5 - 2) = 8, byte 130.
+    Elements / 8: 5 -> 4 (tie, even mantissa), -2.5 -> -2, 0.75 -> 1, 0.25 -> 0,
+    -0.2 -> -0 (sign kept), 7 -> 6 (saturation), 1.75 -> 2."""
+    y = np.zeros((1, 64))
+    y[0, :7] = np.array([5.0, -2.5, 0.75, 0.25, -0.2, 7.0, 1.75]) * 8.0
+    c, sb, _ = O.quantize_mxfp4(y)
+    _check(sb[0, 0] == 130 and sb[0, 1] == 0, "MXFP4 block scale bytes")
+    _check(list(c[0, :7]) == [0b0110, 0b1100, 0b0010, 0b0000, 0b1000, 0b0111, 0b0100], "MXFP4 block codes")
+    _check(not np.any(c[0, 7:]), "MXFP4 zero codes")
+    # the E8M0 byte is an exponent with bias 127 (torch's float8_e8m0fnu decodes it the same way)
+    import torch
+    b = torch.tensor([0, 1, 127, 130, 254], dtype=torch.uint8)
+    _check(torch.equal(b.view(torch.float8_e8m0fnu).float(),
+                       torch.tensor([2.0 ** -127, 2.0 ** -126, 1.0, 8.0, 2.0 ** 127])), "E8M0 bias")
+    yhat = O.dequantize(O.pack_nibbles(c), sb, "mxfp4", 32)
+    _check(np.array_equal(yhat[0, :7], np.array([4.0, -2.0, 1.0, 0.0, -0.0, 6.0, 2.0]) * 8.0),
+           "MXFP4 dequantisation")
+
+
+def pin_mxfp4_invariants(O):
+    """Every non-zero block's maximum lands in [4, 8) scale units (brute force over the
+    candidate exponents), and dequantisation stays within half an E2M1 step, or below the
+    saturation overshoot for maxima in [6, 8)."""
+    rng = np.random.default_rng(20)
+    x = rng.standard_normal((6, 512)) * np.exp(3 * rng.standard_normal((6, 1)))
+    x[0, :64] = 0.0
+    s = np.where(rng.random(512) < 0.5, -1, 1).astype(np.int8)
+    out = O.forward(x, s, "mxfp4", 32)
+    y = out["y"]
+    bmax = np.max(np.abs(y.reshape(6, 16, 32)), axis=-1)
+    for t in range(6):
+        for b in range(16):
+            if bmax[t, b] == 0:
+                continue
+            e = [k for k in range(-127, 128) if 2.0 ** (k + 2) <= bmax[t, b] < 2.0 ** (k + 3)]
+            _check(len(e) == 1 and out["scales"][t, b] == e[0] + 127, "MXFP4 shared exponent")
+    X = np.repeat(np.ldexp(1.0, out["scales"].astype(np.int64) - 127), 32, axis=1)
+    yhat = O.dequantize(out["packed"], out["scales"], "mxfp4", 32)
+    av = np.abs(y) / X
+    bound = np.where(av < 2, 0.25, np.where(av < 4, 0.5, 1.0))
+    bound = np.where(av > 6, av - 6, bound)
+    _check(np.all(np.abs(yhat - y) <= bound * X * (1 + 1e-9)), "MXFP4 dequant bound")
+
+
 ALL_PINS = [
     pin_sylvester_matches_scipy, pin_orthogonality, pin_fwht_equals_dense,
     pin_rotate_matches_scipy_definition, pin_parseval_and_roundtrip, pin_e3_closed_form,
     pin_e1_worked_example, pin_e2_worked_example, pin_int4_rounding, pin_fp16_storage,
-    pin_e2m1, pin_e4m3, pin_nvfp4_invariants,
+    pin_e2m1, pin_e4m3, pin_nvfp4_invariants, pin_mxfp4_closed_form, pin_mxfp4_worked_block,
+    pin_mxfp4_invariants,
 ]

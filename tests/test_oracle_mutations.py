@@ -139,9 +139,32 @@ def _inverse_without_transpose(O):
     O.inverse_rotate = inv
 
 
+def _mxfp4_emax_one(O):
+    orig = O.mxfp4_scale_exponent
+    O.mxfp4_scale_exponent = lambda b: np.clip(orig(b) + 1, -127, 127)
+
+
+def _mxfp4_ceil(O):
+    def exp_ceil(bmax):
+        bmax = np.asarray(bmax, dtype=np.float64)
+        e = np.where(bmax > 0, np.ceil(np.log2(np.where(bmax > 0, bmax, 1.0))) - 2, -127)
+        return np.clip(e, -127, 127).astype(np.int64)
+    O.mxfp4_scale_exponent = exp_ceil
+
+
+def _mxfp4_bias_128(O):
+    orig_q, orig_d = O.quantize_mxfp4, O.dequantize
+
+    def q(y):
+        c, sb, v = orig_q(y)
+        return c, (sb.astype(np.int64) + 1).astype(np.uint8), v
+    O.quantize_mxfp4 = q
+
+
 MUTATIONS = [_no_norm, _signs_after, _h12_transposed_in_rotate, _h12_typo, _round_half_away,
              _swap_nibbles, _scale_over_8, _fp16_truncation, _nvfp4_wrong_constant,
-             _e2m1_ties_up, _e4m3_truncate, _fwht_skip_stage, _inverse_without_transpose]
+             _e2m1_ties_up, _e4m3_truncate, _fwht_skip_stage, _inverse_without_transpose,
+             _mxfp4_emax_one, _mxfp4_ceil, _mxfp4_bias_128]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
