@@ -31,7 +31,7 @@ METRIC = "RHT+4-bit quant tokens/s & HBM GB/s (% of peak) at d=4096 and d=12288"
 HBM_PEAK_GBS = 8000.0
 CACHE_DEFEAT_BYTES = 512 << 20
 HEADLINE = "llama_4096_int4"
-OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096"]
+OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_4096"]
 KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast2.hip",
@@ -72,7 +72,7 @@ def time_workload(R, torch, name, steps, warmup):
     outs = []
     for _ in range(sets):
         packed = torch.empty((w.tokens, w.n // 2), dtype=torch.uint8, device="cuda")
-        sdt = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8}[w.scale_dtype]
+        sdt = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8, "e8m0": torch.uint8}[w.scale_dtype]
         ng = 1 if w.group == 0 else w.n // w.group
         scales = torch.empty((w.tokens, ng), dtype=sdt, device="cuda")
         ts = torch.zeros(1, dtype=torch.float32, device="cuda") if w.fmt == "nvfp4" else None

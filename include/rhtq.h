@@ -17,7 +17,9 @@
  *  - "incoh_rotate=true degrades W4 PPL on Qwen3-8B" (KronQ issue #2), Model
  *    Details table: 12288 = 12 x 1024 is Hadamard-compatible.
  *  - "Methodology checks for NVFP4 W4A4 on Qwen3-8B", the NVFP4 results and the
- *    block-Hadamard comment: E2M1 codes with E4M3 block scales, INT4-g128.
+ *    block-Hadamard comment: E2M1 codes with E4M3 block scales, INT4-g128, and MXFP4
+ *    compared with both.  MXFP4 itself is defined by the OCP Microscaling Formats (MX)
+ *    v1.0 specification (32-element blocks, E8M0 shared scale, E2M1 elements).
  *
  * Per row x of width n (rows contiguous, row-major [tokens][n]):
  *
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define RHTQ_ABI_VERSION 1
+#define RHTQ_ABI_VERSION 2   /* 2: MXFP4 format and E8M0 scales */
 
 /* Status codes. */
 #define RHTQ_OK           0   /* enqueued (or nothing to do)                       */
@@ -68,11 +70,13 @@ extern "C" {
 /* 4-bit formats. */
 #define RHTQ_FMT_INT4  0      /* symmetric absmax INT4, two's complement nibbles     */
 #define RHTQ_FMT_NVFP4 1      /* E2M1 codes, E4M3 block-16 scales, fp32 tensor scale */
+#define RHTQ_FMT_MXFP4 2      /* E2M1 codes, E8M0 (power-of-two) block-32 scales     */
 
 /* Scale storage types. */
 #define RHTQ_SCALE_F32  0
 #define RHTQ_SCALE_F16  1
 #define RHTQ_SCALE_E4M3 2
+#define RHTQ_SCALE_E8M0 3     /* byte = exponent + 127 */
 
 /* NVFP4 tensor-scale handling. */
 #define RHTQ_TENSOR_SCALE_DYNAMIC 0   /* g = fl32(max|y| / (6*448)) computed and written */
@@ -87,7 +91,7 @@ int rhtq_abi_version(void);
 const char* rhtq_status_str(int status);
 
 /* 1 if (n, fmt, group) is supported, else 0.  INT4: group 0 (one group per row) or
- * a power of two >= 16 dividing n.  NVFP4: group 16. */
+ * a power of two >= 16 dividing n.  NVFP4: group 16.  MXFP4: group 32. */
 int rhtq_supported(int32_t n, int fmt, int32_t group);
 
 /*
@@ -124,6 +128,13 @@ int rhtq_rotate(const void* x, int in_dtype, int64_t tokens, int32_t n,
  *   codes         bit 3 = sign of y, bits 0-2 = E2M1 magnitude of |y| / (dec(s_b) g)
  *                 ({0,.5,1,1.5,2,3,4,6}, nearest even, saturating at 6); a block whose
  *                 scale decodes to 0 stores code 0.
+ *
+ * MXFP4 (fmt RHTQ_FMT_MXFP4; OCP MX v1.0, named in the NVFP4 methodology thread):
+ *   group 32, scale_dtype RHTQ_SCALE_E8M0; tensor_scale, tensor_scale_mode ignored
+ *   scales_out    [tokens][n/32] bytes e + 127 with e = floor(log2(max|y_block|)) - 2
+ *                 clamped to [-127, 127] (-127 for an all-zero block); X = 2^e
+ *   codes         bit 3 = sign of y, bits 0-2 = E2M1 magnitude of |y| / X (nearest even,
+ *                 saturating at 6); an all-zero block stores code 0.
  */
 int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n,
                  const int8_t* signs, int fmt, int32_t group, int scale_dtype,
@@ -132,7 +143,7 @@ int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n,
 
 /*
  * Inverse of rhtq_forward: unpack, dequantise with the stored scales (INT4 q*s;
- * NVFP4 e2m1(c) * dec(s_b) * g) and undo the rotation, x_out = diag(s) H_n^T y / sqrt(n)
+ * NVFP4 e2m1(c) * dec(s_b) * g; MXFP4 e2m1(c) * 2^(byte - 127)) and undo the rotation, x_out = diag(s) H_n^T y / sqrt(n)
  * (fp32 [tokens][n]).  Arguments mirror rhtq_forward; tensor_scale is read for NVFP4.
  * Cite: QuaRot reviews, review 2 Summary (the RHT is invertible).
  */

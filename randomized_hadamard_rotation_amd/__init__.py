@@ -17,12 +17,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librhtq.so"
 
 RHTQ_OK, RHTQ_EINVAL, RHTQ_EUNSUPPORTED, RHTQ_EHIP = 0, 1, 2, 3
 RHTQ_IN_BF16, RHTQ_IN_F32 = 0, 1
-RHTQ_FMT_INT4, RHTQ_FMT_NVFP4 = 0, 1
-RHTQ_SCALE_F32, RHTQ_SCALE_F16, RHTQ_SCALE_E4M3 = 0, 1, 2
+RHTQ_FMT_INT4, RHTQ_FMT_NVFP4, RHTQ_FMT_MXFP4 = 0, 1, 2
+RHTQ_SCALE_F32, RHTQ_SCALE_F16, RHTQ_SCALE_E4M3, RHTQ_SCALE_E8M0 = 0, 1, 2, 3
 RHTQ_TENSOR_SCALE_DYNAMIC, RHTQ_TENSOR_SCALE_GIVEN = 0, 1
 
-_FMT = {"int4": RHTQ_FMT_INT4, "nvfp4": RHTQ_FMT_NVFP4}
-_SCALE = {"f32": RHTQ_SCALE_F32, "f16": RHTQ_SCALE_F16, "e4m3": RHTQ_SCALE_E4M3}
+_FMT = {"int4": RHTQ_FMT_INT4, "nvfp4": RHTQ_FMT_NVFP4, "mxfp4": RHTQ_FMT_MXFP4}
+_SCALE = {"f32": RHTQ_SCALE_F32, "f16": RHTQ_SCALE_F16, "e4m3": RHTQ_SCALE_E4M3, "e8m0": RHTQ_SCALE_E8M0}
+_DEFAULT_SCALE = {"int4": "f32", "nvfp4": "e4m3", "mxfp4": "e8m0"}
+_DEFAULT_GROUP = {"nvfp4": 16, "mxfp4": 32}
 
 EXPORTED = ["rhtq_abi_version", "rhtq_status_str", "rhtq_supported", "rhtq_rotate",
             "rhtq_forward", "rhtq_inverse", "rhtq_signs_from_seed"]
@@ -158,20 +160,21 @@ def rhtq_forward(x, signs=None, fmt: str = "int4", group: int = 0, scale_dtype: 
 
     INT4: scales fp32/fp16 [tokens][n/group] (group 0 = one per row).
     NVFP4: scales uint8 E4M3 [tokens][n/16]; tensor_scale a device float32 [1]
-    (written in 'dynamic' mode, read in 'given' mode)."""
+    (written in 'dynamic' mode, read in 'given' mode).
+    MXFP4: scales uint8 E8M0 [tokens][n/32]."""
     torch = _torch()
     _need_device(x)
     x = x.contiguous()
     tokens, n = x.shape
     if scale_dtype is None:
-        scale_dtype = "f32" if fmt == "int4" else "e4m3"
-    if fmt == "nvfp4" and group == 0:
-        group = 16
+        scale_dtype = _DEFAULT_SCALE[fmt]
+    if group == 0:
+        group = _DEFAULT_GROUP.get(fmt, 0)
     s = _signs_tensor(signs, n, x.device)
     if packed is None:
         packed = torch.empty((tokens, n // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
-        sdt = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8}[scale_dtype]
+        sdt = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8, "e8m0": torch.uint8}[scale_dtype]
         scales = torch.empty(scale_shape(tokens, n, fmt, group), dtype=sdt, device=x.device)
     if fmt == "nvfp4" and tensor_scale is None:
         tensor_scale = torch.zeros(1, dtype=torch.float32, device=x.device)
@@ -189,9 +192,9 @@ def rhtq_inverse(packed, scales, n: int, signs=None, fmt: str = "int4", group: i
     _need_device(packed, scales, tensor_scale)
     tokens = packed.shape[0]
     if scale_dtype is None:
-        scale_dtype = "f32" if fmt == "int4" else "e4m3"
-    if fmt == "nvfp4" and group == 0:
-        group = 16
+        scale_dtype = _DEFAULT_SCALE[fmt]
+    if group == 0:
+        group = _DEFAULT_GROUP.get(fmt, 0)
     s = _signs_tensor(signs, n, packed.device)
     if out is None:
         out = torch.empty((tokens, n), dtype=torch.float32, device=packed.device)

@@ -23,6 +23,7 @@ bool width_ok(int32_t n) {
 bool group_ok(int32_t n, int fmt, int32_t group) {
   if (fmt == RHTQ_FMT_INT4) return group == 0 || (is_pow2(group) && group >= 16 && n % group == 0);
   if (fmt == RHTQ_FMT_NVFP4) return group == 16;
+  if (fmt == RHTQ_FMT_MXFP4) return group == 32 && n % 32 == 0;
   return false;
 }
 
@@ -33,12 +34,15 @@ int from_hip(hipError_t e) { return e == hipSuccess ? RHTQ_OK : RHTQ_EHIP; }
 // Shared checks of rhtq_forward / rhtq_inverse.  Returns RHTQ_OK or the status.
 int check_quant_args(int64_t tokens, int32_t n, int fmt, int32_t group, int scale_dtype) {
   if (tokens < 0) return RHTQ_EINVAL;
-  if (fmt != RHTQ_FMT_INT4 && fmt != RHTQ_FMT_NVFP4) return RHTQ_EINVAL;
-  if (scale_dtype != RHTQ_SCALE_F32 && scale_dtype != RHTQ_SCALE_F16 && scale_dtype != RHTQ_SCALE_E4M3)
+  if (fmt != RHTQ_FMT_INT4 && fmt != RHTQ_FMT_NVFP4 && fmt != RHTQ_FMT_MXFP4) return RHTQ_EINVAL;
+  if (scale_dtype != RHTQ_SCALE_F32 && scale_dtype != RHTQ_SCALE_F16 && scale_dtype != RHTQ_SCALE_E4M3 &&
+      scale_dtype != RHTQ_SCALE_E8M0)
     return RHTQ_EINVAL;
   if (!width_ok(n) || !group_ok(n, fmt, group)) return RHTQ_EUNSUPPORTED;
-  if (fmt == RHTQ_FMT_INT4 && scale_dtype == RHTQ_SCALE_E4M3) return RHTQ_EUNSUPPORTED;
+  if (fmt == RHTQ_FMT_INT4 && scale_dtype != RHTQ_SCALE_F32 && scale_dtype != RHTQ_SCALE_F16)
+    return RHTQ_EUNSUPPORTED;
   if (fmt == RHTQ_FMT_NVFP4 && scale_dtype != RHTQ_SCALE_E4M3) return RHTQ_EUNSUPPORTED;
+  if (fmt == RHTQ_FMT_MXFP4 && scale_dtype != RHTQ_SCALE_E8M0) return RHTQ_EUNSUPPORTED;
   return RHTQ_OK;
 }
 
@@ -125,6 +129,7 @@ int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n, const i
   };
 
   if (fmt == RHTQ_FMT_INT4) return from_hip(run(rhtq::OP_INT4));
+  if (fmt == RHTQ_FMT_MXFP4) return from_hip(run(rhtq::OP_MXFP4));
   if (tensor_scale_mode == RHTQ_TENSOR_SCALE_DYNAMIC) {
     hipError_t e = rhtq::launch_zero_word(tensor_scale, s);
     if (e == hipSuccess) e = run(rhtq::OP_AMAX);

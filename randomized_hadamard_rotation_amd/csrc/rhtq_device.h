@@ -243,6 +243,15 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// MX shared exponent of a 32-block with maximum bmax >= 0 (OCP MX v1.0): floor(log2(bmax))
+// minus 2 (the largest E2M1 normal is 1.5 * 2^2), clamped to [-127, 127]; -127 for a zero
+// block.  For a normal bmax the floor of log2 is its unbiased exponent field; a subnormal
+// bmax is below 2^-126 and clamps.
+__device__ __forceinline__ int mx_exponent(float bmax) {
+  const int e = (int)((__float_as_uint(bmax) >> 23) & 0xFF) - 127 - 2;
+  return bmax > 0.0f ? (e < -127 ? -127 : (e > 127 ? 127 : e)) : -127;
+}
+
 // Eight INT4 codes -> one dword, element k in nibble k.  q[k] holds the bits of
 // fma(y, 1/s, 1.5 * 2^23): its low 4 bits are the two's-complement code.
 __device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t* q) {

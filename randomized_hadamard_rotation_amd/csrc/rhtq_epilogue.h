@@ -16,7 +16,8 @@
 // s = amax / 7 stored as fp32 / fp16, codes = clamp(rne(y / s_stored), -8, 7) by the
 // 1.5 * 2^23 magic-constant FMA.  NVFP4 (NVFP4 methodology thread): E4M3 block scale of
 // bmax / (6 g), E2M1 codes by v_cvt_scalef32_pk_fp4_f32 with unit scale; zero-scale blocks
-// store code 0.
+// store code 0.  MXFP4 (OCP MX v1.0; compared with NVFP4 in the same thread): 32-blocks
+// share the E8M0 exponent floor(log2(bmax)) - 2, codes as for NVFP4 with that scale.
 #pragma once
 
 #include "rhtq_device.h"
@@ -29,7 +30,8 @@ __device__ __forceinline__ void store_int4_scale(void* scales, int scale_dtype, 
   else static_cast<__half*>(scales)[gi] = __float2half_rn(fminf(s, 65504.0f));
 }
 
-// OP is OP_INT4 or OP_NVFP4.  G = log2 of the group (0: one INT4 group per row; NVFP4: 4).
+// OP is OP_INT4, OP_NVFP4 or OP_MXFP4.  G = log2 of the group (0: one INT4 group per
+// row; NVFP4: 4; MXFP4: 5).
 // relem0: index of the row's first element in the tensor; N: row width.
 // rowmax(m): row maximum (true units) from this lane's maximum (true units), every lane.
 // row_writer: this lane stores the row's scale when G == 0.
@@ -120,10 +122,18 @@ __device__ __forceinline__ void quant_epilogue(const KernelArgs& a, const int64_
 #pragma unroll
       for (int p = 0; p < R2; ++p) {
         const int qq = R1 >= 2 ? 4 * p + rw : (rw & 1);
-        const Int4Scale sc = int4_scale(c2[p] * invS, cnorm, a.scale_dtype);
-        sl[p] = sc.inv * invS;
-        clamp |= sc.clamp;
-        if (lane_writes) store_int4_scale(a.scales, a.scale_dtype, (relem0 + cbase(qq) + 32 * col) >> G, sc.s);
+        const int64_t gi = (relem0 + cbase(qq) + 32 * col) >> G;
+        if constexpr (OP == OP_MXFP4) {
+          const float bm = (c2[p] * invS) * cnorm;   // block maximum of the rotated values
+          const int ex = mx_exponent(bm);
+          sl[p] = bm > 0.0f ? __builtin_ldexpf(invS * cnorm, -ex) : 0.0f;
+          if (lane_writes) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)(ex + 127);
+        } else {
+          const Int4Scale sc = int4_scale(c2[p] * invS, cnorm, a.scale_dtype);
+          sl[p] = sc.inv * invS;
+          clamp |= sc.clamp;
+          if (lane_writes) store_int4_scale(a.scales, a.scale_dtype, gi, sc.s);
+        }
       }
       float e1[R1];
       if constexpr (R1 >= 2) {
@@ -154,7 +164,7 @@ __device__ __forceinline__ void quant_epilogue(const KernelArgs& a, const int64_
       }
       st_stream(prow + (cbase(q) >> 1) + 4 * lc, pack8_nibbles(qb));
     }
-  } else if constexpr (OP == OP_NVFP4) {
+  } else if constexpr (OP == OP_NVFP4 || OP == OP_MXFP4) {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       const float s = inv[q];

@@ -342,6 +342,31 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
             st_stream(a.packed + (g0 >> 1), words[0]);
           if (S::V == 16 || (lane & 1) == 0) static_cast<uint8_t*>(a.scales)[g0 >> 4] = (uint8_t)code;
         }
+      } else if constexpr (OP == OP_MXFP4) {
+        // 32-element blocks over two lanes (V = 16) or four lanes (V = 8); E8M0 exponent
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < S::V; ++r) m = fmaxf(m, fabsf(y[r]));
+        m = group_max(m, 32 / S::V);
+        const int ex = mx_exponent(m * cnorm);
+        const float inv = m > 0.0f ? __builtin_ldexpf(cnorm, -ex) : 0.0f;
+        uint32_t words[S::V / 8];
+#pragma unroll
+        for (int w = 0; w < S::V / 8; ++w) {
+          uint32_t acc = 0;
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * w + 0] * inv, y[8 * w + 1] * inv, 1.0f, 0);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * w + 2] * inv, y[8 * w + 3] * inv, 1.0f, 1);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * w + 4] * inv, y[8 * w + 5] * inv, 1.0f, 2);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, y[8 * w + 6] * inv, y[8 * w + 7] * inv, 1.0f, 3);
+          words[w] = inv > 0.0f ? acc : 0u;     // an all-zero block stores code 0
+        }
+        if (live) {
+          if constexpr (S::V == 16)
+            st_stream(a.packed + (g0 >> 1), words[0], words[1]);
+          else
+            st_stream(a.packed + (g0 >> 1), words[0]);
+          if ((lane & (32 / S::V - 1)) == 0) static_cast<uint8_t*>(a.scales)[g0 >> 5] = (uint8_t)(ex + 127);
+        }
       }
     }
   }
@@ -413,6 +438,7 @@ hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s) {
     case OP_ROTATE: return dispatch<OP_ROTATE>(a, s);
     case OP_INT4: return dispatch<OP_INT4>(a, s);
     case OP_NVFP4: return dispatch<OP_NVFP4>(a, s);
+    case OP_MXFP4: return dispatch<OP_MXFP4>(a, s);
     case OP_AMAX: return dispatch<OP_AMAX>(a, s);
     default: return hipErrorNotSupported;
   }

@@ -242,6 +242,7 @@ __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
   int G = 0;   // log2 of the INT4 group (0: one group per row)
   if constexpr (OP == OP_INT4) G = a.group == kN ? 0 : __builtin_ctz((unsigned)a.group);
   if constexpr (OP == OP_NVFP4) G = 4;
+  if constexpr (OP == OP_MXFP4) G = 5;
   if (h == 0) fast12_rows<OP, 0>(a, sh, hb, hc, lane, gts, inv6g, G);
   else fast12_rows<OP, 1>(a, sh, hb, hc, lane, gts, inv6g, G);
 }
@@ -273,6 +274,7 @@ hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s) {
     case OP_ROTATE: return launch12<OP_ROTATE>(a, s);
     case OP_INT4: return launch12<OP_INT4>(a, s);
     case OP_NVFP4: return launch12<OP_NVFP4>(a, s);
+    case OP_MXFP4: return launch12<OP_MXFP4>(a, s);
     case OP_AMAX: return launch12<OP_AMAX>(a, s);
     default: return hipErrorNotSupported;
   }

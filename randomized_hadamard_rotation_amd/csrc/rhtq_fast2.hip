@@ -110,6 +110,7 @@ void fast2_kernel(KernelArgs a) {
   int G = 0;   // log2 of the INT4 group (0: one group per row)
   if constexpr (OP == OP_INT4) G = a.group == N ? 0 : __builtin_ctz((unsigned)a.group);
   if constexpr (OP == OP_NVFP4) G = 4;
+  if constexpr (OP == OP_MXFP4) G = 5;
   float run_max = 0.0f;
   // lane chunk: element bits 3-4 = lane >> 4, bits 5-8 = lane & 15
   const int lc = (lane >> 4) | ((lane & 15) << 2);
@@ -212,7 +213,7 @@ void fast2_kernel(KernelArgs a) {
       return;
     }
 
-    if constexpr (OP == OP_INT4 || OP == OP_NVFP4)
+    if constexpr (OP == OP_INT4 || OP == OP_NVFP4 || OP == OP_MXFP4)
       quant_epilogue<OP, R>(a, row, ebase, G, invS, cnorm, gts, inv6g, lane, lane == 0, val,
                             [](int q) { return 512 * q; }, [](float m) { return group_max(m, 64); });
   };
@@ -282,6 +283,7 @@ hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s) {
     case OP_ROTATE: return dispatch2<OP_ROTATE>(a, s);
     case OP_INT4: return dispatch2<OP_INT4>(a, s);
     case OP_NVFP4: return dispatch2<OP_NVFP4>(a, s);
+    case OP_MXFP4: return dispatch2<OP_MXFP4>(a, s);
     case OP_AMAX: return dispatch2<OP_AMAX>(a, s);
     default: return hipErrorNotSupported;
   }

@@ -105,7 +105,9 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(KernelArgs a) {
               v[e] = (float)q * s;
             }
           } else {
-            const float seff = e4m3_value(((const uint8_t*)a.in_scales)[gidx]) * a.in_tensor_scale[0];
+            const uint32_t sb = ((const uint8_t*)a.in_scales)[gidx];
+            const float seff = a.inv_fmt == RHTQ_FMT_MXFP4 ? __builtin_ldexpf(1.0f, (int)sb - 127)
+                                                           : e4m3_value(sb) * a.in_tensor_scale[0];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = e2m1_value((w >> (4 * e)) & 15u) * seff;
           }
@@ -245,6 +247,18 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(KernelArgs a) {
               word |= ((uint32_t)(int)q & 15u) << (4 * e);
             }
           }
+        } else if constexpr (OP == OP_MXFP4) {
+          const int ex = mx_exponent(gmax);
+          if (first) ((uint8_t*)a.scales)[gidx] = (uint8_t)(ex + 127);
+          if (gmax > 0.0f) {
+            const float inv = __builtin_ldexpf(1.0f, -ex);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = lds[lds_idx(e0 + e)] * inv;
+              const uint32_t code = e2m1_mag(fabsf(v)) | (__float_as_uint(v) >> 31 << 3);
+              word |= code << (4 * e);
+            }
+          }
         } else {  // OP_NVFP4
           uint32_t sc = 0;
           if (gts > 0.0f) sc = e4m3_code(gmax / (6.0f * gts));
@@ -334,6 +348,7 @@ hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t
       case OP_ROTATE: return dispatch_width<RHTQ_IN_BF16, OP_ROTATE>(a, s);
       case OP_INT4: return dispatch_width<RHTQ_IN_BF16, OP_INT4>(a, s);
       case OP_NVFP4: return dispatch_width<RHTQ_IN_BF16, OP_NVFP4>(a, s);
+      case OP_MXFP4: return dispatch_width<RHTQ_IN_BF16, OP_MXFP4>(a, s);
       case OP_AMAX: return dispatch_width<RHTQ_IN_BF16, OP_AMAX>(a, s);
       case OP_INVERSE: return dispatch_width<RHTQ_IN_BF16, OP_INVERSE>(a, s);
     }
@@ -342,6 +357,7 @@ hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t
       case OP_ROTATE: return dispatch_width<RHTQ_IN_F32, OP_ROTATE>(a, s);
       case OP_INT4: return dispatch_width<RHTQ_IN_F32, OP_INT4>(a, s);
       case OP_NVFP4: return dispatch_width<RHTQ_IN_F32, OP_NVFP4>(a, s);
+      case OP_MXFP4: return dispatch_width<RHTQ_IN_F32, OP_MXFP4>(a, s);
       case OP_AMAX: return dispatch_width<RHTQ_IN_F32, OP_AMAX>(a, s);
       case OP_INVERSE: return hipErrorInvalidValue;  // inverse input is packed codes
     }

@@ -14,6 +14,7 @@ enum Op : int {
   OP_NVFP4 = 2,    // packed E2M1 + E4M3 scales, reads the tensor scale g
   OP_AMAX = 3,     // atomic max of |y| bits into tensor_scale (NVFP4 dynamic pre-pass)
   OP_INVERSE = 4,  // packed + scales -> x fp32
+  OP_MXFP4 = 5,    // packed E2M1 + E8M0 scales of 32-blocks
 };
 
 struct KernelArgs {

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(R):
 
 
 def test_abi_version_and_status_strings(R):
-    assert R.rhtq_abi_version() == 1
+    assert R.rhtq_abi_version() == 2
     assert R.rhtq_status_str(0) == "ok"
     assert "invalid" in R.rhtq_status_str(1)
     assert "unsupported" in R.rhtq_status_str(2)
@@ -42,6 +42,7 @@ def test_supported_matrix(R):
     for k in range(4, 15):
         assert R.rhtq_supported(1 << k, "int4", 0)
         assert R.rhtq_supported(1 << k, "nvfp4", 16)
+        assert R.rhtq_supported(1 << k, "mxfp4", 32) == (k >= 5)
     for m in (256, 512, 1024, 2048):
         assert R.rhtq_supported(12 * m, "int4", 128)
     for bad in (0, 8, 32768, 100, 12 * 128, 12 * 4096, 11008):
@@ -49,6 +50,8 @@ def test_supported_matrix(R):
     assert not R.rhtq_supported(4096, "int4", 96)      # not a power of two
     assert not R.rhtq_supported(4096, "int4", 8)       # below 16
     assert not R.rhtq_supported(4096, "nvfp4", 32)
+    assert not R.rhtq_supported(4096, "mxfp4", 16)
+    assert R.rhtq_supported(12288, "mxfp4", 32)
 
 
 def test_signs_from_seed_matches_generator(R):
@@ -78,6 +81,12 @@ def test_host_validation(R):
     assert F(fake, 0, 4, 4096, None, 0, 0, 2, fake, fake, None, 0, s) == R.RHTQ_EUNSUPPORTED
     assert F(fake, 0, 4, 4096, None, 1, 16, 1, fake, fake, fake, 0, s) == R.RHTQ_EUNSUPPORTED
     assert F(fake, 0, 4, 4096, None, 1, 16, 2, fake, fake, None, 0, s) == R.RHTQ_EINVAL
+    # MXFP4: group 32 with E8M0 scales only; no tensor scale needed
+    assert F(fake, 0, 4, 4096, None, 2, 32, 2, fake, fake, None, 0, s) == R.RHTQ_EUNSUPPORTED
+    assert F(fake, 0, 4, 4096, None, 2, 16, 3, fake, fake, None, 0, s) == R.RHTQ_EUNSUPPORTED
+    assert F(fake, 0, 4, 4096, None, 0, 0, 3, fake, fake, None, 0, s) == R.RHTQ_EUNSUPPORTED
+    assert F(fake, 0, 4, 4096, None, 2, 32, 4, fake, fake, None, 0, s) == R.RHTQ_EINVAL
+    assert F(fake, 0, 4, 4096, None, 3, 32, 3, fake, fake, None, 0, s) == R.RHTQ_EINVAL
     assert F(fake, 0, 4, 4096, None, 1, 16, 2, fake, fake, fake, 9, s) == R.RHTQ_EINVAL
     assert F(fake, 0, 4, 4096, None, 9, 16, 2, fake, fake, fake, 0, s) == R.RHTQ_EINVAL
     assert F(None, 0, 4, 4096, None, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EINVAL

@@ -62,6 +62,8 @@ def check_forward(R, x, s, fmt, group, scale_dtype, rows=None, y_ref=None, g_ref
         y_ref = O.rotate(x[rows].cpu(), s)
     if fmt == "int4":
         return C.check_int4(packed[rows], scales[rows], y_ref, group, scale_dtype)
+    if fmt == "mxfp4":
+        return C.check_mxfp4(packed[rows], scales[rows], y_ref)
     return C.check_nvfp4(packed[rows], scales[rows], g, y_ref, g_ref)
 
 
@@ -130,6 +132,12 @@ def test_e3_closed_form(R, n, k):
     assert np.all(scales[:, k // 16] == 0x7E) and np.count_nonzero(scales) == 3
     assert np.all(c[:, k] == 0b0111)
     assert np.count_nonzero(c & 7) == 3
+    if n % 32 == 0:
+        # MXFP4: the block of k has exponent floor(log2(sqrt(n))) - 2, the rest exponent -127
+        packed, scales, _ = run_forward(R, x, s, "mxfp4", 32, "e8m0")
+        c = O.unpack_nibbles(packed, signed=False)
+        ref = O.forward(xe, s, "mxfp4", 32)
+        assert np.all(scales == ref["scales"]) and np.all(c == ref["codes"])
 
 
 # ----------------------------------------------------------------------------
@@ -137,7 +145,7 @@ def test_e3_closed_form(R, n, k):
 # ----------------------------------------------------------------------------
 
 REDUCED = [("tiny_128_int4", 64), ("llama_4096_int4", 203), ("downproj_12288_int4g128", 37),
-           ("kv_128_int4g128", 4099), ("nvfp4_4096", 131)]
+           ("kv_128_int4g128", 4099), ("nvfp4_4096", 131), ("mxfp4_4096", 131)]
 
 
 @pytest.mark.parametrize("name,tokens", REDUCED)
@@ -150,7 +158,7 @@ def test_workload_reduced(R, name, tokens):
 
 
 @pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
-                                  "nvfp4_4096"])
+                                  "nvfp4_4096", "mxfp4_4096"])
 def test_workload_full_size_sampled(R, name):
     """Full-size input on the device in the same launch shape as the benchmark;
     the oracle checks sampled rows (first, last, every sink row it can find, random)."""
@@ -219,6 +227,9 @@ def test_quantise_every_width(R, n):
                 check_forward(R, x, s, "int4", group, sd, y_ref=y_ref)
         say(f"nvfp4 n={n} dtype={dt}")
         check_forward(R, x, s, "nvfp4", 16, "e4m3", y_ref=y_ref)
+        if n >= 32:
+            say(f"mxfp4 n={n} dtype={dt}")
+            check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
 def test_nvfp4_given_tensor_scale(R):
@@ -249,6 +260,7 @@ def test_special_inputs(R, kind):
         check_forward(R, x, s, "int4", 0, "f32", y_ref=y_ref)
         check_forward(R, x, s, "int4", 128, "f16", y_ref=y_ref)
         check_forward(R, x, s, "nvfp4", 16, "e4m3", y_ref=y_ref)
+        check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
 def test_zero_tokens_is_noop(R):
@@ -262,7 +274,8 @@ def test_zero_tokens_is_noop(R):
 
 def test_deterministic(R):
     import torch
-    for name in ("llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096"):
+    for name in ("llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096",
+                 "mxfp4_4096"):
         w = WORKLOADS[name]
         say(f"determinism {name}")
         x, s = x_to(w, min(w.tokens, 512))
@@ -276,7 +289,7 @@ def test_deterministic(R):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
-                                  "nvfp4_4096"])
+                                  "nvfp4_4096", "mxfp4_4096"])
 def test_inverse_round_trip(R, name):
     import torch
     w = WORKLOADS[name]

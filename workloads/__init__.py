@@ -56,9 +56,9 @@ class Workload:
     recipe: str            # "gauss_outlier_cols", "llama_like", "kv_spikes"
     seed: int              # value seed
     sign_seed: int         # splitmix64 seed of the sign vector
-    fmt: str               # "int4" or "nvfp4"
+    fmt: str               # "int4", "nvfp4" or "mxfp4"
     group: int             # 0 = per token
-    scale_dtype: str       # "f32", "f16" or "e4m3"
+    scale_dtype: str       # "f32", "f16", "e4m3" or "e8m0"
     tokens_per_row: float = 1.0   # KV rows: 1/32 token per row (32 heads)
     description: str = ""
 
@@ -87,6 +87,11 @@ WORKLOADS = {
         "nvfp4_4096", 16384, 4096, "bf16", "llama_like", 5, 0, "nvfp4", 16, "e4m3",
         description="16384 x 4096 bf16, llama-like recipe with sinks; E2M1 codes, E4M3 block-16 "
                     "scales, fp32 tensor scale = amax/(6*448)"),
+    # MXFP4 on the NVFP4 shape: the thread compares the two FP4 formats on the same model
+    "mxfp4_4096": Workload(
+        "mxfp4_4096", 16384, 4096, "bf16", "llama_like", 6, 0, "mxfp4", 32, "e8m0",
+        description="16384 x 4096 bf16, llama-like recipe with sinks; E2M1 codes with E8M0 "
+                    "power-of-two scales per 32-block (OCP MX)"),
 }
 
 
@@ -167,6 +172,9 @@ def bytes_per_call(w: Workload, tensor_scale_dynamic: bool = True) -> int:
     if w.fmt == "int4":
         groups = 1 if w.group == 0 else w.n // w.group
         sbytes = rows * groups * (4 if w.scale_dtype == "f32" else 2)
+        extra = 0
+    elif w.fmt == "mxfp4":
+        sbytes = rows * (w.n // 32)
         extra = 0
     else:
         sbytes = rows * (w.n // 16)
