@@ -103,7 +103,7 @@ def time_workload(R, torch, name, steps, warmup):
         "buffer_sets": sets, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
         "rows_per_s": w.tokens / (ms * 1e-3), "bytes_per_call": nbytes, "achieved_gbs": gbs,
         "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
-        "launches_per_step": 4 if w.fmt == "nvfp4" else 1,
+        "launches_per_step": 3 if w.fmt == "nvfp4" else 1,
     }
 
 

@@ -131,9 +131,9 @@ int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n, const i
   if (fmt == RHTQ_FMT_INT4) return from_hip(run(rhtq::OP_INT4));
   if (fmt == RHTQ_FMT_MXFP4) return from_hip(run(rhtq::OP_MXFP4));
   if (tensor_scale_mode == RHTQ_TENSOR_SCALE_DYNAMIC) {
+    // the pre-pass leaves g itself in *tensor_scale (atomic max of per-workgroup g)
     hipError_t e = rhtq::launch_zero_word(tensor_scale, s);
     if (e == hipSuccess) e = run(rhtq::OP_AMAX);
-    if (e == hipSuccess) e = rhtq::launch_finalize_tensor_scale(tensor_scale, s);
     if (e != hipSuccess) return RHTQ_EHIP;
   }
   return from_hip(run(rhtq::OP_NVFP4));

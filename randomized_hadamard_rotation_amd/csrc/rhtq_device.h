@@ -252,6 +252,12 @@ __device__ __forceinline__ int mx_exponent(float bmax) {
   return bmax > 0.0f ? (e < -127 ? -127 : (e > 127 ? 127 : e)) : -127;
 }
 
+// NVFP4 tensor scale g = fl32(a / (6 * 448)) of a maximum a (correctly rounded division).
+// Rounding is monotone, so the maximum of these over workgroups equals g of the overall
+// maximum: the pre-pass combines per-workgroup values with an atomic max on the bits
+// (non-negative floats order like their bit patterns) and leaves g itself.
+__device__ __forceinline__ float nvfp4_tensor_scale(float a) { return a / 2688.0f; }
+
 // Eight INT4 codes -> one dword, element k in nibble k.  q[k] holds the bits of
 // fma(y, 1/s, 1.5 * 2^23): its low 4 bits are the two's-complement code.
 __device__ __forceinline__ uint32_t pack8_nibbles(const uint32_t* q) {

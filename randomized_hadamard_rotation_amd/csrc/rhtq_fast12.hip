@@ -207,7 +207,7 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
     if (lane == 0) sh.rmax[h] = run_max;
     __syncthreads();
     if (h == 0 && lane == 0)
-      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(fmaxf(sh.rmax[0], sh.rmax[1]) * cnorm));
+      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(nvfp4_tensor_scale(fmaxf(sh.rmax[0], sh.rmax[1]) * cnorm)));
   }
 }
 

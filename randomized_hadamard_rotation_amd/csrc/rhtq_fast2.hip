@@ -234,7 +234,7 @@ void fast2_kernel(KernelArgs a) {
       float m = wmax[0];
 #pragma unroll
       for (int w = 1; w < kWaves2; ++w) m = fmaxf(m, wmax[w]);
-      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(m * cnorm));
+      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(nvfp4_tensor_scale(m * cnorm)));
     }
   }
 }

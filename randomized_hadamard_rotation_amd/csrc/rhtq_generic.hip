@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(KernelArgs a) {
     if (tid == 0) {
       float m = wmax[0];
       for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, wmax[w]);
-      atomicMax((unsigned int*)a.tensor_scale, __float_as_uint(m * cnorm));
+      atomicMax((unsigned int*)a.tensor_scale, __float_as_uint(nvfp4_tensor_scale(m * cnorm)));
     }
   }
 }
@@ -338,7 +338,6 @@ hipError_t dispatch_width(const KernelArgs& a, hipStream_t s) {
 __global__ void zero_word_kernel(float* p) { *p = 0.0f; }
 
 // g = fl32(amax / (6 * 448)), in place over the accumulated amax.
-__global__ void finalize_tensor_scale_kernel(float* p) { *p = *p / 2688.0f; }
 
 }  // namespace
 
@@ -370,9 +369,5 @@ hipError_t launch_zero_word(float* p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_finalize_tensor_scale(float* p, hipStream_t s) {
-  hipLaunchKernelGGL(finalize_tensor_scale_kernel, dim3(1), dim3(1), 0, s, p);
-  return hipGetLastError();
-}
 
 }  // namespace rhtq

@@ -12,7 +12,7 @@ enum Op : int {
   OP_ROTATE = 0,   // y fp32
   OP_INT4 = 1,     // packed INT4 + scales
   OP_NVFP4 = 2,    // packed E2M1 + E4M3 scales, reads the tensor scale g
-  OP_AMAX = 3,     // atomic max of |y| bits into tensor_scale (NVFP4 dynamic pre-pass)
+  OP_AMAX = 3,     // atomic max of g = fl32(|y| / 2688) bits into tensor_scale (NVFP4 dynamic pre-pass)
   OP_INVERSE = 4,  // packed + scales -> x fp32
   OP_MXFP4 = 5,    // packed E2M1 + E8M0 scales of 32-blocks
 };
@@ -66,8 +66,7 @@ inline bool getenv_fast2_disabled() {
   return v;
 }
 
-// Tiny helper kernels for the dynamic NVFP4 tensor scale.
+// Clears the word the dynamic NVFP4 pre-pass accumulates into.
 hipError_t launch_zero_word(float* p, hipStream_t s);
-hipError_t launch_finalize_tensor_scale(float* p, hipStream_t s);
 
 }  // namespace rhtq
