@@ -35,6 +35,8 @@ OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_409
 KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast2.hip",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_epilogue.h",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_inverse_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_device.h",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_generic.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_api.cpp"]
@@ -105,6 +107,43 @@ def time_workload(R, torch, name, steps, warmup):
         "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
         "launches_per_step": 3 if w.fmt == "nvfp4" else 1,
     }
+
+
+INVERSE = ["kv_128_int4g128"]
+
+
+def time_inverse(R, torch, name, steps, warmup):
+    """The KV-cache read path: rhtq_inverse of the workload's own codes (fp32 output)."""
+    from workloads import WORKLOADS, generate
+    w = WORKLOADS[name]
+    x0, signs = generate(w, "cuda")
+    s_dev = torch.from_numpy(signs).to("cuda")
+    packed, scales, ts = R.rhtq_forward(x0, s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype)
+    del x0
+    nbytes = packed.numel() + scales.numel() * scales.element_size() + w.tokens * w.n * 4
+    sets = max(1, min(8, math.ceil(CACHE_DEFEAT_BYTES / nbytes)))
+    outs = [torch.empty((w.tokens, w.n), dtype=torch.float32, device="cuda") for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        R.rhtq_inverse(packed, scales, w.n, s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype,
+                       tensor_scale=ts, out=outs[i % sets], stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": name + " (inverse)", "rows": w.tokens, "n": w.n, "fmt": w.fmt, "group": w.group,
+            "ms_per_step": ms, "rows_per_s": w.tokens / (ms * 1e-3), "bytes_per_call": nbytes,
+            "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
 def cpu_baseline(name, budget_s=10.0):
@@ -207,6 +246,8 @@ def main():
         for name in OTHERS:
             if name != args.workload:
                 also.append(time_workload(R, torch, name, args.steps, args.warmup))
+        for name in INVERSE:
+            also.append(time_inverse(R, torch, name, args.steps, args.warmup))
 
     per_launch_ms = head["ms_per_step"] / head["launches_per_step"]
     traffic = traffic_for(args.workload)

@@ -161,8 +161,12 @@ int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_
   a.in_scales = scales;
   a.in_tensor_scale = tensor_scale;
   a.inv_fmt = fmt;
-  return from_hip(rhtq::launch_generic(rhtq::OP_INVERSE, RHTQ_IN_BF16, a,
-                                       reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!rhtq::getenv_fast_disabled()) {
+    const hipError_t e = rhtq::launch_inverse_fast(a, s);
+    if (e != hipErrorNotSupported) return from_hip(e);
+  }
+  return from_hip(rhtq::launch_generic(rhtq::OP_INVERSE, RHTQ_IN_BF16, a, s));
 }
 
 int rhtq_signs_from_seed(uint64_t seed, int32_t n, int8_t* host_out) {

@@ -393,16 +393,7 @@ hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
   }
   auto kern = fast_kernel<F, LOGM, OP>;
   const size_t lds = (size_t)S::NF * 64 * 16 + (size_t)kWaves * S::TBUF * 4;
-  static int max_blocks = 0;   // resident blocks per CU x CUs, computed once per instantiation
-  if (max_blocks == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorNotSupported;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kThreads, lds) != hipSuccess ||
-        per_cu < 1)
-      per_cu = 1;
-    max_blocks = cus * per_cu;
-  }
+  static const int max_blocks = resident_blocks((const void*)kern, kThreads, lds);
   const int64_t units = (a.rows + S::RPU - 1) / S::RPU;
   const int64_t want = (units + kWaves - 1) / kWaves;
   const int grid = (int)(want < max_blocks ? want : max_blocks);

@@ -253,15 +253,7 @@ hipError_t launch12(const KernelArgs& a, hipStream_t s) {
     if (!(a.group == kN || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
   auto kern = fast12_kernel<OP>;
-  static int max_blocks = 0;   // resident blocks per CU x CUs, computed once per instantiation
-  if (max_blocks == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorNotSupported;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kT, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    max_blocks = cus * per_cu;
-  }
+  static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();

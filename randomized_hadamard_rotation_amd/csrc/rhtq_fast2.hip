@@ -250,16 +250,7 @@ hipError_t launch2(const KernelArgs& a, hipStream_t s) {
 #else
   auto kern = fast2_kernel<LOGM, OP, 2>;
 #endif
-  static int max_blocks = 0;   // resident blocks per CU x CUs, computed once per instantiation
-  if (max_blocks == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorNotSupported;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kThreads2, 0) != hipSuccess ||
-        per_cu < 1)
-      per_cu = 1;
-    max_blocks = cus * per_cu;
-  }
+  static const int max_blocks = resident_blocks((const void*)kern, kThreads2, 0);
   const int64_t want = (a.rows + kWaves2 - 1) / kWaves2;
   const int grid = (int)(want < max_blocks ? want : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads2), 0, s, a);

@@ -48,6 +48,10 @@ hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s);
 // Two-stage matrix-core kernel for 1024-, 2048- and 4096-wide rows (called by launch_fast).
 hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s);
 
+// Integer matrix-core inverse for KV-cache rows (64, 128, 256) with one INT4 scale per row.
+// Returns hipErrorNotSupported for other cases (the generic kernel then runs).
+hipError_t launch_inverse_fast(const KernelArgs& a, hipStream_t s);
+
 // RHTQ_FORCE_GENERIC=1 routes every call to the generic kernels (read once).
 inline bool getenv_fast_disabled() {
   static const bool v = [] {
@@ -64,6 +68,20 @@ inline bool getenv_fast2_disabled() {
     return e != nullptr && e[0] == '1';
   }();
   return v;
+}
+
+// Resident workgroups of `kern` on the current device: CUs x workgroups per CU (at least one).
+// The persistent kernels size their grid with it; their loops stride over rows, so the value only
+// affects speed.  Callers keep it in a function-local static, which C++ initialises once and
+// thread-safely.
+inline int resident_blocks(const void* kern, int threads, size_t lds) {
+  int dev = 0, cus = 256, per_cu = 1;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return cus * per_cu;
 }
 
 // Clears the word the dynamic NVFP4 pre-pass accumulates into.

@@ -314,3 +314,24 @@ def test_inverse_round_trip(R, name):
     y = R.rhtq_rotate(x, s)
     torch.cuda.synchronize()
     assert np.allclose(O.inverse_rotate(to_np(y), s), xr, rtol=0, atol=1e-5 * np.abs(xr).max())
+
+
+@pytest.mark.parametrize("n", [64, 128, 256])
+def test_inverse_kv_rows(R, n):
+    """KV-cache read path (one INT4 scale per row, head dims 64 / 128 / 256): the device inverse of
+    device codes against the oracle's inverse of the same codes, ragged row counts included."""
+    import torch
+    for tokens in (1, 7, 1000, 1031):
+        for sd in ("f16", "f32"):
+            for seed in (None, 4):
+                say(f"inverse kv n={n} tokens={tokens} scale={sd} signs={seed}")
+                g = torch.Generator().manual_seed(n + tokens)
+                x = (torch.randn(tokens, n, generator=g) * torch.exp(torch.randn(tokens, 1, generator=g)))
+                x = x.to(torch.bfloat16).to(dev())
+                s = None if seed is None else splitmix64_signs(seed, n)
+                packed, scales, _ = R.rhtq_forward(x, s, fmt="int4", group=n, scale_dtype=sd)
+                xh = R.rhtq_inverse(packed, scales, n, s, fmt="int4", group=n, scale_dtype=sd)
+                torch.cuda.synchronize()
+                ref = O.inverse(to_np(packed), to_np(scales), s, "int4", n)
+                err = np.max(np.abs(to_np(xh) - ref), axis=1)
+                assert np.all(err <= 1e-6 * np.max(np.abs(ref), axis=1) + 1e-30), (n, tokens, sd, seed)
