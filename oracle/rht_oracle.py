@@ -46,6 +46,9 @@ Where the pages are silent the oracle takes these readings:
            |y| / (dec(s_b) g), ties to even; sign kept on values that round to 0
   R-e4m3   OCP FP8 E4M3FN: bias 7, max 448, subnormals, NaN never produced
   R-e2m1   OCP MX E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} <-> codes 0..7
+  R-block  block-diagonal rotation ("block-Hadamard-128" in the NVFP4 methodology
+           thread): one random sign vector over the whole row, then H_b on every
+           contiguous b-block, normalised by 1/sqrt(b): y = (I (x) H_b) D x / sqrt(b)
   R-mxfp4  per 32-block X = 2^(floor(log2(blockmax)) - 2) (2 = exponent of the
            largest E2M1 normal, 6 = 1.5 * 2^2), exponent clamped to [-127, 127]
            and stored as the E8M0 byte exponent + 127; codes = sign bit | E2M1 of
@@ -67,7 +70,7 @@ __all__ = [
     "unpack_nibbles", "e4m3_values", "e4m3_encode", "e4m3_decode", "e2m1_values",
     "e2m1_encode", "e2m1_decode", "nvfp4_tensor_scale", "quantize_nvfp4",
     "nvfp4_codes_from_scales", "mxfp4_scale_exponent", "mxfp4_codes_from_scales",
-    "quantize_mxfp4", "forward", "dequantize", "inverse",
+    "quantize_mxfp4", "rotate_blocked", "inverse_rotate_blocked", "forward", "dequantize", "inverse",
 ]
 
 
@@ -185,6 +188,26 @@ def rotate(x, signs=None) -> np.ndarray:
         u = fwht(u)
         y = np.einsum("ab,...bj->...aj", h12().astype(np.float64), u).reshape(x.shape)
     return y / np.sqrt(n)
+
+
+def rotate_blocked(x, signs, block: int) -> np.ndarray:
+    """Block-diagonal rotation: y = (I_{n/b} (x) H_b) D x / sqrt(b) per row, with the signs s of
+    length n applied before the blocks are transformed (NVFP4 methodology thread, the
+    block-Hadamard-128 comment).  block = n is rotate()."""
+    x = _as_f64(x)
+    n = x.shape[-1]
+    if block < 1 or block & (block - 1) or n % block:
+        raise ValueError("block must be a power of two dividing n")
+    u = (x * _signs(signs, n)).reshape(*x.shape[:-1], n // block, block)
+    return (fwht(u) / np.sqrt(block)).reshape(x.shape)
+
+
+def inverse_rotate_blocked(y, signs, block: int) -> np.ndarray:
+    """x = D (I (x) H_b^T) y / sqrt(b): the exact inverse of rotate_blocked()."""
+    y = np.asarray(y, dtype=np.float64)
+    n = y.shape[-1]
+    u = fwht(y.reshape(*y.shape[:-1], n // block, block)).reshape(y.shape)
+    return u * _signs(signs, n) / np.sqrt(block)
 
 
 def rotate_dense(x, signs=None) -> np.ndarray:
@@ -414,10 +437,12 @@ def quantize_mxfp4(y):
 # Whole forward / inverse
 # ---------------------------------------------------------------------------
 
-def forward(x, signs, fmt: str, group: int = 0, scale_dtype: str = "f32", tensor_scale=None):
-    """Rotate then quantise then pack.  Returns a dict with y (fp64), codes,
-    packed bytes, scales, tensor_scale (NVFP4) and the pre-rounding values v."""
-    y = rotate(x, signs)
+def forward(x, signs, fmt: str, group: int = 0, scale_dtype: str = "f32", tensor_scale=None,
+            block: int | None = None):
+    """Rotate (block-diagonally when block < n) then quantise then pack.  Returns a dict with
+    y (fp64), codes, packed bytes, scales, tensor_scale (NVFP4) and the pre-rounding values v."""
+    n = np.shape(x)[-1]
+    y = rotate(x, signs) if block is None or block == n else rotate_blocked(x, signs, block)
     if fmt == "int4":
         q, s, v = quantize_int4(y, group, scale_dtype)
         return {"y": y, "codes": q, "packed": pack_nibbles(q), "scales": s,
@@ -455,6 +480,10 @@ def dequantize(packed, scales, fmt: str, group: int = 0, tensor_scale=None) -> n
     return (e2m1_decode(c).reshape(T, n // 16, 16) * seff).reshape(T, n)
 
 
-def inverse(packed, scales, signs, fmt: str, group: int = 0, tensor_scale=None) -> np.ndarray:
-    """x_hat = D H^T y_hat / sqrt(n): dequantise then undo the rotation."""
-    return inverse_rotate(dequantize(packed, scales, fmt, group, tensor_scale), signs)
+def inverse(packed, scales, signs, fmt: str, group: int = 0, tensor_scale=None,
+            block: int | None = None) -> np.ndarray:
+    """x_hat = D H^T y_hat / sqrt(n) (blockwise when block < n): dequantise, undo the rotation."""
+    yh = dequantize(packed, scales, fmt, group, tensor_scale)
+    if block is None or block == yh.shape[-1]:
+        return inverse_rotate(yh, signs)
+    return inverse_rotate_blocked(yh, signs, block)

@@ -312,10 +312,27 @@ def pin_mxfp4_invariants(O):
     _check(np.all(np.abs(yhat - y) <= bound * X * (1 + 1e-9)), "MXFP4 dequant bound")
 
 
+def pin_blocked_rotation(O):
+    """Block-diagonal rotation against its dense definition kron(I, H_b) D / sqrt(b) (scipy's
+    Hadamard), block = n reducing to the full rotation, orthogonality and the exact inverse."""
+    rng = np.random.default_rng(21)
+    for n, b in [(64, 16), (256, 128), (512, 32), (3072, 1024), (96, 32)]:
+        x = rng.standard_normal((3, n))
+        s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+        dense = np.kron(np.eye(n // b), scipy.linalg.hadamard(b)) * s[None, :] / math.sqrt(b)
+        y = O.rotate_blocked(x, s, b)
+        _check(np.max(np.abs(y - x @ dense.T)) <= 1e-12 * np.abs(y).max(), f"blocked rotation n={n} b={b}")
+        _check(np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12), "blocked Parseval")
+        _check(np.max(np.abs(O.inverse_rotate_blocked(y, s, b) - x)) <= 1e-12 * np.abs(x).max(), "blocked inverse")
+    x = rng.standard_normal((2, 1024))
+    s = np.where(rng.random(1024) < 0.5, -1, 1).astype(np.int8)
+    _check(np.array_equal(O.rotate_blocked(x, s, 1024), O.rotate(x, s)), "block = n is the full rotation")
+
+
 ALL_PINS = [
     pin_sylvester_matches_scipy, pin_orthogonality, pin_fwht_equals_dense,
     pin_rotate_matches_scipy_definition, pin_parseval_and_roundtrip, pin_e3_closed_form,
     pin_e1_worked_example, pin_e2_worked_example, pin_int4_rounding, pin_fp16_storage,
     pin_e2m1, pin_e4m3, pin_nvfp4_invariants, pin_mxfp4_closed_form, pin_mxfp4_worked_block,
-    pin_mxfp4_invariants,
+    pin_mxfp4_invariants, pin_blocked_rotation,
 ]

@@ -161,10 +161,26 @@ def _mxfp4_bias_128(O):
     O.quantize_mxfp4 = q
 
 
+def _blocked_norm_sqrt_n(O):
+    orig = O.rotate_blocked
+    O.rotate_blocked = lambda x, s, b: orig(x, s, b) * math.sqrt(b) / math.sqrt(np.shape(x)[-1])
+
+
+def _blocked_signs_tiled(O):
+    """signs of the first block reused for every block instead of the full-length vector"""
+    orig = O.rotate_blocked
+
+    def bad(x, s, b):
+        n = np.shape(x)[-1]
+        st = None if s is None else np.tile(np.asarray(s)[:b], n // b)
+        return orig(x, st, b)
+    O.rotate_blocked = bad
+
+
 MUTATIONS = [_no_norm, _signs_after, _h12_transposed_in_rotate, _h12_typo, _round_half_away,
              _swap_nibbles, _scale_over_8, _fp16_truncation, _nvfp4_wrong_constant,
              _e2m1_ties_up, _e4m3_truncate, _fwht_skip_stage, _inverse_without_transpose,
-             _mxfp4_emax_one, _mxfp4_ceil, _mxfp4_bias_128]
+             _mxfp4_emax_one, _mxfp4_ceil, _mxfp4_bias_128, _blocked_norm_sqrt_n, _blocked_signs_tiled]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
