@@ -31,7 +31,7 @@ METRIC = "RHT+4-bit quant tokens/s & HBM GB/s (% of peak) at d=4096 and d=12288"
 HBM_PEAK_GBS = 8000.0
 CACHE_DEFEAT_BYTES = 512 << 20
 HEADLINE = "llama_4096_int4"
-OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_4096"]
+OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128"]
 KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast2.hip",
@@ -84,7 +84,7 @@ def time_workload(R, torch, name, steps, warmup):
     def step(i):
         packed, scales, ts = outs[i % sets]
         R.rhtq_forward(xs[i % sets], s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype,
-                       tensor_scale=ts, packed=packed, scales=scales, stream=stream)
+                       tensor_scale=ts, packed=packed, scales=scales, stream=stream, block=w.block or None)
 
     for i in range(warmup):
         step(i)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define RHTQ_ABI_VERSION 2   /* 2: MXFP4 format and E8M0 scales */
+#define RHTQ_ABI_VERSION 3   /* 2: MXFP4 format and E8M0 scales; 3: block-diagonal calls */
 
 /* Status codes. */
 #define RHTQ_OK           0   /* enqueued (or nothing to do)                       */
@@ -150,6 +150,31 @@ int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n,
 int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_scale,
                  int64_t tokens, int32_t n, const int8_t* signs, int fmt, int32_t group,
                  int scale_dtype, float* x_out, rhtq_stream_t stream);
+
+/*
+ * Block-diagonal variants (NVFP4 methodology thread, the block-Hadamard-128 comment: a Hadamard
+ * per 128-element block instead of one over the whole row).  Per row x of width n, with the sign
+ * vector s of length n applied first and H_b on every contiguous block of b elements:
+ *
+ *     y = (I_{n/b} (x) H_b) diag(s) x / sqrt(b)
+ *
+ *   block   a power of two, 16 <= block <= n, dividing n (block == n is the plain call)
+ *   group   quantisation groups lie inside a block: INT4 a power of two >= 16 dividing block
+ *           (group 0, one group per row, only when block == n); NVFP4 16; MXFP4 32
+ * Every other argument, layout and status is as in the plain call of the same name.
+ */
+int rhtq_rotate_blocked(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t block,
+                        const int8_t* signs, float* y_out, rhtq_stream_t stream);
+
+int rhtq_forward_blocked(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t block,
+                         const int8_t* signs, int fmt, int32_t group, int scale_dtype,
+                         uint8_t* packed_out, void* scales_out, float* tensor_scale,
+                         int tensor_scale_mode, rhtq_stream_t stream);
+
+/* x_out = diag(s) (I (x) H_b^T) y_hat / sqrt(b) with y_hat dequantised as in rhtq_inverse. */
+int rhtq_inverse_blocked(const uint8_t* packed, const void* scales, const float* tensor_scale,
+                         int64_t tokens, int32_t n, int32_t block, const int8_t* signs, int fmt,
+                         int32_t group, int scale_dtype, float* x_out, rhtq_stream_t stream);
 
 /*
  * Host helper: a random sign vector from a seed with splitmix64 (Steele, Lea and

@@ -4,7 +4,7 @@ The functions carry the names of the C entry points in include/rhtq.h and only
 marshal arguments: torch provides device memory and the current HIP stream, every
 step of the computation runs in the library's HIP kernels.  There is no CPU
 fallback: calls on CPU tensors raise, and importing the package raises when the
-library has not been built (python -m randomized_hadamard_rotation_amd.build).
+library has not been built (python randomized_hadamard_rotation_amd/build.py).
 """
 from __future__ import annotations
 
@@ -27,7 +27,8 @@ _DEFAULT_SCALE = {"int4": "f32", "nvfp4": "e4m3", "mxfp4": "e8m0"}
 _DEFAULT_GROUP = {"nvfp4": 16, "mxfp4": 32}
 
 EXPORTED = ["rhtq_abi_version", "rhtq_status_str", "rhtq_supported", "rhtq_rotate",
-            "rhtq_forward", "rhtq_inverse", "rhtq_signs_from_seed"]
+            "rhtq_forward", "rhtq_inverse", "rhtq_signs_from_seed", "rhtq_rotate_blocked",
+            "rhtq_forward_blocked", "rhtq_inverse_blocked"]
 
 
 class RhtqError(RuntimeError):
@@ -39,7 +40,7 @@ class RhtqError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m randomized_hadamard_rotation_amd.build`")
+                          "`python randomized_hadamard_rotation_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
     ci = ctypes.c_int
@@ -57,6 +58,12 @@ def _load() -> ctypes.CDLL:
     lib.rhtq_inverse.argtypes = [vp, vp, vp, i64, i32, vp, ci, i32, ci, vp, vp]
     lib.rhtq_signs_from_seed.restype = ci
     lib.rhtq_signs_from_seed.argtypes = [u64, i32, vp]
+    lib.rhtq_rotate_blocked.restype = ci
+    lib.rhtq_rotate_blocked.argtypes = [vp, ci, i64, i32, i32, vp, vp, vp]
+    lib.rhtq_forward_blocked.restype = ci
+    lib.rhtq_forward_blocked.argtypes = [vp, ci, i64, i32, i32, vp, ci, i32, ci, vp, vp, vp, ci, vp]
+    lib.rhtq_inverse_blocked.restype = ci
+    lib.rhtq_inverse_blocked.argtypes = [vp, vp, vp, i64, i32, i32, vp, ci, i32, ci, vp, vp]
     return lib
 
 
@@ -134,8 +141,9 @@ def rhtq_signs_from_seed(seed: int, n: int) -> np.ndarray:
     return out
 
 
-def rhtq_rotate(x, signs=None, out=None, stream=None):
-    """y = H_n diag(signs) x / sqrt(n) per row, fp32 [tokens][n]."""
+def rhtq_rotate(x, signs=None, out=None, stream=None, block=None):
+    """y = H_n diag(signs) x / sqrt(n) per row, fp32 [tokens][n].  With block = b < n the
+    rotation is block-diagonal: (I (x) H_b) diag(signs) x / sqrt(b)."""
     torch = _torch()
     _need_device(x)
     x = x.contiguous()
@@ -143,8 +151,12 @@ def rhtq_rotate(x, signs=None, out=None, stream=None):
     s = _signs_tensor(signs, n, x.device)
     if out is None:
         out = torch.empty((tokens, n), dtype=torch.float32, device=x.device)
-    _check(lib.rhtq_rotate(_ptr(x), _in_dtype(x), tokens, n, _ptr(s), _ptr(out), _stream(stream)),
-           "rhtq_rotate")
+    if block is None or block == n:
+        _check(lib.rhtq_rotate(_ptr(x), _in_dtype(x), tokens, n, _ptr(s), _ptr(out), _stream(stream)),
+               "rhtq_rotate")
+    else:
+        _check(lib.rhtq_rotate_blocked(_ptr(x), _in_dtype(x), tokens, n, block, _ptr(s), _ptr(out),
+                                       _stream(stream)), "rhtq_rotate_blocked")
     return out
 
 
@@ -155,13 +167,14 @@ def scale_shape(tokens: int, n: int, fmt: str, group: int):
 
 def rhtq_forward(x, signs=None, fmt: str = "int4", group: int = 0, scale_dtype: str | None = None,
                  tensor_scale=None, tensor_scale_mode: str = "dynamic", packed=None, scales=None,
-                 stream=None):
+                 stream=None, block=None):
     """Rotate, quantise, pack.  Returns (packed uint8 [tokens][n/2], scales, tensor_scale).
 
     INT4: scales fp32/fp16 [tokens][n/group] (group 0 = one per row).
     NVFP4: scales uint8 E4M3 [tokens][n/16]; tensor_scale a device float32 [1]
     (written in 'dynamic' mode, read in 'given' mode).
-    MXFP4: scales uint8 E8M0 [tokens][n/32]."""
+    MXFP4: scales uint8 E8M0 [tokens][n/32].
+    block = b < n: block-diagonal rotation (groups inside a block)."""
     torch = _torch()
     _need_device(x)
     x = x.contiguous()
@@ -179,14 +192,19 @@ def rhtq_forward(x, signs=None, fmt: str = "int4", group: int = 0, scale_dtype: 
     if fmt == "nvfp4" and tensor_scale is None:
         tensor_scale = torch.zeros(1, dtype=torch.float32, device=x.device)
     mode = RHTQ_TENSOR_SCALE_DYNAMIC if tensor_scale_mode == "dynamic" else RHTQ_TENSOR_SCALE_GIVEN
-    _check(lib.rhtq_forward(_ptr(x), _in_dtype(x), tokens, n, _ptr(s), _FMT[fmt], group,
-                            _SCALE[scale_dtype], _ptr(packed), _ptr(scales), _ptr(tensor_scale),
-                            mode, _stream(stream)), "rhtq_forward")
+    if block is None or block == n:
+        _check(lib.rhtq_forward(_ptr(x), _in_dtype(x), tokens, n, _ptr(s), _FMT[fmt], group,
+                                _SCALE[scale_dtype], _ptr(packed), _ptr(scales), _ptr(tensor_scale),
+                                mode, _stream(stream)), "rhtq_forward")
+    else:
+        _check(lib.rhtq_forward_blocked(_ptr(x), _in_dtype(x), tokens, n, block, _ptr(s), _FMT[fmt], group,
+                                        _SCALE[scale_dtype], _ptr(packed), _ptr(scales), _ptr(tensor_scale),
+                                        mode, _stream(stream)), "rhtq_forward_blocked")
     return packed, scales, tensor_scale
 
 
 def rhtq_inverse(packed, scales, n: int, signs=None, fmt: str = "int4", group: int = 0,
-                 scale_dtype: str | None = None, tensor_scale=None, out=None, stream=None):
+                 scale_dtype: str | None = None, tensor_scale=None, out=None, stream=None, block=None):
     """Dequantise and undo the rotation: x_hat fp32 [tokens][n]."""
     torch = _torch()
     _need_device(packed, scales, tensor_scale)
@@ -198,7 +216,12 @@ def rhtq_inverse(packed, scales, n: int, signs=None, fmt: str = "int4", group: i
     s = _signs_tensor(signs, n, packed.device)
     if out is None:
         out = torch.empty((tokens, n), dtype=torch.float32, device=packed.device)
-    _check(lib.rhtq_inverse(_ptr(packed.contiguous()), _ptr(scales.contiguous()), _ptr(tensor_scale),
-                            tokens, n, _ptr(s), _FMT[fmt], group, _SCALE[scale_dtype], _ptr(out),
-                            _stream(stream)), "rhtq_inverse")
+    if block is None or block == n:
+        _check(lib.rhtq_inverse(_ptr(packed.contiguous()), _ptr(scales.contiguous()), _ptr(tensor_scale),
+                                tokens, n, _ptr(s), _FMT[fmt], group, _SCALE[scale_dtype], _ptr(out),
+                                _stream(stream)), "rhtq_inverse")
+    else:
+        _check(lib.rhtq_inverse_blocked(_ptr(packed.contiguous()), _ptr(scales.contiguous()), _ptr(tensor_scale),
+                                        tokens, n, block, _ptr(s), _FMT[fmt], group, _SCALE[scale_dtype],
+                                        _ptr(out), _stream(stream)), "rhtq_inverse_blocked")
     return out

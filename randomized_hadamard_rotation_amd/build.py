@@ -1,6 +1,8 @@
 """Build librhtq.so in-tree with hipcc for gfx950.
 
-    python -m randomized_hadamard_rotation_amd.build
+    python randomized_hadamard_rotation_amd/build.py
+
+(run as a script: importing the package itself needs the library this builds)
 
 Every HIP translation unit is compiled with packed-FP32 instruction selection
 disabled; objects are compiled in parallel and linked into one shared library next

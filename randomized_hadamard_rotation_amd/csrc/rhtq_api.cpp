@@ -2,6 +2,8 @@
 // Every check happens before the first HIP call, so a rejected call enqueues nothing.
 #include <stdint.h>
 
+#include <climits>
+
 #include "rhtq.h"
 #include "rhtq_internal.h"
 
@@ -50,38 +52,48 @@ uintptr_t scale_align(int scale_dtype) {
   return scale_dtype == RHTQ_SCALE_F32 ? 4 : (scale_dtype == RHTQ_SCALE_F16 ? 2 : 1);
 }
 
-}  // namespace
+// ---- shared bodies of the plain and block-diagonal entry points -------------------------------
+// A block-diagonal call on rows of width n with blocks of b runs the kernels on tokens * n / b rows
+// of width b whose signs repeat every n elements; the memory layouts of x, y, codes and scales are
+// the same either way.  block == n is the plain call.
 
-extern "C" {
-
-int rhtq_abi_version(void) { return RHTQ_ABI_VERSION; }
-
-const char* rhtq_status_str(int status) {
-  switch (status) {
-    case RHTQ_OK: return "ok";
-    case RHTQ_EINVAL: return "invalid argument";
-    case RHTQ_EUNSUPPORTED: return "unsupported width, format or group";
-    case RHTQ_EHIP: return "HIP runtime error while enqueueing";
-    default: return "unknown status";
-  }
+bool block_ok(int32_t n, int32_t block) {
+  return block == n || (is_pow2(block) && block >= 16 && block < n && n % block == 0);
 }
 
-int rhtq_supported(int32_t n, int fmt, int32_t group) { return width_ok(n) && group_ok(n, fmt, group); }
-
-int rhtq_rotate(const void* x, int in_dtype, int64_t tokens, int32_t n, const int8_t* signs,
-                float* y_out, rhtq_stream_t stream) {
+// Fills the shape fields of a; RHTQ_OK or the status.
+int shape_args(int64_t tokens, int32_t n, int32_t block, rhtq::KernelArgs& a) {
   if (tokens < 0) return RHTQ_EINVAL;
+  if (!width_ok(n) || !block_ok(n, block)) return RHTQ_EUNSUPPORTED;
+  const int64_t per = n / block;
+  if (tokens > INT64_MAX / per) return RHTQ_EINVAL;
+  a.rows = tokens * per;
+  a.n = block;
+  a.sign_period = n;
+  return RHTQ_OK;
+}
+
+// Quantisation arguments of a call with blocks of b: the group lies inside a block; one group per
+// row (group 0) only when the block is the whole row.
+int check_quant_block(int32_t n, int32_t block, int fmt, int32_t group, int scale_dtype) {
+  const int st = check_quant_args(0, block, fmt, group, scale_dtype);
+  if (st != RHTQ_OK) return st;
+  if (group == 0 && block != n) return RHTQ_EUNSUPPORTED;
+  return RHTQ_OK;
+}
+
+int rotate_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t block, const int8_t* signs,
+                float* y_out, rhtq_stream_t stream) {
   if (in_dtype != RHTQ_IN_BF16 && in_dtype != RHTQ_IN_F32) return RHTQ_EINVAL;
-  if (!width_ok(n)) return RHTQ_EUNSUPPORTED;
+  rhtq::KernelArgs a{};
+  const int st = shape_args(tokens, n, block, a);
+  if (st != RHTQ_OK) return st;
   if (tokens == 0) return RHTQ_OK;
   if (!x || !y_out) return RHTQ_EINVAL;
   if (!aligned(x, 16) || !aligned(y_out, 16) || !aligned(signs, 16)) return RHTQ_EINVAL;
-  rhtq::KernelArgs a{};
   a.x = x;
   a.signs = signs;
-  a.rows = tokens;
-  a.n = n;
-  a.group = n;
+  a.group = a.n;
   a.y = y_out;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (in_dtype == RHTQ_IN_BF16) {
@@ -91,11 +103,13 @@ int rhtq_rotate(const void* x, int in_dtype, int64_t tokens, int32_t n, const in
   return from_hip(rhtq::launch_generic(rhtq::OP_ROTATE, in_dtype, a, s));
 }
 
-int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n, const int8_t* signs, int fmt,
-                 int32_t group, int scale_dtype, uint8_t* packed_out, void* scales_out,
+int forward_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t block, const int8_t* signs,
+                 int fmt, int32_t group, int scale_dtype, uint8_t* packed_out, void* scales_out,
                  float* tensor_scale, int tensor_scale_mode, rhtq_stream_t stream) {
   if (in_dtype != RHTQ_IN_BF16 && in_dtype != RHTQ_IN_F32) return RHTQ_EINVAL;
-  const int st = check_quant_args(tokens, n, fmt, group, scale_dtype);
+  rhtq::KernelArgs a{};
+  int st = shape_args(tokens, n, block, a);
+  if (st == RHTQ_OK) st = check_quant_block(n, block, fmt, group, scale_dtype);
   if (st != RHTQ_OK) return st;
   if (fmt == RHTQ_FMT_NVFP4 && tensor_scale_mode != RHTQ_TENSOR_SCALE_DYNAMIC &&
       tensor_scale_mode != RHTQ_TENSOR_SCALE_GIVEN)
@@ -108,12 +122,9 @@ int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n, const i
     return RHTQ_EINVAL;
   if (fmt == RHTQ_FMT_NVFP4 && !aligned(tensor_scale, 4)) return RHTQ_EINVAL;
 
-  rhtq::KernelArgs a{};
   a.x = x;
   a.signs = signs;
-  a.rows = tokens;
-  a.n = n;
-  a.group = group == 0 ? n : group;
+  a.group = group == 0 ? a.n : group;
   a.scale_dtype = scale_dtype;
   a.packed = packed_out;
   a.scales = scales_out;
@@ -139,10 +150,12 @@ int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n, const i
   return from_hip(run(rhtq::OP_NVFP4));
 }
 
-int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_scale, int64_t tokens,
-                 int32_t n, const int8_t* signs, int fmt, int32_t group, int scale_dtype, float* x_out,
-                 rhtq_stream_t stream) {
-  const int st = check_quant_args(tokens, n, fmt, group, scale_dtype);
+int inverse_impl(const uint8_t* packed, const void* scales, const float* tensor_scale, int64_t tokens,
+                 int32_t n, int32_t block, const int8_t* signs, int fmt, int32_t group, int scale_dtype,
+                 float* x_out, rhtq_stream_t stream) {
+  rhtq::KernelArgs a{};
+  int st = shape_args(tokens, n, block, a);
+  if (st == RHTQ_OK) st = check_quant_block(n, block, fmt, group, scale_dtype);
   if (st != RHTQ_OK) return st;
   if (tokens == 0) return RHTQ_OK;
   if (!packed || !scales || !x_out) return RHTQ_EINVAL;
@@ -150,11 +163,8 @@ int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_
   if (!aligned(packed, 4) || !aligned(x_out, 16) || !aligned(scales, scale_align(scale_dtype)) ||
       !aligned(signs, 16))
     return RHTQ_EINVAL;
-  rhtq::KernelArgs a{};
   a.signs = signs;
-  a.rows = tokens;
-  a.n = n;
-  a.group = group == 0 ? n : group;
+  a.group = group == 0 ? a.n : group;
   a.scale_dtype = scale_dtype;
   a.y = x_out;
   a.in_packed = packed;
@@ -167,6 +177,62 @@ int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_
     if (e != hipErrorNotSupported) return from_hip(e);
   }
   return from_hip(rhtq::launch_generic(rhtq::OP_INVERSE, RHTQ_IN_BF16, a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rhtq_abi_version(void) { return RHTQ_ABI_VERSION; }
+
+const char* rhtq_status_str(int status) {
+  switch (status) {
+    case RHTQ_OK: return "ok";
+    case RHTQ_EINVAL: return "invalid argument";
+    case RHTQ_EUNSUPPORTED: return "unsupported width, format or group";
+    case RHTQ_EHIP: return "HIP runtime error while enqueueing";
+    default: return "unknown status";
+  }
+}
+
+int rhtq_supported(int32_t n, int fmt, int32_t group) { return width_ok(n) && group_ok(n, fmt, group); }
+
+int rhtq_rotate(const void* x, int in_dtype, int64_t tokens, int32_t n, const int8_t* signs,
+                float* y_out, rhtq_stream_t stream) {
+  return rotate_impl(x, in_dtype, tokens, n, n, signs, y_out, stream);
+}
+
+int rhtq_rotate_blocked(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t block,
+                        const int8_t* signs, float* y_out, rhtq_stream_t stream) {
+  return rotate_impl(x, in_dtype, tokens, n, block, signs, y_out, stream);
+}
+
+int rhtq_forward(const void* x, int in_dtype, int64_t tokens, int32_t n, const int8_t* signs, int fmt,
+                 int32_t group, int scale_dtype, uint8_t* packed_out, void* scales_out,
+                 float* tensor_scale, int tensor_scale_mode, rhtq_stream_t stream) {
+  return forward_impl(x, in_dtype, tokens, n, n, signs, fmt, group, scale_dtype, packed_out, scales_out,
+                      tensor_scale, tensor_scale_mode, stream);
+}
+
+int rhtq_forward_blocked(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t block,
+                         const int8_t* signs, int fmt, int32_t group, int scale_dtype, uint8_t* packed_out,
+                         void* scales_out, float* tensor_scale, int tensor_scale_mode,
+                         rhtq_stream_t stream) {
+  return forward_impl(x, in_dtype, tokens, n, block, signs, fmt, group, scale_dtype, packed_out, scales_out,
+                      tensor_scale, tensor_scale_mode, stream);
+}
+
+int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_scale, int64_t tokens,
+                 int32_t n, const int8_t* signs, int fmt, int32_t group, int scale_dtype, float* x_out,
+                 rhtq_stream_t stream) {
+  return inverse_impl(packed, scales, tensor_scale, tokens, n, n, signs, fmt, group, scale_dtype, x_out, stream);
+}
+
+int rhtq_inverse_blocked(const uint8_t* packed, const void* scales, const float* tensor_scale, int64_t tokens,
+                         int32_t n, int32_t block, const int8_t* signs, int fmt, int32_t group, int scale_dtype,
+                         float* x_out, rhtq_stream_t stream) {
+  return inverse_impl(packed, scales, tensor_scale, tokens, n, block, signs, fmt, group, scale_dtype, x_out,
+                      stream);
 }
 
 int rhtq_signs_from_seed(uint64_t seed, int32_t n, int8_t* host_out) {

@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   extern __shared__ uint32_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  float* tbuf = reinterpret_cast<float*>(smem + S::NF * 256) + wave * S::TBUF;
+  float* tbuf = reinterpret_cast<float*>(smem + (a.sign_period > S::UNIT ? a.sign_period / S::UNIT : 1) * S::NF * 256) +
+                wave * S::TBUF;
 
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)S::N));
   const int64_t units = (a.rows + S::RPU - 1) / S::RPU;
@@ -97,14 +98,17 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   uint4 raw[S::NF];
   load_unit<S>(x, u, units, a.rows, lane, raw);
 
-  // bf16 sign-bit masks in load order: entry f * 64 + lane holds the four mask dwords
-  // (bit 15 / bit 31 of each bf16 pair) of the 8 elements that lane loads for fragment f
+  // bf16 sign-bit masks in load order: entry (slice * NF + f) * 64 + lane holds the four mask
+  // dwords (bit 15 / bit 31 of each bf16 pair) of the 8 elements that lane loads for fragment f of
+  // a unit whose first element sits at slice * UNIT within the sign period.  The table spans
+  // max(UNIT, sign period) elements: one slice unless the rows are blocks of longer rows.
   uint4* sign_tab = reinterpret_cast<uint4*>(smem);
-  for (int k = threadIdx.x; k < S::NF * 64; k += kThreads) {
+  const int slices = a.sign_period > S::UNIT ? a.sign_period / S::UNIT : 1;
+  for (int k = threadIdx.x; k < slices * S::NF * 64; k += kThreads) {
     uint4 m = make_uint4(0, 0, 0, 0);
     if (a.signs) {
-      const int kl = k & 63;
-      const int col = (512 * (k >> 6) + 32 * (kl & 15) + 8 * (kl >> 4)) % S::N;
+      const int kl = k & 63, kf = k >> 6;   // kf = slice * NF + f
+      const int col = (S::UNIT * (kf / S::NF) + 512 * (kf % S::NF) + 32 * (kl & 15) + 8 * (kl >> 4)) % a.sign_period;
       const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + col);
       m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
       m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
@@ -126,13 +130,14 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     if constexpr (!S::PREFETCH)
       if (u != (int64_t)blockIdx.x * kWaves + wave) load_unit<S>(x, u, units, a.rows, lane, raw);
     const int64_t ubase = u * S::UNIT;                 // element index of the unit start
+    const int slice = slices > 1 ? (int)((ubase % a.sign_period) / S::UNIT) : 0;
     const int64_t valid = (a.rows - u * S::RPU) * S::N;  // elements of the unit that exist (may exceed UNIT)
 
     // ---------------- sign, MFMA ----------------
     float v[S::NF][2][4];
 #pragma unroll
     for (int f = 0; f < S::NF; ++f) {
-      const uint4 m = sign_tab[f * 64 + lane];
+      const uint4 m = sign_tab[(slice * S::NF + f) * 64 + lane];
       uint4 r = raw[f];
       r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
       bf16x8 av;
@@ -392,7 +397,9 @@ hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
     if (!(a.group == S::N || a.group <= S::CHUNK)) return hipErrorNotSupported;
   }
   auto kern = fast_kernel<F, LOGM, OP>;
-  const size_t lds = (size_t)S::NF * 64 * 16 + (size_t)kWaves * S::TBUF * 4;
+  const int slices = a.sign_period > S::UNIT ? a.sign_period / S::UNIT : 1;
+  const size_t lds = (size_t)slices * S::NF * 64 * 16 + (size_t)kWaves * S::TBUF * 4;
+  if (lds > 65536) return hipErrorNotSupported;
   static const int max_blocks = resident_blocks((const void*)kern, kThreads, lds);
   const int64_t units = (a.rows + S::RPU - 1) / S::RPU;
   const int64_t want = (units + kWaves - 1) / kWaves;

@@ -249,6 +249,7 @@ __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
 
 template <int OP>
 hipError_t launch12(const KernelArgs& a, hipStream_t s) {
+  if (a.sign_period != kN) return hipErrorNotSupported;
   if constexpr (OP == OP_INT4) {
     if (!(a.group == kN || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }

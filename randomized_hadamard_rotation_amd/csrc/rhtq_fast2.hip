@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RHTQ_
 void fast2_kernel(KernelArgs a) {
   using S2 = Shape2<LOGM>;
   constexpr int N = S2::N, NF = S2::NF, NG = S2::NG, R = S2::R;
-  __shared__ uint4 sign_tab[NF * 64];
+  extern __shared__ uint4 sign_tab[];   // [sign period / N][NF][64]
   __shared__ float wmax[kWaves2];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -84,13 +84,16 @@ void fast2_kernel(KernelArgs a) {
   if constexpr (DEPTH >= 1) load_row<LOGM>(x, row, a.rows, lane, raw);
   if constexpr (DEPTH == 2) load_row<LOGM>(x, row + rstride, a.rows, lane, raw2);
 
-  // bf16 sign-bit masks in load order: entry f * 64 + lane covers the 8 elements that
-  // lane loads for fragment f
-  for (int k = threadIdx.x; k < NF * 64; k += kThreads2) {
+  // bf16 sign-bit masks in load order: entry (slice * NF + f) * 64 + lane covers the 8 elements
+  // that lane loads for fragment f of a row whose index is slice modulo the rows per sign period
+  // (one slice unless the rows are blocks of longer rows)
+  const int slices = a.sign_period / N;
+  for (int k = threadIdx.x; k < slices * NF * 64; k += kThreads2) {
     uint4 m = make_uint4(0, 0, 0, 0);
     if (a.signs) {
-      const int kl = k & 63;
-      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + 512 * (k >> 6) + 32 * (kl & 15) + 8 * (kl >> 4));
+      const int kl = k & 63, kf = k >> 6;
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + N * (kf / NF) + 512 * (kf % NF) + 32 * (kl & 15) +
+                                                       8 * (kl >> 4));
       m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
       m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
       m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
@@ -119,9 +122,10 @@ void fast2_kernel(KernelArgs a) {
     if constexpr (DEPTH == 0) load_row<LOGM>(x, row, a.rows, lane, raw);
     // ---------------- stage 1 ----------------
     float d1[NF][2][4];
+    const int slice = slices > 1 ? (int)(row % slices) : 0;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const uint4 m = sign_tab[f * 64 + lane];
+      const uint4 m = sign_tab[(slice * NF + f) * 64 + lane];
       uint4 r = raw[f];
       r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
       bf16x8 av;
@@ -250,10 +254,12 @@ hipError_t launch2(const KernelArgs& a, hipStream_t s) {
 #else
   auto kern = fast2_kernel<LOGM, OP, 2>;
 #endif
-  static const int max_blocks = resident_blocks((const void*)kern, kThreads2, 0);
+  static const int max_blocks = resident_blocks((const void*)kern, kThreads2, S2::NF * 64 * 16);
   const int64_t want = (a.rows + kWaves2 - 1) / kWaves2;
   const int grid = (int)(want < max_blocks ? want : max_blocks);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads2), 0, s, a);
+  const size_t lds = (size_t)(a.sign_period / S2::N) * S2::NF * 64 * 16;
+  if (lds > 65536) return hipErrorNotSupported;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads2), lds, s, a);
   return hipGetLastError();
 }
 

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(KernelArgs a) {
             v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
           }
           if (a.signs) {
-            const int col = e0 % N;
+            const int col = (int)((gbase + e0) % a.sign_period);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
               if (a.signs[col + e] < 0) v[e] = -v[e];
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(KernelArgs a) {
         for (int e = 0; e < 8; ++e) v[e] = lds[lds_idx(e0 + e)] * cnorm;
         if constexpr (OP == OP_INVERSE) {
           if (a.signs) {
-            const int col = e0 % N;
+            const int col = (int)((gbase + e0) % a.sign_period);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
               if (a.signs[col + e] < 0) v[e] = -v[e];

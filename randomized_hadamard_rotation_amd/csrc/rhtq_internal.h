@@ -32,6 +32,9 @@ struct KernelArgs {
   const void* in_scales;    // OP_INVERSE input
   const float* in_tensor_scale;  // OP_INVERSE input (NVFP4)
   int32_t inv_fmt;          // OP_INVERSE: RHTQ_FMT_*
+  int32_t sign_period;      // signs repeat every sign_period elements of the flattened rows (a multiple
+                            // of n; n itself except for block-diagonal calls, where rows of width n are
+                            // the b-blocks of longer rows and the sign vector spans the long row)
 };
 
 // Generic LDS-staged path: every width, both input types, every op.

@@ -148,7 +148,7 @@ hipError_t launch_inv(const KernelArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_inverse_fast(const KernelArgs& a, hipStream_t s) {
-  if (a.inv_fmt != RHTQ_FMT_INT4 || a.group != a.n) return hipErrorNotSupported;
+  if (a.inv_fmt != RHTQ_FMT_INT4 || a.group != a.n || a.sign_period != a.n) return hipErrorNotSupported;
   if (reinterpret_cast<uintptr_t>(a.in_packed) & 7) return hipErrorNotSupported;
   switch (a.n) {
     case 64: return launch_inv<6>(a, s);

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(R):
     decl = declared_functions()
-    assert len(decl) == 7
+    assert len(decl) == 10
     lib = ctypes.CDLL(R.LIB_PATH)
     for name in decl:
         assert hasattr(lib, name), name
@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(R):
 
 
 def test_abi_version_and_status_strings(R):
-    assert R.rhtq_abi_version() == 2
+    assert R.rhtq_abi_version() == 3
     assert R.rhtq_status_str(0) == "ok"
     assert "invalid" in R.rhtq_status_str(1)
     assert "unsupported" in R.rhtq_status_str(2)
@@ -110,3 +110,25 @@ def test_python_binding_refuses_cpu_tensors(R):
         R.rhtq_rotate(torch.zeros(2, 128, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         R.rhtq_forward(torch.zeros(2, 128, dtype=torch.bfloat16))
+
+
+def test_blocked_host_validation(R):
+    lib = R.lib
+    fake = ctypes.c_void_p(0x100000)          # never dereferenced: every call below fails validation
+    s = ctypes.c_void_p(0)
+    RB = lambda *a: lib.rhtq_rotate_blocked(*a)
+    assert RB(fake, 0, 4, 4096, 100, None, fake, s) == R.RHTQ_EUNSUPPORTED     # block not a power of two
+    assert RB(fake, 0, 4, 4096, 8, None, fake, s) == R.RHTQ_EUNSUPPORTED       # below 16
+    assert RB(fake, 0, 4, 4096, 8192, None, fake, s) == R.RHTQ_EUNSUPPORTED    # above n
+    assert RB(fake, 0, 4, 3072, 2048, None, fake, s) == R.RHTQ_EUNSUPPORTED    # does not divide n
+    assert RB(fake, 0, -1, 4096, 128, None, fake, s) == R.RHTQ_EINVAL
+    assert RB(None, 0, 0, 4096, 128, None, None, s) == R.RHTQ_OK               # empty: no-op
+    assert RB(fake, 0, 2**62, 4096, 16, None, fake, s) == R.RHTQ_EINVAL        # rows overflow
+    FB = lambda *a: lib.rhtq_forward_blocked(*a)
+    assert FB(fake, 0, 4, 4096, 128, None, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EUNSUPPORTED  # per-row
+    assert FB(fake, 0, 4, 4096, 128, None, 0, 256, 0, fake, fake, None, 0, s) == R.RHTQ_EUNSUPPORTED  # group > block
+    assert FB(None, 0, 4, 4096, 128, None, 0, 128, 1, fake, fake, None, 0, s) == R.RHTQ_EINVAL     # null x
+    assert FB(None, 0, 0, 4096, 4096, None, 0, 0, 0, None, None, None, 0, s) == R.RHTQ_OK
+    IB = lambda *a: lib.rhtq_inverse_blocked(*a)
+    assert IB(fake, fake, None, 4, 4096, 128, None, 2, 16, 3, fake, s) == R.RHTQ_EUNSUPPORTED      # mxfp4 group 16
+    assert IB(None, fake, None, 4, 4096, 128, None, 2, 32, 3, fake, s) == R.RHTQ_EINVAL

@@ -48,18 +48,24 @@ def to_np(t):
 
 def run_forward(R, x, s, fmt, group, scale_dtype, **kw):
     import torch
+    if kw.get("block") in (0, None):
+        kw.pop("block", None)
     packed, scales, ts = R.rhtq_forward(x, s, fmt=fmt, group=group, scale_dtype=scale_dtype, **kw)
     torch.cuda.synchronize()
     return to_np(packed), to_np(scales), (None if ts is None else float(ts.item()))
 
 
-def check_forward(R, x, s, fmt, group, scale_dtype, rows=None, y_ref=None, g_ref=None):
+def ref_rotate(x, s, block=0):
+    return O.rotate(x, s) if not block else O.rotate_blocked(x, s, block)
+
+
+def check_forward(R, x, s, fmt, group, scale_dtype, rows=None, y_ref=None, g_ref=None, block=0):
     """Device forward of all rows of x; oracle on `rows` (all by default)."""
-    packed, scales, g = run_forward(R, x, s, fmt, group, scale_dtype)
+    packed, scales, g = run_forward(R, x, s, fmt, group, scale_dtype, block=block)
     if rows is None:
         rows = np.arange(x.shape[0])
     if y_ref is None:
-        y_ref = O.rotate(x[rows].cpu(), s)
+        y_ref = ref_rotate(x[rows].cpu(), s, block)
     if fmt == "int4":
         return C.check_int4(packed[rows], scales[rows], y_ref, group, scale_dtype)
     if fmt == "mxfp4":
@@ -145,7 +151,8 @@ def test_e3_closed_form(R, n, k):
 # ----------------------------------------------------------------------------
 
 REDUCED = [("tiny_128_int4", 64), ("llama_4096_int4", 203), ("downproj_12288_int4g128", 37),
-           ("kv_128_int4g128", 4099), ("nvfp4_4096", 131), ("mxfp4_4096", 131)]
+           ("kv_128_int4g128", 4099), ("nvfp4_4096", 131), ("mxfp4_4096", 131),
+           ("blockh128_4096_int4g128", 131)]
 
 
 @pytest.mark.parametrize("name,tokens", REDUCED)
@@ -153,12 +160,12 @@ def test_workload_reduced(R, name, tokens):
     w = WORKLOADS[name]
     say(f"{name} reduced to {tokens} rows")
     x, s = x_to(w, tokens)
-    rep = check_forward(R, x, s, w.fmt, w.group, w.scale_dtype)
+    rep = check_forward(R, x, s, w.fmt, w.group, w.scale_dtype, block=w.block)
     print(rep)
 
 
 @pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
-                                  "nvfp4_4096", "mxfp4_4096"])
+                                  "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128"])
 def test_workload_full_size_sampled(R, name):
     """Full-size input on the device in the same launch shape as the benchmark;
     the oracle checks sampled rows (first, last, every sink row it can find, random)."""
@@ -179,11 +186,12 @@ def test_workload_full_size_sampled(R, name):
         for r0 in range(0, T, 2048):
             amax = max(amax, float(np.max(np.abs(O.rotate(x[r0:r0 + 2048].cpu(), s)))))
         g_ref = np.float32(amax / 2688.0)
-    rep = check_forward(R, x, s, w.fmt, w.group, w.scale_dtype, rows=rows, g_ref=g_ref)
+    rep = check_forward(R, x, s, w.fmt, w.group, w.scale_dtype, rows=rows, g_ref=g_ref, block=w.block)
     print(rep)
     # properties over the whole output: INT4 codes never -8
     if w.fmt == "int4":
-        packed, _, _ = R.rhtq_forward(x, s, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype)
+        packed, _, _ = R.rhtq_forward(x, s, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype,
+                                      block=w.block or None)
         lo = (packed & 0xF)
         hi = (packed >> 4)
         assert not bool(((lo == 8) | (hi == 8)).any())
@@ -335,3 +343,44 @@ def test_inverse_kv_rows(R, n):
                 ref = O.inverse(to_np(packed), to_np(scales), s, "int4", n)
                 err = np.max(np.abs(to_np(xh) - ref), axis=1)
                 assert np.all(err <= 1e-6 * np.max(np.abs(ref), axis=1) + 1e-30), (n, tokens, sd, seed)
+
+
+BLOCKED = [(4096, 128), (4096, 1024), (12288, 1024), (12288, 4096), (256, 128), (2048, 16), (8192, 2048),
+           (1024, 512)]
+
+
+@pytest.mark.parametrize("n,block", BLOCKED)
+def test_blocked_rotation_and_quantisation(R, n, block):
+    """Block-diagonal rotation (NVFP4 methodology thread, block-Hadamard-128): full-length signs, then
+    H_b per block; every format whose groups fit a block; the inverse of the device's codes."""
+    import torch
+    g = torch.Generator().manual_seed(n + block)
+    xc = torch.randn(21, n, generator=g) * torch.exp(torch.randn(n, generator=g))
+    s = splitmix64_signs(8, n)
+    for dt in (torch.bfloat16, torch.float32):
+        x = xc.to(dt).to(dev())
+        y_ref = O.rotate_blocked(x.cpu(), s, block)
+        say(f"blocked rotate n={n} b={block} dtype={dt}")
+        C.check_rotation(to_np(R.rhtq_rotate(x, s, block=block)), y_ref)
+        cases = [("int4", 16, "f16"), ("nvfp4", 16, "e4m3")]
+        if block >= 32:
+            cases.append(("mxfp4", 32, "e8m0"))
+        if block >= 128:
+            cases.append(("int4", 128, "f32"))
+        for fmt, grp, sd in cases:
+            say(f"blocked {fmt} g{grp} n={n} b={block} dtype={dt}")
+            packed, scales, ts = R.rhtq_forward(x, s, fmt=fmt, group=grp, scale_dtype=sd, block=block)
+            torch.cuda.synchronize()
+            p, sc = to_np(packed), to_np(scales)
+            if fmt == "int4":
+                C.check_int4(p, sc, y_ref, grp, sd)
+            elif fmt == "mxfp4":
+                C.check_mxfp4(p, sc, y_ref)
+            else:
+                C.check_nvfp4(p, sc, float(ts.item()), y_ref)
+            xh = R.rhtq_inverse(packed, scales, n, s, fmt=fmt, group=grp, scale_dtype=sd, tensor_scale=ts,
+                                block=block)
+            torch.cuda.synchronize()
+            ref = O.inverse(p, sc, s, fmt, grp, None if ts is None else float(ts.item()), block=block)
+            err = np.max(np.abs(to_np(xh) - ref), axis=1)
+            assert np.all(err <= 1e-5 * np.max(np.abs(ref), axis=1) + 1e-30)

@@ -61,6 +61,7 @@ class Workload:
     scale_dtype: str       # "f32", "f16", "e4m3" or "e8m0"
     tokens_per_row: float = 1.0   # KV rows: 1/32 token per row (32 heads)
     description: str = ""
+    block: int = 0                # block-diagonal rotation with blocks of this size (0: whole row)
 
     def with_tokens(self, tokens: int) -> "Workload":
         return dataclasses.replace(self, tokens=tokens)
@@ -87,6 +88,11 @@ WORKLOADS = {
         "nvfp4_4096", 16384, 4096, "bf16", "llama_like", 5, 0, "nvfp4", 16, "e4m3",
         description="16384 x 4096 bf16, llama-like recipe with sinks; E2M1 codes, E4M3 block-16 "
                     "scales, fp32 tensor scale = amax/(6*448)"),
+    # block-Hadamard-128 before INT4-g128 on the hidden width (the NVFP4 methodology thread's ablation)
+    "blockh128_4096_int4g128": Workload(
+        "blockh128_4096_int4g128", 16384, 4096, "bf16", "llama_like", 7, 0, "int4", 128, "f16",
+        description="16384 x 4096 bf16, llama-like recipe; block-diagonal H128 with full-length signs, "
+                    "INT4 group 128, fp16 scales", block=128),
     # MXFP4 on the NVFP4 shape: the thread compares the two FP4 formats on the same model
     "mxfp4_4096": Workload(
         "mxfp4_4096", 16384, 4096, "bf16", "llama_like", 6, 0, "mxfp4", 32, "e8m0",
