@@ -158,7 +158,10 @@ int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_
  *
  *     y = (I_{n/b} (x) H_b) diag(s) x / sqrt(b)
  *
- *   block   a power of two, 16 <= block <= n, dividing n (block == n is the plain call)
+ *   block   a power of two, 16 <= block < n, dividing n; the row width n itself may then be any
+ *           multiple of block up to 2^20 (for example 11008 = 86 x 128, the Llama-2-7B
+ *           intermediate width, which has no Hadamard matrix of its own in this library).
+ *           block == n is the plain call (n a supported width).
  *   group   quantisation groups lie inside a block: INT4 a power of two >= 16 dividing block
  *           (group 0, one group per row, only when block == n); NVFP4 16; MXFP4 32
  * Every other argument, layout and status is as in the plain call of the same name.

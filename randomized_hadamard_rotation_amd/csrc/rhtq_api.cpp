@@ -57,14 +57,19 @@ uintptr_t scale_align(int scale_dtype) {
 // of width b whose signs repeat every n elements; the memory layouts of x, y, codes and scales are
 // the same either way.  block == n is the plain call.
 
+// Rows of a block-diagonal call need not have a Hadamard width themselves (11008 = 86 x 128 for
+// the Llama-2-7B intermediate activation): only the block must, and it must divide the row.
+constexpr int32_t kMaxBlockedWidth = 1 << 20;
+
 bool block_ok(int32_t n, int32_t block) {
-  return block == n || (is_pow2(block) && block >= 16 && block < n && n % block == 0);
+  if (block == n) return width_ok(n);
+  return is_pow2(block) && block >= 16 && block < n && n % block == 0 && n <= kMaxBlockedWidth;
 }
 
 // Fills the shape fields of a; RHTQ_OK or the status.
 int shape_args(int64_t tokens, int32_t n, int32_t block, rhtq::KernelArgs& a) {
   if (tokens < 0) return RHTQ_EINVAL;
-  if (!width_ok(n) || !block_ok(n, block)) return RHTQ_EUNSUPPORTED;
+  if (!block_ok(n, block)) return RHTQ_EUNSUPPORTED;
   const int64_t per = n / block;
   if (tokens > INT64_MAX / per) return RHTQ_EINVAL;
   a.rows = tokens * per;

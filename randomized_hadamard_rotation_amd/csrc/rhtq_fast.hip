@@ -79,14 +79,21 @@ __device__ __forceinline__ void load_unit(const uint16_t* x, int64_t u, int64_t 
   }
 }
 
+// Units of the sign table: lcm(UNIT, sign period) / UNIT (UNIT is a power of two).
+template <typename S>
+__host__ __device__ inline int sign_slices(int period) {
+  int g = S::UNIT;
+  while (period % g) g >>= 1;   // gcd(period, UNIT)
+  return period / g;            // lcm / UNIT = period / gcd
+}
+
 template <int F, int LOGM, int OP>
 __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   using S = Shape<F, LOGM>;
   extern __shared__ uint32_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  float* tbuf = reinterpret_cast<float*>(smem + (a.sign_period > S::UNIT ? a.sign_period / S::UNIT : 1) * S::NF * 256) +
-                wave * S::TBUF;
+  float* tbuf = reinterpret_cast<float*>(smem + sign_slices<S>(a.sign_period) * S::NF * 256) + wave * S::TBUF;
 
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)S::N));
   const int64_t units = (a.rows + S::RPU - 1) / S::RPU;
@@ -100,10 +107,10 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
 
   // bf16 sign-bit masks in load order: entry (slice * NF + f) * 64 + lane holds the four mask
   // dwords (bit 15 / bit 31 of each bf16 pair) of the 8 elements that lane loads for fragment f of
-  // a unit whose first element sits at slice * UNIT within the sign period.  The table spans
-  // max(UNIT, sign period) elements: one slice unless the rows are blocks of longer rows.
+  // a unit starting at element slice * UNIT modulo lcm(UNIT, sign period): one slice unless the rows
+  // are blocks of longer rows.
   uint4* sign_tab = reinterpret_cast<uint4*>(smem);
-  const int slices = a.sign_period > S::UNIT ? a.sign_period / S::UNIT : 1;
+  const int slices = sign_slices<S>(a.sign_period);
   for (int k = threadIdx.x; k < slices * S::NF * 64; k += kThreads) {
     uint4 m = make_uint4(0, 0, 0, 0);
     if (a.signs) {
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     if constexpr (!S::PREFETCH)
       if (u != (int64_t)blockIdx.x * kWaves + wave) load_unit<S>(x, u, units, a.rows, lane, raw);
     const int64_t ubase = u * S::UNIT;                 // element index of the unit start
-    const int slice = slices > 1 ? (int)((ubase % a.sign_period) / S::UNIT) : 0;
+    const int slice = slices > 1 ? (int)((ubase % ((int64_t)slices * S::UNIT)) / S::UNIT) : 0;
     const int64_t valid = (a.rows - u * S::RPU) * S::N;  // elements of the unit that exist (may exceed UNIT)
 
     // ---------------- sign, MFMA ----------------
@@ -397,7 +404,7 @@ hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
     if (!(a.group == S::N || a.group <= S::CHUNK)) return hipErrorNotSupported;
   }
   auto kern = fast_kernel<F, LOGM, OP>;
-  const int slices = a.sign_period > S::UNIT ? a.sign_period / S::UNIT : 1;
+  const int slices = sign_slices<S>(a.sign_period);
   const size_t lds = (size_t)slices * S::NF * 64 * 16 + (size_t)kWaves * S::TBUF * 4;
   if (lds > 65536) return hipErrorNotSupported;
   static const int max_blocks = resident_blocks((const void*)kern, kThreads, lds);

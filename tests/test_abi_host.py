@@ -121,6 +121,9 @@ def test_blocked_host_validation(R):
     assert RB(fake, 0, 4, 4096, 8, None, fake, s) == R.RHTQ_EUNSUPPORTED       # below 16
     assert RB(fake, 0, 4, 4096, 8192, None, fake, s) == R.RHTQ_EUNSUPPORTED    # above n
     assert RB(fake, 0, 4, 3072, 2048, None, fake, s) == R.RHTQ_EUNSUPPORTED    # does not divide n
+    assert RB(fake, 0, 4, 11008, 512, None, fake, s) == R.RHTQ_EUNSUPPORTED    # 11008 = 21.5 x 512
+    assert RB(fake, 0, 4, 11000, 11000, None, fake, s) == R.RHTQ_EUNSUPPORTED  # plain call: no H_11000
+    assert RB(fake, 0, 4, (1 << 20) + 128, 128, None, fake, s) == R.RHTQ_EUNSUPPORTED
     assert RB(fake, 0, -1, 4096, 128, None, fake, s) == R.RHTQ_EINVAL
     assert RB(None, 0, 0, 4096, 128, None, None, s) == R.RHTQ_OK               # empty: no-op
     assert RB(fake, 0, 2**62, 4096, 16, None, fake, s) == R.RHTQ_EINVAL        # rows overflow
