@@ -37,6 +37,12 @@ Where the pages are silent the oracle takes these readings:
   R-side   signs first, then H; for row vectors Y = X D H^T
   R-h12    the order-12 factor is the Williamson array built from A = J3 and
            B = J3 - 2 I3; for n = 12 m, H_n = H12 (x) H_m with j = j1*m + j2
+  R-h172   the order-172 factor (QuaRot reviews, review 2 Questions: 172 is the
+           non-power-of-two part of the Llama 2 7B width, 11008 = 172 x 64) is the Williamson array of four symmetric circulants of
+           order 43 whose first rows are +1 at 0 and constant on each coset of the
+           order-6 subgroup {1, 6, 7, 36, 37, 42} of the units mod 43 (cosets
+           3^c * K, c = 0..6, signs in WILLIAMSON43); for n = 172 m, H_n = H172 (x) H_m
+           with j = j1*m + j2, as for 12
   R-int4   symmetric absmax INT4: scale = amax / 7, stored (fp32 or fp16, RNE),
            codes = clamp(round_half_even(y / stored_scale), -8, 7); a zero
            group has scale 0 and codes 0
@@ -65,7 +71,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "sylvester", "h12", "hadamard", "split_width", "fwht", "rotate", "rotate_dense",
+    "sylvester", "h12", "h172", "WILLIAMSON43", "williamson43_rows", "factor_matrix", "hadamard", "split_width", "fwht", "rotate", "rotate_dense",
     "inverse_rotate", "int4_scale_store", "int4_codes", "quantize_int4", "pack_nibbles",
     "unpack_nibbles", "e4m3_values", "e4m3_encode", "e4m3_decode", "e2m1_values",
     "e2m1_encode", "e2m1_decode", "nvfp4_tensor_scale", "quantize_nvfp4",
@@ -110,21 +116,82 @@ def h12() -> np.ndarray:
                      [-B, -B, B, A]])
 
 
+# Coset signs of the four order-43 circulants (A, B, C, D) of the order-172 factor:
+# entry c is the sign of every k = 3^c * t mod 43, t in {1, 6, 7, 36, 37, 42}.
+WILLIAMSON43 = (
+    (+1, +1, +1, +1, -1, -1, -1),
+    (-1, +1, +1, -1, -1, +1, -1),
+    (-1, +1, -1, +1, +1, +1, -1),
+    (-1, -1, +1, +1, -1, +1, +1),
+)
+
+
+def _circulant(first_row) -> np.ndarray:
+    r = np.asarray(first_row, dtype=np.int64)
+    p = r.size
+    idx = (np.arange(p)[None, :] - np.arange(p)[:, None]) % p   # C[i][j] = r[(j - i) mod p]
+    return r[idx]
+
+
+def williamson43_rows() -> list:
+    """First rows of the circulants A, B, C, D of order 43: +1 at index 0, and at every
+    k = 3^c * t (mod 43), t in the order-6 subgroup, the sign WILLIAMSON43[.][c]."""
+    p = 43
+    sub = [1, 6, 7, 36, 37, 42]
+    rows = []
+    for signs in WILLIAMSON43:
+        r = np.zeros(p, dtype=np.int64)
+        r[0] = 1
+        for c, sg in enumerate(signs):
+            for t in sub:
+                r[(pow(3, c, p) * t) % p] = sg
+        rows.append(r)
+    return rows
+
+
+def h172() -> np.ndarray:
+    """Order-172 Hadamard matrix as the Williamson array
+
+        [[ A,  B,  C,  D],
+         [-B,  A, -D,  C],
+         [-C,  D,  A, -B],
+         [-D, -C,  B,  A]]
+
+    of the symmetric circulants of williamson43_rows(), which commute and satisfy
+    A^2 + B^2 + C^2 + D^2 = 172 I43, so H H^T = 172 I.  Not symmetric: the inverse uses H^T."""
+    A, B, C, D = (_circulant(r) for r in williamson43_rows())
+    return np.block([[A, B, C, D],
+                     [-B, A, -D, C],
+                     [-C, D, A, -B],
+                     [-D, -C, B, A]])
+
+
+def factor_matrix(f: int) -> np.ndarray:
+    """The non-power-of-two Kronecker factor of order f (12 or 172)."""
+    if f == 12:
+        return h12()
+    if f == 172:
+        return h172()
+    raise ValueError(f"no factor of order {f}")
+
+
 def split_width(n: int):
-    """Return (f, m) with n = f * m, f in {1, 12}, m a power of two."""
+    """Return (f, m) with n = f * m, f in {1, 12, 172}, m a power of two."""
     if n >= 1 and n & (n - 1) == 0:
         return 1, n
-    if n % 12 == 0:
-        m = n // 12
-        if m & (m - 1) == 0:
-            return 12, m
-    raise ValueError(f"width {n} is neither 2^k nor 12 * 2^k")
+    for f in (12, 172):
+        if n % f == 0:
+            m = n // f
+            if m & (m - 1) == 0:
+                return f, m
+    raise ValueError(f"width {n} is none of 2^k, 12 * 2^k, 172 * 2^k")
 
 
 def hadamard(n: int) -> np.ndarray:
-    """Dense H_n: Sylvester for 2^k, H12 (x) H_m (Kronecker, H12 outer) for 12 * 2^k."""
+    """Dense H_n: Sylvester for 2^k, H_f (x) H_m (Kronecker, the order-f factor outer) for
+    f * 2^k, f = 12 or 172."""
     f, m = split_width(n)
-    return sylvester(m) if f == 1 else np.kron(h12(), sylvester(m))
+    return sylvester(m) if f == 1 else np.kron(factor_matrix(f), sylvester(m))
 
 
 # ---------------------------------------------------------------------------
@@ -174,8 +241,8 @@ def _signs(signs, n):
 def rotate(x, signs=None) -> np.ndarray:
     """y = H_n (s * x) / sqrt(n) for every row of x [T][n] (row form Y = X D H^T / sqrt(n)).
 
-    Power-of-two widths use the fast Walsh-Hadamard transform; n = 12 m applies
-    H_m along the contiguous index j2 and H12 across j1 (j = j1 * m + j2).
+    Power-of-two widths use the fast Walsh-Hadamard transform; n = f m (f = 12, 172)
+    applies H_m along the contiguous index j2 and H_f across j1 (j = j1 * m + j2).
     """
     x = _as_f64(x)
     n = x.shape[-1]
@@ -184,9 +251,9 @@ def rotate(x, signs=None) -> np.ndarray:
     if f == 1:
         y = fwht(u)
     else:
-        u = u.reshape(*u.shape[:-1], 12, m)
+        u = u.reshape(*u.shape[:-1], f, m)
         u = fwht(u)
-        y = np.einsum("ab,...bj->...aj", h12().astype(np.float64), u).reshape(x.shape)
+        y = np.einsum("ab,...bj->...aj", factor_matrix(f).astype(np.float64), u).reshape(x.shape)
     return y / np.sqrt(n)
 
 
@@ -227,8 +294,8 @@ def inverse_rotate(y, signs=None) -> np.ndarray:
     if f == 1:
         u = fwht(y)            # Sylvester H is symmetric
     else:
-        v = y.reshape(*y.shape[:-1], 12, m)
-        v = np.einsum("ba,...bj->...aj", h12().astype(np.float64), v)   # H12^T
+        v = y.reshape(*y.shape[:-1], f, m)
+        v = np.einsum("ba,...bj->...aj", factor_matrix(f).astype(np.float64), v)   # H_f^T
         u = fwht(v).reshape(y.shape)
     return u * _signs(signs, n) / np.sqrt(n)
 

@@ -43,6 +43,31 @@ def pin_orthogonality(O):
         _check(np.array_equal(H @ H.T, n * np.eye(n, dtype=np.int64)), f"H_{n} H^T != n I")
 
 
+def pin_h172_williamson(O):
+    """The order-172 factor: four symmetric, pairwise commuting +-1 circulants of order 43 whose
+    squares sum to 172 I, and the array built from them is Hadamard (H H^T = 172 I)."""
+    rows = O.williamson43_rows()
+    mats = []
+    for r in rows:
+        r = np.asarray(r, dtype=np.int64)
+        _check(r.shape == (43,) and set(np.unique(r)) <= {-1, 1} and r[0] == 1, "circulant first row")
+        _check(np.array_equal(r[1:], r[1:][::-1]), "circulant must be symmetric (r[k] = r[43 - k])")
+        mats.append(scipy.linalg.circulant(r).T)   # scipy's circulant has r as its first column
+    S = sum(m @ m for m in mats)
+    _check(np.array_equal(S, 172 * np.eye(43, dtype=np.int64)), "A^2 + B^2 + C^2 + D^2 != 172 I")
+    for i in range(4):
+        for j in range(4):
+            _check(np.array_equal(mats[i] @ mats[j], mats[j] @ mats[i]), "circulants must commute")
+    H = O.h172()
+    _check(H.shape == (172, 172) and set(np.unique(H)) == {-1, 1}, "H172 entries must be +-1")
+    _check(np.array_equal(H @ H.T, 172 * np.eye(172, dtype=np.int64)), "H172 H172^T != 172 I")
+    # the first block row is [A B C D]
+    _check(np.array_equal(H[:43, :43], mats[0]) and np.array_equal(H[:43, 129:], mats[3]), "block row 0")
+    for n in [172, 344, 688]:
+        Hn = O.hadamard(n)
+        _check(np.array_equal(Hn @ Hn.T, n * np.eye(n, dtype=np.int64)), f"H_{n} H^T != n I")
+
+
 def pin_fwht_equals_dense(O):
     rng = np.random.default_rng(11)
     for n in [1, 2, 4, 8, 16, 32, 64, 128, 256, 1024, 4096]:
@@ -58,6 +83,14 @@ def pin_fwht_equals_dense(O):
         dense = (v * s) @ O.hadamard(n).T.astype(np.float64)
         _check(np.allclose(fast, dense, rtol=0, atol=1e-9 * np.abs(dense).max()),
                f"fast 12x rotation != dense at n={n}")
+    for m in [1, 2, 16]:
+        n = 172 * m
+        v = rng.integers(-1000, 1000, size=(2, n)).astype(np.float64)
+        s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+        fast = O.rotate(v, s) * math.sqrt(n)
+        dense = (v * s) @ O.hadamard(n).T.astype(np.float64)
+        _check(np.allclose(fast, dense, rtol=0, atol=1e-9 * np.abs(dense).max()),
+               f"fast 172x rotation != dense at n={n}")
 
 
 def pin_rotate_matches_scipy_definition(O):
@@ -71,7 +104,7 @@ def pin_rotate_matches_scipy_definition(O):
 
 def pin_parseval_and_roundtrip(O):
     rng = np.random.default_rng(13)
-    for n in [16, 128, 4096, 12288, 3072]:
+    for n in [16, 128, 4096, 12288, 3072, 11008, 2752]:
         x = rng.standard_normal((3, n)) * np.exp(rng.standard_normal(n))
         s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
         y = O.rotate(x, s)
@@ -90,14 +123,14 @@ def _signed_row(O, n, k, s):
         pc = np.array([bin(int(t)).count("1") for t in a])
         row = np.where(pc & 1, -1.0, 1.0)
     else:
-        row = np.kron(O.h12()[k // m].astype(np.float64), _signed_row(O, m, k % m, np.ones(m)))
+        row = np.kron(O.factor_matrix(f)[k // m].astype(np.float64), _signed_row(O, m, k % m, np.ones(m)))
     return row * s
 
 
 def pin_e3_closed_form(O):
     """x = s * H_n[k] rotates to sqrt(n) e_k; its quantisation is fully determined."""
     rng = np.random.default_rng(14)
-    for n, k in [(16, 5), (128, 77), (4096, 1234), (12288, 7000), (3072, 2049)]:
+    for n, k in [(16, 5), (128, 77), (4096, 1234), (12288, 7000), (3072, 2049), (11008, 9000)]:
         s = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
         x = _signed_row(O, n, k, s)[None, :]
         y = O.rotate(x, s)
@@ -330,7 +363,7 @@ def pin_blocked_rotation(O):
 
 
 ALL_PINS = [
-    pin_sylvester_matches_scipy, pin_orthogonality, pin_fwht_equals_dense,
+    pin_sylvester_matches_scipy, pin_orthogonality, pin_h172_williamson, pin_fwht_equals_dense,
     pin_rotate_matches_scipy_definition, pin_parseval_and_roundtrip, pin_e3_closed_form,
     pin_e1_worked_example, pin_e2_worked_example, pin_int4_rounding, pin_fp16_storage,
     pin_e2m1, pin_e4m3, pin_nvfp4_invariants, pin_mxfp4_closed_form, pin_mxfp4_worked_block,

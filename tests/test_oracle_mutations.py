@@ -48,9 +48,39 @@ def _h12_transposed_in_rotate(O):
         f, m = O.split_width(n)
         if f == 1:
             return O.fwht(u) / np.sqrt(n)
-        u = O.fwht(u.reshape(*u.shape[:-1], 12, m))
-        return np.einsum("ba,...bj->...aj", O.h12().astype(np.float64), u).reshape(x.shape) / np.sqrt(n)
+        u = O.fwht(u.reshape(*u.shape[:-1], f, m))
+        return np.einsum("ba,...bj->...aj", O.factor_matrix(f).astype(np.float64), u).reshape(x.shape) / np.sqrt(n)
     O.rotate = rot
+
+
+def _h172_transposed_in_rotate(O):
+    """rotate() applies H172^T for 172 * 2^k widths only; H12 stays right."""
+    orig = O.rotate
+
+    def rot(x, signs=None):
+        x = O._as_f64(x)
+        n = x.shape[-1]
+        f, m = O.split_width(n)
+        if f != 172:
+            return orig(x, signs)
+        u = O.fwht((x * O._signs(signs, n)).reshape(*x.shape[:-1], f, m))
+        return np.einsum("ba,...bj->...aj", O.h172().astype(np.float64), u).reshape(x.shape) / np.sqrt(n)
+    O.rotate = rot
+
+
+def _h172_coset_sign(O):
+    """one coset sign of one order-43 circulant flipped"""
+    w = [list(r) for r in O.WILLIAMSON43]
+    w[2][3] *= -1
+    O.WILLIAMSON43 = tuple(tuple(r) for r in w)
+
+
+def _h172_array_sign(O):
+    """the Williamson array with one block sign wrong (-D and D swapped in block row 1)"""
+    def bad():
+        A, B, C, D = (O._circulant(r) for r in O.williamson43_rows())
+        return np.block([[A, B, C, D], [-B, A, D, -C], [-C, D, A, -B], [-D, -C, B, A]])
+    O.h172 = bad
 
 
 def _h12_typo(O):
@@ -180,7 +210,8 @@ def _blocked_signs_tiled(O):
 MUTATIONS = [_no_norm, _signs_after, _h12_transposed_in_rotate, _h12_typo, _round_half_away,
              _swap_nibbles, _scale_over_8, _fp16_truncation, _nvfp4_wrong_constant,
              _e2m1_ties_up, _e4m3_truncate, _fwht_skip_stage, _inverse_without_transpose,
-             _mxfp4_emax_one, _mxfp4_ceil, _mxfp4_bias_128, _blocked_norm_sqrt_n, _blocked_signs_tiled]
+             _mxfp4_emax_one, _mxfp4_ceil, _mxfp4_bias_128, _blocked_norm_sqrt_n, _blocked_signs_tiled,
+             _h172_transposed_in_rotate, _h172_coset_sign, _h172_array_sign]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
