@@ -9,6 +9,8 @@
  *                              fast algorithm; combined with grouped quantisation.
  *      review 2, Summary ..... the random Hadamard transform is invertible up to
  *                              machine precision; activations are quantised to INT4.
+ *      review 2, Questions ... widths with a large non-power-of-two part, 172 for
+ *                              Llama 2 7B (11008 = 172 x 64), are costly.
  *      review 3, Strengths ... the online Hadamard is applied to activations and to
  *                              the KV cache.
  *      review 3, Questions ... the Hadamard block computes Y = X H^T.
@@ -28,7 +30,12 @@
  * H_n is the Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i&j)) for
  * n = 2^k, and H12 (x) H_m with index j = j1*m + j2 for n = 12*m, where H12 is
  * the Williamson array [[A,B,B,B],[-B,A,-B,B],[-B,B,A,-B],[-B,-B,B,A]] with
- * A = J3 (all ones) and B = J3 - 2*I3.  s is a +-1 vector shared by all rows.
+ * A = J3 (all ones) and B = J3 - 2*I3.  For n = 172*m it is H172 (x) H_m, H172
+ * the array [[A,B,C,D],[-B,A,-D,C],[-C,D,A,-B],[-D,-C,B,A]] of the symmetric
+ * order-43 circulants whose first rows are +1 at 0 and, at k != 0, -1 exactly when
+ * k lies in the listed cosets of the subgroup {1,6,7,36,37,42} of the units mod 43
+ * (coset c = 3^c * subgroup): A {4,5,6}, B {0,3,4,6}, C {0,2,6}, D {0,1,4}.
+ * s is a +-1 vector shared by all rows.
  *
  * Conventions shared by every call:
  *  - Every data pointer is a DEVICE pointer owned by the caller; the library
@@ -41,8 +48,9 @@
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.
  *  - Alignment: x, y_out, packed_out, x_out and signs must be 16-byte aligned;
  *    scale buffers aligned to their element size.
- *  - Supported widths: n = 2^k with 16 <= n <= 16384, and n = 12 * 2^k with
- *    256 <= 2^k <= 2048 (3072, 6144, 12288, 24576).
+ *  - Supported widths: n = 2^k with 16 <= n <= 16384, n = 12 * 2^k with
+ *    256 <= 2^k <= 2048 (3072, 6144, 12288, 24576), and n = 172 * 2^k with
+ *    16 <= 2^k <= 128 (2752, 5504, 11008, 22016).
  *  - signs: device int8 [n] with values +1 / -1, or NULL for all +1 (plain
  *    Hadamard).  Other values are undefined behaviour.
  */
@@ -159,8 +167,8 @@ int rhtq_inverse(const uint8_t* packed, const void* scales, const float* tensor_
  *     y = (I_{n/b} (x) H_b) diag(s) x / sqrt(b)
  *
  *   block   a power of two, 16 <= block < n, dividing n; the row width n itself may then be any
- *           multiple of block up to 2^20 (for example 11008 = 86 x 128, the Llama-2-7B
- *           intermediate width, which has no Hadamard matrix of its own in this library).
+ *           multiple of block up to 2^20 (for example 11008 = 86 x 128, the Llama 2 7B
+ *           intermediate width, rotated per 128-block instead of by H172 (x) H64).
  *           block == n is the plain call (n a supported width).
  *   group   quantisation groups lie inside a block: INT4 a power of two >= 16 dividing block
  *           (group 0, one group per row, only when block == n); NVFP4 16; MXFP4 32

@@ -11,10 +11,15 @@ namespace {
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-// n = 2^k (16..16384) or 12 * 2^k (2^k in 256..2048): the power-of-two widths and
-// the 12 x 2^k widths (KronQ issue #2, Model Details: 12288 = 12 x 1024).
+// n = 2^k (16..16384), 12 * 2^k (2^k in 256..2048) or 172 * 2^k (2^k in 16..128): the
+// power-of-two widths, the 12 x 2^k widths (KronQ issue #2, Model Details: 12288 = 12 x 1024)
+// and the 172 x 2^k widths (QuaRot reviews, review 2 Questions: 11008 = 172 x 64, Llama 2 7B).
 bool width_ok(int32_t n) {
   if (is_pow2(n)) return n >= 16 && n <= 16384;
+  if (n % 172 == 0) {
+    const int32_t m = n / 172;
+    return is_pow2(m) && m >= 16 && m <= 128;
+  }
   if (n % 12 == 0) {
     const int32_t m = n / 12;
     return is_pow2(m) && m >= 256 && m <= 2048;

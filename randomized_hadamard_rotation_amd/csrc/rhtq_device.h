@@ -89,6 +89,47 @@ __host__ __device__ constexpr int h12_entry(int r, int c) {
   return bsign * e;
 }
 
+// Order-172 factor (QuaRot reviews, review 2 Questions: 172 is the non-power-of-two part of
+// the Llama 2 7B width): the same Williamson array with four symmetric circulants A, B, C, D
+// of order 43 in place of A, B, B, B, so block (bi, bj) holds circulant bi ^ bj, negated
+// under the same mask 0x3950.  Circulant t has entry (r, c) = f_t((c - r) mod 43) with
+// f_t(0) = +1 and, for k != 0, f_t(k) = -1 exactly when the coset of k modulo the order-6
+// subgroup {1, 6, 7, 36, 37, 42} of the units mod 43 is in the mask kNeg43[t]; coset
+// index = (discrete log of k to base 3) mod 7.  Then A^2 + B^2 + C^2 + D^2 = 172 I.
+constexpr uint32_t kNeg43[4] = {0x70u, 0x59u, 0x45u, 0x13u};
+
+// Coset index of every k in 1..42 ((discrete log of k to base 3) mod 7); entry 0 unused.
+struct Coset43 {
+  int8_t c[43];
+  constexpr Coset43() : c() {
+    int p = 1;
+    for (int e = 0; e < 42; ++e) {
+      c[p] = (int8_t)(e % 7);
+      p = (p * 3) % 43;
+    }
+  }
+};
+constexpr Coset43 kCoset43{};
+
+__host__ __device__ constexpr int h172_entry(int r, int c) {
+  const int bi = r / 43, bj = c / 43;
+  const int bsign = ((0x3950 >> (4 * bi + bj)) & 1) ? -1 : 1;
+  const int k = ((c % 43) - (r % 43) + 43) % 43;
+  const int e = (k == 0) ? 1 : (((kNeg43[bi ^ bj] >> kCoset43.c[k]) & 1) ? -1 : 1);
+  return bsign * e;
+}
+
+// Bit j of word w[i][j >> 5] is set when H172[i][j] = -1 (T: of H172^T).
+template <bool T>
+struct H172Bits {
+  uint32_t w[172][6];
+  constexpr H172Bits() : w() {
+    for (int i = 0; i < 172; ++i)
+      for (int j = 0; j < 172; ++j)
+        if ((T ? h172_entry(j, i) : h172_entry(i, j)) < 0) w[i][j >> 5] |= 1u << (j & 31);
+  }
+};
+
 // w <- H12 w using the array's structure: with v1..v4 the four 3-blocks, sk = sum(vk),
 // A v = sk * 1 and B v = sk * 1 - 2 v, so block k of the result is
 // T_k * 1 + 2 (+-vi +-vj +-vl) with T_k = +-s1 +-s2 +-s3 +-s4 (52 adds/FMAs per 12 values).

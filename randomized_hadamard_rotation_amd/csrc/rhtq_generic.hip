@@ -4,7 +4,8 @@
 // one row for wider rows) into LDS as fp32, runs the Walsh-Hadamard butterflies
 // three index bits per pass (QuaRot reviews, review 1 Summary: the online Hadamard
 // uses the Walsh-Hadamard fast algorithm), the order-12 factor for n = 12*m
-// (KronQ issue #2, Model Details: 12288 = 12 x 1024), then the epilogue.  The
+// (KronQ issue #2, Model Details: 12288 = 12 x 1024) or the order-172 factor for
+// n = 172*m (QuaRot reviews, review 2 Questions: Llama 2 7B), then the epilogue.  The
 // register-resident kernels in rhtq_fast.hip cover the bf16 hot shapes; this one
 // is the complete fallback and the path for fp32 input and for the inverse.
 #include <hip/hip_fp16.h>
@@ -18,6 +19,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileTarget = 4096;
+
+// Sign bits of H172 and of its transpose, for the dense order-172 contraction.
+__constant__ H172Bits<false> kH172;
+__constant__ H172Bits<true> kH172T;
 
 __host__ __device__ constexpr int lds_idx(int j) { return j + (j >> 5); }
 
@@ -146,6 +151,53 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(KernelArgs a) {
       if (LOGM - b >= 3) fwht_pass<3, TE>(lds, b);
       else if (LOGM - b == 2) fwht_pass<2, TE>(lds, b);
       else fwht_pass<1, TE>(lds, b);
+      __syncthreads();
+    }
+    if constexpr (F == 172) {
+      // dense order-172 contraction across j1 for every (row, j2): work item = (row, j2, four
+      // consecutive outputs); all reads finish before the barrier, results are held in registers
+      constexpr int ITEMS = R * M * 43;
+      constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+      const H172Bits<OP == OP_INVERSE>& hb = [] () -> const H172Bits<OP == OP_INVERSE>& {
+        if constexpr (OP == OP_INVERSE) return kH172T; else return kH172;
+      }();
+      float res[PER][4];
+#pragma unroll
+      for (int t = 0; t < PER; ++t) {
+        const int w = tid + t * kThreads;
+        if (w < ITEMS) {
+          const int iq = (w / M) % 43, j2 = w % M, r = w / (M * 43);
+          const int base = r * N + j2;
+          // fp64 sums: a 172-term fp32 chain would lose up to 172 ulps of its partial sums
+          double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+          for (int jw = 0; jw < 6; ++jw) {
+            uint32_t bits[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bits[q] = hb.w[4 * iq + q][jw];
+            const int jn = jw < 5 ? 32 : 172 - 160;
+#pragma unroll 4
+            for (int jj = 0; jj < jn; ++jj) {
+              const int j = 32 * jw + jj;
+              const uint32_t v = __float_as_uint(lds[lds_idx(base + j * M)]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[q] += (double)__uint_as_float(v ^ (((bits[q] >> jj) & 1u) << 31));
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) res[t][q] = (float)acc[q];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < PER; ++t) {
+        const int w = tid + t * kThreads;
+        if (w < ITEMS) {
+          const int iq = (w / M) % 43, j2 = w % M, r = w / (M * 43);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) lds[lds_idx(r * N + (4 * iq + q) * M + j2)] = res[t][q];
+        }
+      }
       __syncthreads();
     }
     if constexpr (F == 12) {
@@ -331,6 +383,10 @@ hipError_t dispatch_width(const KernelArgs& a, hipStream_t s) {
     case 6144: return launch_one<IN, 12, 9, OP>(a, s);
     case 12288: return launch_one<IN, 12, 10, OP>(a, s);
     case 24576: return launch_one<IN, 12, 11, OP>(a, s);
+    case 2752: return launch_one<IN, 172, 4, OP>(a, s);
+    case 5504: return launch_one<IN, 172, 5, OP>(a, s);
+    case 11008: return launch_one<IN, 172, 6, OP>(a, s);
+    case 22016: return launch_one<IN, 172, 7, OP>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

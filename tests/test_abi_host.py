@@ -45,7 +45,14 @@ def test_supported_matrix(R):
         assert R.rhtq_supported(1 << k, "mxfp4", 32) == (k >= 5)
     for m in (256, 512, 1024, 2048):
         assert R.rhtq_supported(12 * m, "int4", 128)
-    for bad in (0, 8, 32768, 100, 12 * 128, 12 * 4096, 11008):
+    for m in (16, 32, 64, 128):
+        assert R.rhtq_supported(172 * m, "int4", 0)
+        assert R.rhtq_supported(172 * m, "int4", 16)
+        assert R.rhtq_supported(172 * m, "nvfp4", 16)
+        assert R.rhtq_supported(172 * m, "mxfp4", 32)
+    assert R.rhtq_supported(11008, "int4", 128) and R.rhtq_supported(11008, "int4", 256)
+    assert not R.rhtq_supported(11008, "int4", 512)    # 11008 = 21.5 x 512
+    for bad in (0, 8, 32768, 100, 12 * 128, 12 * 4096, 172, 172 * 8, 172 * 256, 11000, 10752):
         assert not R.rhtq_supported(bad, "int4", 0)
     assert not R.rhtq_supported(4096, "int4", 96)      # not a power of two
     assert not R.rhtq_supported(4096, "int4", 8)       # below 16

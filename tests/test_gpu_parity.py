@@ -114,7 +114,7 @@ def test_e2_exact_example(R):
 
 
 @pytest.mark.parametrize("n,k", [(16, 3), (128, 77), (4096, 1234), (12288, 7000), (3072, 2049),
-                                 (16384, 9999), (24576, 123)])
+                                 (16384, 9999), (24576, 123), (11008, 9000), (2752, 43), (22016, 21999)])
 def test_e3_closed_form(R, n, k):
     say(f"E3 n={n} k={k}")
     import torch
@@ -152,7 +152,7 @@ def test_e3_closed_form(R, n, k):
 
 REDUCED = [("tiny_128_int4", 64), ("llama_4096_int4", 203), ("downproj_12288_int4g128", 37),
            ("kv_128_int4g128", 4099), ("nvfp4_4096", 131), ("mxfp4_4096", 131),
-           ("blockh128_4096_int4g128", 131)]
+           ("blockh128_4096_int4g128", 131), ("downproj7b_11008_int4g128", 37)]
 
 
 @pytest.mark.parametrize("name,tokens", REDUCED)
@@ -165,7 +165,8 @@ def test_workload_reduced(R, name, tokens):
 
 
 @pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
-                                  "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128"])
+                                  "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128",
+                                  "downproj7b_11008_int4g128"])
 def test_workload_full_size_sampled(R, name):
     """Full-size input on the device in the same launch shape as the benchmark;
     the oracle checks sampled rows (first, last, every sink row it can find, random)."""
@@ -201,7 +202,8 @@ def test_workload_full_size_sampled(R, name):
 # sweeps: every width, several token counts, signs on / off, fp32 input
 # ----------------------------------------------------------------------------
 
-WIDTHS = [16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 3072, 6144, 12288, 24576]
+WIDTHS = [16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 3072, 6144, 12288, 24576,
+          2752, 5504, 11008, 22016]
 
 
 @pytest.mark.parametrize("n", WIDTHS)
@@ -228,7 +230,7 @@ def test_quantise_every_width(R, n):
     for dt in (torch.bfloat16, torch.float32):
         x = xc.to(dt).to(dev())
         y_ref = O.rotate(x.cpu(), s)
-        groups = [0, 16, 128] if n >= 128 else [0, 16]
+        groups = [0, 16, 128] if n % 128 == 0 else [0, 16]
         for group in groups:
             for sd in ("f32", "f16"):
                 say(f"int4 n={n} group={group} scale={sd} dtype={dt}")
@@ -297,7 +299,7 @@ def test_deterministic(R):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
-                                  "nvfp4_4096", "mxfp4_4096"])
+                                  "nvfp4_4096", "mxfp4_4096", "downproj7b_11008_int4g128"])
 def test_inverse_round_trip(R, name):
     import torch
     w = WORKLOADS[name]

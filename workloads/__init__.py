@@ -93,6 +93,11 @@ WORKLOADS = {
         "blockh128_4096_int4g128", 16384, 4096, "bf16", "llama_like", 7, 0, "int4", 128, "f16",
         description="16384 x 4096 bf16, llama-like recipe; block-diagonal H128 with full-length signs, "
                     "INT4 group 128, fp16 scales", block=128),
+    # the Llama 2 7B down_proj input: intermediate width 11008 = 172 x 64 (QuaRot reviews, review 2
+    # Questions name its non-power-of-two factor 172)
+    "downproj7b_11008_int4g128": Workload(
+        "downproj7b_11008_int4g128", 8192, 11008, "bf16", "llama_like", 8, 0, "int4", 128, "f16",
+        description="8192 x 11008 bf16 (H172 x H64), llama-like recipe; INT4 group 128, fp16 scales"),
     # MXFP4 on the NVFP4 shape: the thread compares the two FP4 formats on the same model
     "mxfp4_4096": Workload(
         "mxfp4_4096", 16384, 4096, "bf16", "llama_like", 6, 0, "mxfp4", 32, "e8m0",
