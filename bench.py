@@ -31,10 +31,12 @@ METRIC = "RHT+4-bit quant tokens/s & HBM GB/s (% of peak) at d=4096 and d=12288"
 HBM_PEAK_GBS = 8000.0
 CACHE_DEFEAT_BYTES = 512 << 20
 HEADLINE = "llama_4096_int4"
-OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128"]
+OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128",
+          "downproj7b_11008_int4g128"]
 KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast2.hip",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_fast172.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_epilogue.h",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_inverse_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_device.h",

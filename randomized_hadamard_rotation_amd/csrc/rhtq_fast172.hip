@@ -1,0 +1,384 @@
+// Matrix-core kernel for bf16 rows of 11008 = 172 x 64 elements, the Llama 2 7B intermediate
+// width (QuaRot reviews, review 2 Questions: its non-power-of-two part 172 makes the rotation
+// costly).  Element j = 64 a + b (a < 172, b < 64) and
+//
+//     Y[a'][b''] = sum_a sum_b H172[a'][a] H64[b''][b] s[a][b] x[a][b] / sqrt(11008).
+//
+// The order-172 factor has no fast algorithm, so it is a dense contraction and runs on the
+// matrix cores.  One workgroup of four waves owns one row at a time (persistent grid):
+//
+//  1. The row (172 x 128 bytes) arrives by 16-byte loads issued one row ahead; the random
+//     signs are XORed onto the bf16 sign bits (masks in LDS) and the row is written to LDS
+//     as 172 rows a of 64 bf16, row pitch 160 bytes; rows 172..191 are zero.
+//  2. Stage 1, H172 over a, exact on the bf16 input: v_mfma_f32_16x16x32_bf16 with
+//     A = X^T (M = b, K = a), read from LDS two bytes per lane and slot, and B = H172^T
+//     (K = a, N = a'), a +-1 operand held in registers.  K slot e of lane group g stands for
+//     a = 32 ks + g + 4 e, so the four lane groups of one read hit disjoint LDS banks.  Wave w
+//     owns the output tiles a' in [16 t, 16 t + 16), t = w, w + 4, w + 8 (11 tiles, 172
+//     padded to 176).  Result D1[b][a']: lane l holds a' = 16 t + (l & 15) and
+//     b = 16 mt + 4 (l >> 4) + i in tile mt, register i.
+//  3. Stage 2, H64 = H2 (x) H32 over b: index bit 5 (mt >> 1) is a register butterfly, the
+//     other five bits one v_mfma_f32_16x16x32_f16 with A = H32 (M = b''_lo, K = b_lo) and
+//     B = the butterflied values, whose registers already are that B layout (slot e of lane
+//     group g is b_lo = 16 (e >> 2) + 4 g + (e & 3)).  fp32 does not fit an f16 operand, so
+//     each value u is split as u S = hi + lo (two f16 terms, S a power of two per output
+//     column a' with |u S| < 2^15) and both halves accumulate through the same operand:
+//     22 significant bits.
+//  4. Output D2[b''][a']: lane l holds a' = 16 t + (l & 15) and, in run r = 2 hb + mt2,
+//     b'' = 16 r + 4 (l >> 4) + i.  Groups of 16 and 32 are runs, groups of 64..256 are
+//     1..4 consecutive a' (lane bits 0-1); maxima by lane swaps and DPP.  INT4 codes by the
+//     magic-constant FMA, E2M1 by v_cvt_scalef32_pk_fp4_f32; lane groups g and g ^ 1 trade
+//     runs so that each lane stores eight consecutive codes as one dword.
+#include <hip/hip_fp16.h>
+
+#include "rhtq.h"
+#include "rhtq_device.h"
+#include "rhtq_internal.h"
+
+namespace rhtq {
+namespace {
+
+constexpr int kW = 4;
+constexpr int kT = 64 * kW;
+constexpr int kN = 11008;                        // 172 x 64
+constexpr int kPitch = 160;                      // LDS bytes per a-row (128 data + 32 pad)
+constexpr int kXRows = 192;                      // six K-steps of 32
+constexpr int kChunks = kN / 8;                  // 16-byte chunks per row
+constexpr int kLoads = (kChunks + kT - 1) / kT;  // loads per thread and row
+
+__constant__ H172Bits<false> kH172Rows;
+
+// Stage-1 B operand for output tile t and K-step ks: slot e of lane group g stands for
+// a = 32 ks + g + 4 e, column n = lane & 15 for a' = 16 t + n; H172[a'][a] as bf16 +-1,
+// zero outside 172 x 172.
+__device__ bf16x8 h172t_operand(int lane, int t, int ks) {
+  const int ap = 16 * t + (lane & 15), g = lane >> 4;
+  uint16_t bits[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = 32 * ks + g + 4 * e;
+    uint16_t v = 0;
+    if (k < 172 && ap < 172) v = ((kH172Rows.w[ap][k >> 5] >> (k & 31)) & 1u) ? 0xBF80 : 0x3F80;
+    bits[e] = v;
+  }
+  bf16x8 r;
+  __builtin_memcpy(&r, bits, 16);
+  return r;
+}
+
+// Stage-2 A operand for M-tile mt2: row m = lane & 15 stands for b''_lo = 16 mt2 + m, slot e
+// of lane group g for b_lo = 16 (e >> 2) + 4 g + (e & 3); entry H32[b''_lo][b_lo] as f16.
+__device__ f16x8 h32_b_operand(int lane, int mt2) {
+  const int m = 16 * mt2 + (lane & 15), g = lane >> 4;
+  uint16_t bits[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = 16 * (e >> 2) + 4 * g + (e & 3);
+    bits[e] = (__builtin_popcount(m & k) & 1) ? 0xBC00 : 0x3C00;
+  }
+  f16x8 r;
+  __builtin_memcpy(&r, bits, 16);
+  return r;
+}
+
+// Maximum over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) of non-negative values.
+__device__ __forceinline__ float col_max(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = umax(p[0], p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(umax(q[0], q[1]));
+}
+
+template <int OP, int NT>
+__device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const float cnorm = (float)(1.0 / __builtin_sqrt((double)kN));
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+
+  bf16x8 hb[NT][6];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand(lane, wave + 4 * j, ks);
+  const f16x8 ha[2] = {h32_b_operand(lane, 0), h32_b_operand(lane, 1)};
+
+  float gts = 0.0f, inv6g = 0.0f;
+  if constexpr (OP == OP_NVFP4) {
+    gts = a.tensor_scale[0];
+    inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
+  }
+  int LG = 0;   // log2 of the group
+  if constexpr (OP == OP_INT4) LG = __builtin_ctz((unsigned)a.group);
+  if constexpr (OP == OP_NVFP4) LG = 4;
+  if constexpr (OP == OP_MXFP4) LG = 5;
+  float run_max = 0.0f;
+
+  uint4 raw[kLoads];
+  auto load = [&](int64_t row) {
+    if (row >= a.rows) return;
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int c = tid + kT * k;
+      if (c < kChunks) raw[k] = ld_stream(x + row * kN + 8 * c);
+    }
+  };
+  int64_t row = blockIdx.x;
+  load(row);
+
+  const uint8_t* xb = xs + g * kPitch + 2 * n;   // this lane's column b = n of the a-row g
+  for (; row < a.rows; row += gridDim.x) {
+    __syncthreads();   // the previous row's LDS reads are done
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int c = tid + kT * k;
+      if (c < kChunks) {
+        const uint4 m = sgn[c];
+        uint4 r = raw[k];
+        r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
+        *reinterpret_cast<uint4*>(xs + (c >> 3) * kPitch + 16 * (c & 7)) = r;
+      }
+    }
+    load(row + gridDim.x);   // the next row's loads run during this row's work
+    __syncthreads();
+
+    // ---------------- stage 1: H172 over a ----------------
+    f32x4 acc[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[j][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks) {
+      bf16x8 av[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint8_t* p = xb + 32 * ks * kPitch + 32 * mt;
+        uint16_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const uint16_t*>(p + 4 * e * kPitch);
+        __builtin_memcpy(&av[mt], v, 16);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], hb[j][ks], acc[j][mt], 0, 0, 0);
+    }
+
+    const int64_t rbase = row * kN;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int ap = 16 * (wave + 4 * j) + n;
+      const bool valid = ap < 172;
+      // ---------------- stage 2: H2 by butterfly, H32 on the matrix cores ----------------
+      float u[2][2][4];   // [hb][mt & 1][i], b_lo = 16 (mt & 1) + 4 g + i
+      float m = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = acc[j][h][i], q = acc[j][h + 2][i];
+          u[0][h][i] = p + q;
+          u[1][h][i] = p - q;
+          m = fmaxf(m, fmaxf(fabsf(p + q), fabsf(p - q)));
+        }
+      float S, invS;
+      split_scale(__float_as_uint(col_max(m)), S, invS);
+      float d2[4][4];   // [run r = 2 hb + mt2][i]: b'' = 16 r + 4 g + i
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float ys[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ys[e] = u[h][e >> 2][e & 3];
+        uint32_t hw[4], lw[4];
+        split8(ys, S, hw, lw);
+        f16x8 bh, bl;
+        __builtin_memcpy(&bh, hw, 16);
+        __builtin_memcpy(&bl, lw, 16);
+#pragma unroll
+        for (int mt2 = 0; mt2 < 2; ++mt2) {
+          const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+          f32x4 o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[mt2], bh, z, 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[mt2], bl, o, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d2[2 * h + mt2][i] = o[i];
+        }
+      }
+
+      const int64_t ebase = rbase + 64 * ap + 4 * g;   // element of run 0, i = 0
+      if constexpr (OP == OP_ROTATE) {
+        if (valid) {
+          const float f = invS * cnorm;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st_stream(a.y + ebase + 16 * r, d2[r][0] * f, d2[r][1] * f, d2[r][2] * f, d2[r][3] * f);
+        }
+        continue;
+      }
+      float mr[4];   // run maxima, split units
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        mr[r] = fmaxf(fmaxf(fabsf(d2[r][0]), fabsf(d2[r][1])), fmaxf(fabsf(d2[r][2]), fabsf(d2[r][3])));
+      if constexpr (OP == OP_AMAX) {
+        run_max = fmaxf(run_max, fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3])) * invS);
+        continue;
+      }
+
+      // ---------------- group scales ----------------
+      float gm[4];   // group maximum (true units, before 1/sqrt(n)) of the group holding run r
+      if (LG == 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gm[r] = col_max(mr[r]) * invS;
+      } else if (LG == 5) {
+        const float m0 = col_max(fmaxf(mr[0], mr[1])) * invS, m1 = col_max(fmaxf(mr[2], mr[3])) * invS;
+        gm[0] = gm[1] = m0;
+        gm[2] = gm[3] = m1;
+      } else {
+        float mm = col_max(fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3]))) * invS;
+        if (LG >= 7) mm = dpp_max<0xB1>(mm);   // a' pairs (lane xor 1)
+        if (LG >= 8) mm = dpp_max<0x4E>(mm);   // a' quads (lane xor 2)
+        gm[0] = gm[1] = gm[2] = gm[3] = mm;
+      }
+      // the group of run r, and whether this lane stores its scale: for LG 4 / 5 lane group g
+      // stores group g of the a'-row, for LG >= 6 lane group 0 of the first a' of the group
+      float sl[4];
+      bool clamp = false;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t gi = (rbase + 64 * ap + 16 * r) >> LG;
+        const bool writer = valid && (LG == 4 ? g == r : LG == 5 ? (g == (r >> 1) && (r & 1) == 0)
+                                                                  : (g == 0 && r == 0 && (ap & ((1 << (LG - 6)) - 1)) == 0));
+        const float bm = gm[r];
+        if constexpr (OP == OP_INT4) {
+          const Int4Scale sc = int4_scale(bm, cnorm, a.scale_dtype);
+          sl[r] = sc.inv * invS;
+          clamp |= sc.clamp;
+          if (writer) {
+            if (a.scale_dtype == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[gi] = sc.s;
+            else static_cast<__half*>(a.scales)[gi] = __float2half_rn(fminf(sc.s, 65504.0f));
+          }
+        } else if constexpr (OP == OP_NVFP4) {
+          const uint32_t code = e4m3_code((bm * cnorm) * inv6g);
+          const float seff = e4m3_value(code) * gts;
+          sl[r] = seff > 0.0f ? (cnorm * __builtin_amdgcn_rcpf(seff)) * invS : 0.0f;
+          if (writer) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)code;
+        } else {
+          const float bt = bm * cnorm;
+          const int ex = mx_exponent(bt);
+          sl[r] = bt > 0.0f ? __builtin_ldexpf(invS * cnorm, -ex) : 0.0f;
+          if (writer) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)(ex + 127);
+        }
+      }
+
+      // ---------------- codes: runs 0,1 -> p01, runs 2,3 -> p23 (run in 16-bit halves) ----------------
+      uint32_t p01, p23;
+      if constexpr (OP == OP_INT4) {
+        const bool any_clamp = __builtin_amdgcn_ballot_w64(clamp) != 0;
+        uint32_t q[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            q[r][i] = any_clamp ? __float_as_uint(__builtin_amdgcn_fmed3f(d2[r][i] * sl[r], -8.0f, 7.0f) + 12582912.0f)
+                                : __float_as_uint(__builtin_fmaf(d2[r][i], sl[r], 12582912.0f));
+        const uint32_t q01[8] = {q[0][0], q[0][1], q[0][2], q[0][3], q[1][0], q[1][1], q[1][2], q[1][3]};
+        const uint32_t q23[8] = {q[2][0], q[2][1], q[2][2], q[2][3], q[3][0], q[3][1], q[3][2], q[3][3]};
+        p01 = pack8_nibbles(q01);
+        p23 = pack8_nibbles(q23);
+      } else {
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr) {
+            const int r = 2 * h + rr;
+            const float s = sl[r];
+            uint32_t t = 0;
+            t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, d2[r][0] * s, d2[r][1] * s, 1.0f, 0);
+            t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, d2[r][2] * s, d2[r][3] * s, 1.0f, 1);
+            w[h] |= (s > 0.0f ? (t & 0xFFFFu) : 0u) << (16 * rr);   // zero-scale group -> code 0
+          }
+        }
+        p01 = w[0];
+        p23 = w[1];
+      }
+      // lane group g keeps runs g & 1 and 2 + (g & 1), sends the other two to g ^ 1 and
+      // receives the partner's halves of its own runs: eight consecutive codes per dword
+      const bool odd = g & 1;
+      const uint32_t send = __builtin_amdgcn_perm(p23, p01, odd ? 0x05040100u : 0x07060302u);
+      const uint32_t keep = __builtin_amdgcn_perm(p23, p01, odd ? 0x07060302u : 0x05040100u);
+      auto pr = __builtin_amdgcn_permlane16_swap(send, send, false, false);
+      const uint32_t recv = odd ? pr[0] : pr[1];
+      const uint32_t lo = odd ? recv : keep, hi = odd ? keep : recv;
+      if (valid) {
+        uint8_t* prow = a.packed + ((rbase + 64 * ap) >> 1) + 2 * (g & 2);
+        st_stream(prow + 8 * (g & 1), __builtin_amdgcn_perm(hi, lo, 0x05040100u));
+        st_stream(prow + 8 * (2 + (g & 1)), __builtin_amdgcn_perm(hi, lo, 0x07060302u));
+      }
+    }
+  }
+
+  if constexpr (OP == OP_AMAX) {
+    run_max = group_max(run_max, 64);
+    if (lane == 0) wmax[wave] = run_max;
+    __syncthreads();
+    if (tid == 0) {
+      float mm = wmax[0];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) mm = fmaxf(mm, wmax[w]);
+      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(nvfp4_tensor_scale(mm * cnorm)));
+    }
+  }
+}
+
+template <int OP>
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fast172_kernel(KernelArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kXRows * kPitch];
+  __shared__ uint4 sgn[kChunks];
+  __shared__ float wmax[kW];
+  const int tid = threadIdx.x;
+  for (int c = tid; c < kChunks; c += kT) {
+    uint4 m = make_uint4(0, 0, 0, 0);
+    if (a.signs) {
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + 8 * c);
+      m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
+      m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
+      m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
+      m.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
+    }
+    sgn[c] = m;
+  }
+  for (int c = tid; c < (kXRows - 172) * kPitch / 16; c += kT)
+    reinterpret_cast<uint4*>(xs + 172 * kPitch)[c] = make_uint4(0, 0, 0, 0);
+  // (the first barrier of the row loop orders these writes before any read)
+  if ((tid >> 6) < 3) rows172<OP, 3>(a, xs, sgn, wmax);
+  else rows172<OP, 2>(a, xs, sgn, wmax);
+}
+
+template <int OP>
+hipError_t launch172(const KernelArgs& a, hipStream_t s) {
+  auto kern = fast172_kernel<OP>;
+  static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
+  const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s) {
+  if (a.n != kN || a.sign_period != kN) return hipErrorNotSupported;
+  if (reinterpret_cast<uintptr_t>(a.x) & 15) return hipErrorNotSupported;
+  switch (op) {
+    case OP_ROTATE: return launch172<OP_ROTATE>(a, s);
+    case OP_INT4:
+      if (!(a.group >= 16 && a.group <= 256)) return hipErrorNotSupported;   // per-row INT4: generic
+      return launch172<OP_INT4>(a, s);
+    case OP_NVFP4: return launch172<OP_NVFP4>(a, s);
+    case OP_MXFP4: return launch172<OP_MXFP4>(a, s);
+    case OP_AMAX: return launch172<OP_AMAX>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace rhtq

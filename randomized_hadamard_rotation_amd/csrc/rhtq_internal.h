@@ -48,6 +48,9 @@ hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
 // Two-wave kernel for 12288-wide rows (called by launch_fast).
 hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s);
 
+// Matrix-core kernel for 11008-wide rows, H172 (x) H64 (called by launch_fast).
+hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s);
+
 // Two-stage matrix-core kernel for 1024-, 2048- and 4096-wide rows (called by launch_fast).
 hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s);
 
