@@ -9,14 +9,16 @@
 //
 //  1. The row (172 x 128 bytes) arrives by 16-byte loads issued one row ahead; the random
 //     signs are XORed onto the bf16 sign bits (masks in LDS) and the row is written to LDS
-//     as 172 rows a of 64 bf16, row pitch 160 bytes; rows 172..191 are zero.
+//     transposed, as 64 rows b of 192 bf16 (a contiguous, a >= 172 zero); row b starts at
+//     528 b + 16 ((b >> 3) & 7) bytes.  The pitch (4 mod 32 dwords) puts the rows of one
+//     16-byte read on distinct banks, and the shift does the same for the eight rows b = 8 k + e
+//     of one 2-byte write, so neither conflicts.
 //  2. Stage 1, H172 over a, exact on the bf16 input: v_mfma_f32_16x16x32_bf16 with
-//     A = X^T (M = b, K = a), read from LDS two bytes per lane and slot, and B = H172^T
+//     A = X^T (M = b, K = a), one 16-byte LDS read per fragment, and B = H172^T
 //     (K = a, N = a'), a +-1 operand held in registers.  K slot e of lane group g stands for
-//     a = 32 ks + g + 4 e, so the four lane groups of one read hit disjoint LDS banks.  Wave w
-//     owns the output tiles a' in [16 t, 16 t + 16), t = w, w + 4, w + 8 (11 tiles, 172
-//     padded to 176).  Result D1[b][a']: lane l holds a' = 16 t + (l & 15) and
-//     b = 16 mt + 4 (l >> 4) + i in tile mt, register i.
+//     a = 32 ks + 8 g + e.  Wave w owns the output tiles a' in [16 t, 16 t + 16),
+//     t = w, w + 4, w + 8 (11 tiles, 172 padded to 176).  Result D1[b][a']: lane l holds
+//     a' = 16 t + (l & 15) and b = 16 mt + 4 (l >> 4) + i in tile mt, register i.
 //  3. Stage 2, H64 = H2 (x) H32 over b: index bit 5 (mt >> 1) is a register butterfly, the
 //     other five bits one v_mfma_f32_16x16x32_f16 with A = H32 (M = b''_lo, K = b_lo) and
 //     B = the butterflied values, whose registers already are that B layout (slot e of lane
@@ -41,22 +43,23 @@ namespace {
 constexpr int kW = 4;
 constexpr int kT = 64 * kW;
 constexpr int kN = 11008;                        // 172 x 64
-constexpr int kPitch = 160;                      // LDS bytes per a-row (128 data + 32 pad)
-constexpr int kXRows = 192;                      // six K-steps of 32
+constexpr int kPitch = 528;                      // LDS bytes per b-row: 192 bf16, shift, pad
+constexpr int kXBytes = 64 * kPitch;
+__host__ __device__ constexpr int xrow(int b) { return b * kPitch + 16 * ((b >> 3) & 7); }
 constexpr int kChunks = kN / 8;                  // 16-byte chunks per row
 constexpr int kLoads = (kChunks + kT - 1) / kT;  // loads per thread and row
 
 __constant__ H172Bits<false> kH172Rows;
 
 // Stage-1 B operand for output tile t and K-step ks: slot e of lane group g stands for
-// a = 32 ks + g + 4 e, column n = lane & 15 for a' = 16 t + n; H172[a'][a] as bf16 +-1,
+// a = 32 ks + 8 g + e, column n = lane & 15 for a' = 16 t + n; H172[a'][a] as bf16 +-1,
 // zero outside 172 x 172.
 __device__ bf16x8 h172t_operand(int lane, int t, int ks) {
   const int ap = 16 * t + (lane & 15), g = lane >> 4;
   uint16_t bits[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int k = 32 * ks + g + 4 * e;
+    const int k = 32 * ks + 8 * g + e;
     uint16_t v = 0;
     if (k < 172 && ap < 172) v = ((kH172Rows.w[ap][k >> 5] >> (k & 31)) & 1u) ? 0xBF80 : 0x3F80;
     bits[e] = v;
@@ -90,7 +93,12 @@ __device__ __forceinline__ float col_max(float v) {
   return __uint_as_float(umax(q[0], q[1]));
 }
 
-template <int OP, int NT>
+// Maximum of two non-negative floats as unsigned bit patterns (no canonicalisation needed).
+__device__ __forceinline__ float nnmax(float a, float b) { return __uint_as_float(umax(__float_as_uint(a), __float_as_uint(b))); }
+
+// GC: group class, 4 (16-element groups: one run), 5 (32: two runs), 6 (64..256: whole
+// a'-rows); SD: INT4 scale storage (RHTQ_SCALE_F32 / F16).
+template <int OP, int GC, int SD, int NT>
 __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
@@ -109,10 +117,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
     gts = a.tensor_scale[0];
     inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
   }
-  int LG = 0;   // log2 of the group
-  if constexpr (OP == OP_INT4) LG = __builtin_ctz((unsigned)a.group);
-  if constexpr (OP == OP_NVFP4) LG = 4;
-  if constexpr (OP == OP_MXFP4) LG = 5;
+  const int LG = GC == 6 ? __builtin_ctz((unsigned)a.group) : GC;   // log2 of the group
   float run_max = 0.0f;
 
   uint4 raw[kLoads];
@@ -127,72 +132,86 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   int64_t row = blockIdx.x;
   load(row);
 
-  const uint8_t* xb = xs + g * kPitch + 2 * n;   // this lane's column b = n of the a-row g
-  for (; row < a.rows; row += gridDim.x) {
-    __syncthreads();   // the previous row's LDS reads are done
+  // this thread's chunks c = tid + 256 k hold a = (tid >> 3) + 32 k (a >> 3 = wave + 4 k) and
+  // b = 8 (tid & 7) + e
+  uint8_t* wbase = xs + xrow(8 * (tid & 7)) + 16 * wave + 2 * ((tid >> 3) & 7);
+  // fragment (ks, mt) of this lane: row b = 16 mt + n, a = 32 ks + 8 g .. + 7
+  const uint8_t* rbase_l[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) rbase_l[mt] = xs + xrow(16 * mt + n) + 16 * g;
+  // x of the row in raw[] -> LDS, signs applied
+  auto write_lds = [&]() {
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = tid + kT * k;
       if (c < kChunks) {
         const uint4 m = sgn[c];
-        uint4 r = raw[k];
-        r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
-        *reinterpret_cast<uint4*>(xs + (c >> 3) * kPitch + 16 * (c & 7)) = r;
+        const uint32_t w[4] = {raw[k].x ^ m.x, raw[k].y ^ m.y, raw[k].z ^ m.z, raw[k].w ^ m.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint16_t*>(wbase + e * kPitch + 64 * k) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
       }
     }
-    load(row + gridDim.x);   // the next row's loads run during this row's work
-    __syncthreads();
-
+  };
+  __syncthreads();   // sign masks and zeroed rows
+  if (row < a.rows) write_lds();
+  load(row + gridDim.x);
+  __syncthreads();
+  // per row: stage 1 reads the row from LDS; after the barrier that ends those reads the next
+  // row goes into LDS (its loads were issued one row earlier) and the loads of the row after
+  // it are issued, then stage 2 and the epilogue of this row run from registers
+  for (; row < a.rows; row += gridDim.x) {
     // ---------------- stage 1: H172 over a ----------------
     f32x4 acc[NT][4];
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[j][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) {
       bf16x8 av[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint8_t* p = xb + 32 * ks * kPitch + 32 * mt;
-        uint16_t v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const uint16_t*>(p + 4 * e * kPitch);
-        __builtin_memcpy(&av[mt], v, 16);
-      }
+      for (int mt = 0; mt < 4; ++mt) av[mt] = *reinterpret_cast<const bf16x8*>(rbase_l[mt] + 64 * ks);
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], hb[j][ks], acc[j][mt], 0, 0, 0);
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], hb[j][ks], ks == 0 ? z : acc[j][mt], 0, 0, 0);
+        }
     }
+    __syncthreads();   // every wave has read this row
+    if (row + gridDim.x < a.rows) write_lds();
+    load(row + 2 * (int64_t)gridDim.x);
 
     const int64_t rbase = row * kN;
+    // ---------------- stage 2: H2 by butterfly, H32 on the matrix cores ----------------
+    // (each step runs over all of this wave's tiles before the next, so that the tiles'
+    // independent chains interleave)
+    float u[NT][2][2][4];   // [tile][hb][mt & 1][i], b_lo = 16 (mt & 1) + 4 g + i
+    float S[NT], invS_t[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int ap = 16 * (wave + 4 * j) + n;
-      const bool valid = ap < 172;
-      // ---------------- stage 2: H2 by butterfly, H32 on the matrix cores ----------------
-      float u[2][2][4];   // [hb][mt & 1][i], b_lo = 16 (mt & 1) + 4 g + i
       float m = 0.0f;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = acc[j][h][i], q = acc[j][h + 2][i];
-          u[0][h][i] = p + q;
-          u[1][h][i] = p - q;
+          u[j][0][h][i] = p + q;
+          u[j][1][h][i] = p - q;
           m = fmaxf(m, fmaxf(fabsf(p + q), fabsf(p - q)));
         }
-      float S, invS;
-      split_scale(__float_as_uint(col_max(m)), S, invS);
-      float d2[4][4];   // [run r = 2 hb + mt2][i]: b'' = 16 r + 4 g + i
+      S[j] = m;
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) split_scale(__float_as_uint(col_max(S[j])), S[j], invS_t[j]);
+    float d2a[NT][4][4];   // [tile][run r = 2 hb + mt2][i]: b'' = 16 r + 4 g + i
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         float ys[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ys[e] = u[h][e >> 2][e & 3];
+        for (int e = 0; e < 8; ++e) ys[e] = u[j][h][e >> 2][e & 3];
         uint32_t hw[4], lw[4];
-        split8(ys, S, hw, lw);
+        split8(ys, S[j], hw, lw);
         f16x8 bh, bl;
         __builtin_memcpy(&bh, hw, 16);
         __builtin_memcpy(&bl, lw, 16);
@@ -202,10 +221,16 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
           f32x4 o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[mt2], bh, z, 0, 0, 0);
           o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[mt2], bl, o, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) d2[2 * h + mt2][i] = o[i];
+          for (int i = 0; i < 4; ++i) d2a[j][2 * h + mt2][i] = o[i];
         }
       }
 
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int ap = 16 * (wave + 4 * j) + n;
+      const bool valid = ap < 172;
+      const float invS = invS_t[j];
+      const auto& d2 = d2a[j];
       const int64_t ebase = rbase + 64 * ap + 4 * g;   // element of run 0, i = 0
       if constexpr (OP == OP_ROTATE) {
         if (valid) {
@@ -220,54 +245,50 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       for (int r = 0; r < 4; ++r)
         mr[r] = fmaxf(fmaxf(fabsf(d2[r][0]), fabsf(d2[r][1])), fmaxf(fabsf(d2[r][2]), fabsf(d2[r][3])));
       if constexpr (OP == OP_AMAX) {
-        run_max = fmaxf(run_max, fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3])) * invS);
+        run_max = nnmax(run_max, nnmax(nnmax(mr[0], mr[1]), nnmax(mr[2], mr[3])) * invS);
         continue;
       }
 
-      // ---------------- group scales ----------------
-      float gm[4];   // group maximum (true units, before 1/sqrt(n)) of the group holding run r
-      if (LG == 4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gm[r] = col_max(mr[r]) * invS;
-      } else if (LG == 5) {
-        const float m0 = col_max(fmaxf(mr[0], mr[1])) * invS, m1 = col_max(fmaxf(mr[2], mr[3])) * invS;
-        gm[0] = gm[1] = m0;
-        gm[2] = gm[3] = m1;
-      } else {
-        float mm = col_max(fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3]))) * invS;
-        if (LG >= 7) mm = dpp_max<0xB1>(mm);   // a' pairs (lane xor 1)
-        if (LG >= 8) mm = dpp_max<0x4E>(mm);   // a' quads (lane xor 2)
-        gm[0] = gm[1] = gm[2] = gm[3] = mm;
-      }
-      // the group of run r, and whether this lane stores its scale: for LG 4 / 5 lane group g
-      // stores group g of the a'-row, for LG >= 6 lane group 0 of the first a' of the group
+      // ---------------- group scales, once per group ----------------
+      // sl[r]: factor from split units to code units for run r (0 for an all-zero group)
       float sl[4];
       bool clamp = false;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t gi = (rbase + 64 * ap + 16 * r) >> LG;
-        const bool writer = valid && (LG == 4 ? g == r : LG == 5 ? (g == (r >> 1) && (r & 1) == 0)
-                                                                  : (g == 0 && r == 0 && (ap & ((1 << (LG - 6)) - 1)) == 0));
-        const float bm = gm[r];
+      auto scale_of = [&](float bm, int64_t gi, bool writer) -> float {   // bm: true units, before 1/sqrt(n)
         if constexpr (OP == OP_INT4) {
-          const Int4Scale sc = int4_scale(bm, cnorm, a.scale_dtype);
-          sl[r] = sc.inv * invS;
+          const Int4Scale sc = int4_scale(bm, cnorm, SD);
           clamp |= sc.clamp;
           if (writer) {
-            if (a.scale_dtype == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[gi] = sc.s;
+            if constexpr (SD == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[gi] = sc.s;
             else static_cast<__half*>(a.scales)[gi] = __float2half_rn(fminf(sc.s, 65504.0f));
           }
+          return sc.inv * invS;
         } else if constexpr (OP == OP_NVFP4) {
           const uint32_t code = e4m3_code((bm * cnorm) * inv6g);
           const float seff = e4m3_value(code) * gts;
-          sl[r] = seff > 0.0f ? (cnorm * __builtin_amdgcn_rcpf(seff)) * invS : 0.0f;
           if (writer) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)code;
+          return seff > 0.0f ? (cnorm * __builtin_amdgcn_rcpf(seff)) * invS : 0.0f;
         } else {
           const float bt = bm * cnorm;
           const int ex = mx_exponent(bt);
-          sl[r] = bt > 0.0f ? __builtin_ldexpf(invS * cnorm, -ex) : 0.0f;
           if (writer) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)(ex + 127);
+          return bt > 0.0f ? __builtin_ldexpf(invS * cnorm, -ex) : 0.0f;
         }
+      };
+      const int64_t e0 = rbase + 64 * ap;   // first element of this lane's a'-row
+      if constexpr (GC == 4) {   // a run per group; lane group g stores the scale of run g
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sl[r] = scale_of(col_max(mr[r]) * invS, (e0 + 16 * r) >> 4, valid && g == r);
+      } else if constexpr (GC == 5) {   // two runs per group; lane groups 0 and 1 store
+        const float s0 = scale_of(col_max(nnmax(mr[0], mr[1])) * invS, e0 >> 5, valid && g == 0);
+        const float s1 = scale_of(col_max(nnmax(mr[2], mr[3])) * invS, (e0 + 32) >> 5, valid && g == 1);
+        sl[0] = sl[1] = s0;
+        sl[2] = sl[3] = s1;
+      } else {   // 1, 2 or 4 whole a'-rows per group; lane group 0 of the group's first a' stores
+        float mm = col_max(nnmax(nnmax(mr[0], mr[1]), nnmax(mr[2], mr[3]))) * invS;
+        if (LG >= 7) mm = dpp_max<0xB1>(mm);   // a' pairs (lane xor 1)
+        if (LG >= 8) mm = dpp_max<0x4E>(mm);   // a' quads (lane xor 2)
+        const float s0 = scale_of(mm, e0 >> LG, valid && g == 0 && (ap & ((1 << (LG - 6)) - 1)) == 0);
+        sl[0] = sl[1] = sl[2] = sl[3] = s0;
       }
 
       // ---------------- codes: runs 0,1 -> p01, runs 2,3 -> p23 (run in 16-bit halves) ----------------
@@ -275,12 +296,18 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       if constexpr (OP == OP_INT4) {
         const bool any_clamp = __builtin_amdgcn_ballot_w64(clamp) != 0;
         uint32_t q[4][4];
+        if (!any_clamp) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            q[r][i] = any_clamp ? __float_as_uint(__builtin_amdgcn_fmed3f(d2[r][i] * sl[r], -8.0f, 7.0f) + 12582912.0f)
-                                : __float_as_uint(__builtin_fmaf(d2[r][i], sl[r], 12582912.0f));
+            for (int i = 0; i < 4; ++i) q[r][i] = __float_as_uint(__builtin_fmaf(d2[r][i], sl[r], 12582912.0f));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              q[r][i] = __float_as_uint(__builtin_amdgcn_fmed3f(d2[r][i] * sl[r], -8.0f, 7.0f) + 12582912.0f);
+        }
         const uint32_t q01[8] = {q[0][0], q[0][1], q[0][2], q[0][3], q[1][0], q[1][1], q[1][2], q[1][3]};
         const uint32_t q23[8] = {q[2][0], q[2][1], q[2][2], q[2][3], q[3][0], q[3][1], q[3][2], q[3][3]};
         p01 = pack8_nibbles(q01);
@@ -316,6 +343,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
         st_stream(prow + 8 * (2 + (g & 1)), __builtin_amdgcn_perm(hi, lo, 0x07060302u));
       }
     }
+    __syncthreads();   // the next row is in LDS
   }
 
   if constexpr (OP == OP_AMAX) {
@@ -325,15 +353,15 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
     if (tid == 0) {
       float mm = wmax[0];
 #pragma unroll
-      for (int w = 1; w < kW; ++w) mm = fmaxf(mm, wmax[w]);
+      for (int w = 1; w < kW; ++w) mm = nnmax(mm, wmax[w]);
       atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(nvfp4_tensor_scale(mm * cnorm)));
     }
   }
 }
 
-template <int OP>
+template <int OP, int GC, int SD>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fast172_kernel(KernelArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kXRows * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
   __shared__ uint4 sgn[kChunks];
   __shared__ float wmax[kW];
   const int tid = threadIdx.x;
@@ -348,20 +376,28 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fa
     }
     sgn[c] = m;
   }
-  for (int c = tid; c < (kXRows - 172) * kPitch / 16; c += kT)
-    reinterpret_cast<uint4*>(xs + 172 * kPitch)[c] = make_uint4(0, 0, 0, 0);
-  // (the first barrier of the row loop orders these writes before any read)
-  if ((tid >> 6) < 3) rows172<OP, 3>(a, xs, sgn, wmax);
-  else rows172<OP, 2>(a, xs, sgn, wmax);
+  for (int c = tid; c < kXBytes / 16; c += kT) reinterpret_cast<uint4*>(xs)[c] = make_uint4(0, 0, 0, 0);   // a >= 172 stays 0
+  if ((tid >> 6) < 3) rows172<OP, GC, SD, 3>(a, xs, sgn, wmax);
+  else rows172<OP, GC, SD, 2>(a, xs, sgn, wmax);
 }
 
-template <int OP>
+template <int OP, int GC, int SD>
 hipError_t launch172(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast172_kernel<OP>;
+  auto kern = fast172_kernel<OP, GC, SD>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
+}
+
+template <int SD>
+hipError_t launch172_int4(const KernelArgs& a, hipStream_t s) {
+  switch (a.group) {
+    case 16: return launch172<OP_INT4, 4, SD>(a, s);
+    case 32: return launch172<OP_INT4, 5, SD>(a, s);
+    case 64: case 128: case 256: return launch172<OP_INT4, 6, SD>(a, s);
+    default: return hipErrorNotSupported;   // per-row INT4: the generic kernel
+  }
 }
 
 }  // namespace
@@ -370,13 +406,12 @@ hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s) {
   if (a.n != kN || a.sign_period != kN) return hipErrorNotSupported;
   if (reinterpret_cast<uintptr_t>(a.x) & 15) return hipErrorNotSupported;
   switch (op) {
-    case OP_ROTATE: return launch172<OP_ROTATE>(a, s);
+    case OP_ROTATE: return launch172<OP_ROTATE, 6, 0>(a, s);
     case OP_INT4:
-      if (!(a.group >= 16 && a.group <= 256)) return hipErrorNotSupported;   // per-row INT4: generic
-      return launch172<OP_INT4>(a, s);
-    case OP_NVFP4: return launch172<OP_NVFP4>(a, s);
-    case OP_MXFP4: return launch172<OP_MXFP4>(a, s);
-    case OP_AMAX: return launch172<OP_AMAX>(a, s);
+      return a.scale_dtype == RHTQ_SCALE_F32 ? launch172_int4<RHTQ_SCALE_F32>(a, s) : launch172_int4<RHTQ_SCALE_F16>(a, s);
+    case OP_NVFP4: return launch172<OP_NVFP4, 4, 0>(a, s);
+    case OP_MXFP4: return launch172<OP_MXFP4, 5, 0>(a, s);
+    case OP_AMAX: return launch172<OP_AMAX, 6, 0>(a, s);
     default: return hipErrorNotSupported;
   }
 }
