@@ -29,8 +29,9 @@
 //  4. Output D2[b''][a']: lane l holds a' = 16 t + (l & 15) and, in run r = 2 hb + mt2,
 //     b'' = 16 r + 4 (l >> 4) + i.  Groups of 16 and 32 are runs, groups of 64..256 are
 //     1..4 consecutive a' (lane bits 0-1); maxima by lane swaps and DPP.  INT4 codes by the
-//     magic-constant FMA, E2M1 by v_cvt_scalef32_pk_fp4_f32; lane groups g and g ^ 1 trade
-//     runs so that each lane stores eight consecutive codes as one dword.
+//     magic-constant FMA, E2M1 by v_cvt_scalef32_pk_fp4_f32; two lane swaps (lane groups
+//     g ^ 1, then g ^ 2) leave lane group g with run g whole, so each store instruction writes
+//     sixteen complete 32-byte a'-rows.
 #include <hip/hip_fp16.h>
 
 #include "rhtq.h"
@@ -337,11 +338,14 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       auto pr = __builtin_amdgcn_permlane16_swap(send, send, false, false);
       const uint32_t recv = odd ? pr[0] : pr[1];
       const uint32_t lo = odd ? recv : keep, hi = odd ? keep : recv;
-      if (valid) {
-        uint8_t* prow = a.packed + ((rbase + 64 * ap) >> 1) + 2 * (g & 2);
-        st_stream(prow + 8 * (g & 1), __builtin_amdgcn_perm(hi, lo, 0x05040100u));
-        st_stream(prow + 8 * (2 + (g & 1)), __builtin_amdgcn_perm(hi, lo, 0x07060302u));
-      }
+      // now w0 holds bytes 2 (g & 2) + 8 (g & 1) .. + 3 of the a'-row and w1 the same + 16; lane
+      // groups g and g ^ 2 trade once more so that lane group g holds bytes 8 g .. 8 g + 7
+      const uint32_t w0 = __builtin_amdgcn_perm(hi, lo, 0x05040100u), w1 = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+      const bool upper = g & 2;
+      const uint32_t send2 = upper ? w0 : w1;
+      auto pr2 = __builtin_amdgcn_permlane32_swap(send2, send2, false, false);
+      const uint32_t recv2 = upper ? pr2[0] : pr2[1];
+      if (valid) st_stream(a.packed + ((rbase + 64 * ap) >> 1) + 8 * g, upper ? recv2 : w0, upper ? w1 : recv2);
     }
     __syncthreads();   // the next row is in LDS
   }
