@@ -52,19 +52,36 @@ __device__ __forceinline__ Int4Scale int4_scale(float amax, float cnorm, int sca
   return r;
 }
 
-// Constant MFMA B operand of v_mfma_f32_16x16x32_bf16 for a 32-point Sylvester
-// Hadamard: B_t[x][n] = H32[x][2n + t] with x = 8 (lane >> 4) + e and n = lane & 15, so
-// output column n of N-tile t is element 2n + t of the transformed 32-vector.
-__device__ __forceinline__ bf16x8 h32_operand(int lane, int t) {
-  uint16_t bits[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int xk = 8 * (lane >> 4) + e;
-    const int o = 2 * (lane & 15) + t;
-    bits[e] = (__builtin_popcount(xk & o) & 1) ? 0xBF80 : 0x3F80;
+// Constant +-1 MFMA operands, per lane, as compile-time tables (one 16-byte load per lane
+// instead of building them with popcounts at kernel start):
+//  b1[t][lane]: B operand of v_mfma_f32_16x16x32_bf16 for a 32-point Sylvester Hadamard,
+//    B_t[x][n] = H32[x][2n + t] with x = 8 (lane >> 4) + e and n = lane & 15, so output
+//    column n of N-tile t is element 2n + t of the transformed 32-vector (bf16).
+//  s2[t2][lane]: stage-2 B operand of v_mfma_f32_16x16x32_f16, the H32 over element bits
+//    5-9: k = 8 (lane >> 4) + e stands for bits 5,6 = e & 3, bits 7,8 = lane >> 4,
+//    bit 9 = e >> 2; column n = lane & 15 stands for output bits 5-8 and tile t2 for
+//    output bit 9 (f16).
+struct alignas(16) H32Operands {
+  uint16_t b1[2][64][8];
+  uint16_t s2[2][64][8];
+  constexpr H32Operands() : b1(), s2() {
+    for (int t = 0; t < 2; ++t)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          const int xk = 8 * (lane >> 4) + e, o = 2 * (lane & 15) + t;
+          b1[t][lane][e] = (__builtin_popcount(xk & o) & 1) ? 0xBF80 : 0x3F80;
+          const int k = (e & 3) | ((lane >> 4) << 2) | ((e >> 2) << 4), n = (lane & 15) | (t << 4);
+          s2[t][lane][e] = (__builtin_popcount(k & n) & 1) ? 0xBC00 : 0x3C00;
+        }
   }
+};
+namespace {
+__constant__ H32Operands kH32Ops;
+}
+
+__device__ __forceinline__ bf16x8 h32_operand(int lane, int t) {
   bf16x8 r;
-  __builtin_memcpy(&r, bits, 16);
+  __builtin_memcpy(&r, &kH32Ops.b1[t][lane][0], 16);
   return r;
 }
 
@@ -176,19 +193,9 @@ __device__ __forceinline__ float group_max(float v, int G) {
 
 // ---- two-stage matrix-core transform helpers ----
 
-// Stage-2 B operand of v_mfma_f32_16x16x32_f16: the +-1 H32 over element bits 5-9.
-// k = 8 (lane >> 4) + e stands for bits 5,6 = e & 3, bits 7,8 = lane >> 4, bit 9 = e >> 2;
-// column n = lane & 15 stands for output bits 5-8 and tile t2 for output bit 9.
 __device__ __forceinline__ f16x8 h32_stage2_operand(int lane, int t2) {
-  uint16_t bits[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int k = (e & 3) | ((lane >> 4) << 2) | ((e >> 2) << 4);
-    const int n = (lane & 15) | (t2 << 4);
-    bits[e] = (__builtin_popcount(k & n) & 1) ? 0xBC00 : 0x3C00;
-  }
   f16x8 r;
-  __builtin_memcpy(&r, bits, 16);
+  __builtin_memcpy(&r, &kH32Ops.s2[t2][lane][0], 16);
   return r;
 }
 

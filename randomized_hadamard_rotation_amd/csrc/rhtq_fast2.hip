@@ -243,6 +243,222 @@ void fast2_kernel(KernelArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small row counts at n = 4096: two waves per row, two rows per workgroup.  With one wave per
+// row a SIMD holds only the few rows the call has and sits idle while they wait on their own
+// dependency chains; splitting each row doubles the waves and halves each chain.  Wave h takes
+// the row half j = 2048 h + [0, 2048) (fragments 4 h .. 4 h + 3): stages 1 and 2 and the
+// bit-10 butterfly as above, in its own split units.  Bit 11 pairs the halves: wave h keeps
+// its partial sums for output chunks with bit 10 = h, sends the others through LDS, and both
+// sides go to the smaller of the two split scales (powers of two, exact).  Wave h then owns
+// the output chunks 1024 (2 h' + h) + [0, 1024), h' = 0, 1.  Per-row INT4 takes the row
+// maximum over both waves through LDS.  The sign masks are built once per workgroup in LDS
+// (shared by its two rows).  If the row count is odd the last workgroup's second pair repeats
+// the last row (identical bytes), so both pairs always pass the same barriers.
+// ---------------------------------------------------------------------------
+#ifndef RHTQ_PAIR_WAVES
+#define RHTQ_PAIR_WAVES 4
+#endif
+
+struct PairShared {
+  uint4 xch[2][4][64];   // [wave h][value quad][lane]
+  float xs[2];           // [h]: split scale S
+  float rmax[2];         // [h]: row maximum of the half (true units)
+};
+
+// Wave H's half of one row (H a template parameter so every register array is indexed by
+// constants).  sign_tab: [sign period / N][8 fragments][64 lanes] masks, as fast2_kernel.
+template <int OP, int H>
+__device__ __forceinline__ void pair_row(const KernelArgs& a, const uint4* sign_tab, PairShared& sh, int64_t row) {
+  constexpr int N = 4096, NF = 8;
+  const int lane = threadIdx.x & 63;
+  const float cnorm = (float)(1.0 / __builtin_sqrt((double)N));
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const int lcol = 32 * (lane & 15) + 8 * (lane >> 4);   // this lane's 8 elements within a fragment
+
+  uint4 raw[4];
+#pragma unroll
+  for (int fl = 0; fl < 4; ++fl) raw[fl] = ld_stream(x + row * N + 512 * (4 * H + fl) + lcol);
+  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
+  int G = 0;
+  if constexpr (OP == OP_INT4) G = a.group == N ? 0 : __builtin_ctz((unsigned)a.group);
+  if constexpr (OP == OP_NVFP4) G = 4;
+  if constexpr (OP == OP_MXFP4) G = 5;
+  const int lc = (lane >> 4) | ((lane & 15) << 2);
+
+  // ---------------- stage 1 (fragments 4 H .. 4 H + 3) ----------------
+  const int slices = a.sign_period / N;
+  const int slice = slices > 1 ? (int)(row % slices) : 0;
+  float d1[4][2][4];
+#pragma unroll
+  for (int fl = 0; fl < 4; ++fl) {
+    uint4 r = raw[fl];
+    const uint4 m = sign_tab[(slice * NF + 4 * H + fl) * 64 + lane];
+    r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
+    bf16x8 av;
+    __builtin_memcpy(&av, &r, 16);
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
+    const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { d1[fl][0][i] = p0[i]; d1[fl][1][i] = p1[i]; }
+  }
+  float m1 = 0.0f;
+#pragma unroll
+  for (int fl = 0; fl < 4; ++fl)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fabsf(d1[fl][t][i]));
+  m1 = group_max(m1, 64);
+  float S, invS;
+  split_scale(__float_as_uint(m1), S, invS);
+
+  // ---------------- stage 2 + bit 10 ----------------
+  // d2[t][gl][t2][i2]: element t + 2 i2 + 8 lc + 512 t2 + 1024 gl of this half
+  float d2[2][2][2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int gl = 0; gl < 2; ++gl) {
+      float ys[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ys[e] = d1[2 * gl + (e >> 2)][t][e & 3];
+      uint32_t hw[4], lw[4];
+      split8(ys, S, hw, lw);
+      f16x8 ah, al;
+      __builtin_memcpy(&ah, hw, 16);
+      __builtin_memcpy(&al, lw, 16);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, hc[t2], z, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, hc[t2], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d2[t][gl][t2][i] = acc[i];
+      }
+    }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bfly(d2[t][0][t2][i], d2[t][1][t2][i]);
+
+  // ---------------- bit 11: exchange halves ----------------
+  // sent: the partial sums with bit-10 index 1 - H, as quads q = 2 t + t2
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float* sv = d2[q >> 1][1 - H][q & 1];
+    sh.xch[H][q][lane] = make_uint4(__float_as_uint(sv[0]), __float_as_uint(sv[1]), __float_as_uint(sv[2]),
+                                    __float_as_uint(sv[3]));
+  }
+  if (lane == 0) sh.xs[H] = S;
+  __syncthreads();   // (workgroup-wide: both pairs of the workgroup pass it together)
+  // common units: the smaller of the two split scales (the half with the larger maximum), so
+  // neither side is scaled up; only the side with the larger scale is rescaled
+  const float So = sh.xs[1 - H];
+  const bool own_common = S <= So;
+  const float f = own_common ? S * __builtin_amdgcn_rcpf(So) : So * invS;   // power of two <= 1
+  if (!own_common) invS = __builtin_amdgcn_rcpf(So);
+  // y2[hp][t][t2][i]: output element t + 2 i + 8 lc + 512 t2 + 1024 (2 hp + H)
+  float y2[2][2][2][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = q >> 1, t2 = q & 1;
+    const uint4 rv = sh.xch[1 - H][q][lane];
+    const float r4[4] = {__uint_as_float(rv.x), __uint_as_float(rv.y), __uint_as_float(rv.z), __uint_as_float(rv.w)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float own = d2[t][H][t2][i], oth = r4[i];
+      if (own_common) oth *= f; else own *= f;
+      // y[j] = (half 0) + (half 1) and y[j + 2048] = (half 0) - (half 1)
+      y2[0][t][t2][i] = own + oth;
+      y2[1][t][t2][i] = H == 0 ? own - oth : oth - own;
+    }
+  }
+
+  auto val = [&](int q, int r) -> float { return y2[q >> 1][r & 1][q & 1][r >> 1]; };
+  auto cbase = [](int q) { return 512 * (q & 1) + 2048 * (q >> 1) + 1024 * H; };
+  const int64_t ebase = row * N;
+
+  if constexpr (OP == OP_AMAX) {
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(val(q, r)));
+    m = group_max(m * invS, 64);
+    if (lane == 0) sh.rmax[H] = m;
+    __syncthreads();
+    if (lane == 0 && H == 0)   // one atomic per row (per pair)
+      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale),
+                __float_as_uint(nvfp4_tensor_scale(fmaxf(sh.rmax[0], sh.rmax[1]) * cnorm)));
+  } else if constexpr (OP == OP_ROTATE) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float o[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) o[r] = (val(q, r) * invS) * cnorm;
+      float* p = a.y + ebase + cbase(q) + 8 * lc;
+      st_stream(p, o[0], o[1], o[2], o[3]);
+      st_stream(p + 4, o[4], o[5], o[6], o[7]);
+    }
+  } else {
+    float gts = 0.0f, inv6g = 0.0f;
+    if constexpr (OP == OP_NVFP4) {
+      gts = a.tensor_scale[0];
+      inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
+    }
+    quant_epilogue<OP, 4>(a, row, ebase, G, invS, cnorm, gts, inv6g, lane, lane == 0 && H == 0, val, cbase,
+                          [&](float m) {
+                            const float wm = group_max(m, 64);
+                            if (lane == 0) sh.rmax[H] = wm;
+                            __syncthreads();
+                            return fmaxf(sh.rmax[0], sh.rmax[1]);
+                          });
+  }
+}
+
+template <int OP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RHTQ_PAIR_WAVES))) void fast2p_kernel(KernelArgs a) {
+  constexpr int N = 4096, NF = 8;
+  extern __shared__ uint4 sign_tab[];   // [sign period / N][NF][64]
+  __shared__ PairShared sh[2];
+  const int slices = a.sign_period / N;
+  for (int k = threadIdx.x; k < slices * NF * 64; k += 256) {
+    uint4 m = make_uint4(0, 0, 0, 0);
+    if (a.signs) {
+      const int kl = k & 63, kf = k >> 6;
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + N * (kf / NF) + 512 * (kf % NF) + 32 * (kl & 15) +
+                                                       8 * (kl >> 4));
+      m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
+      m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
+      m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
+      m.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
+    }
+    sign_tab[k] = m;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, pair = wave >> 1;
+  int64_t row = 2 * (int64_t)blockIdx.x + pair;
+  if (row >= a.rows) row = a.rows - 1;   // odd row count: repeat the last row
+  if (wave & 1) pair_row<OP, 1>(a, sign_tab, sh[pair], row);
+  else pair_row<OP, 0>(a, sign_tab, sh[pair], row);
+}
+
+template <int OP>
+hipError_t launch2p(const KernelArgs& a, hipStream_t s) {
+  if constexpr (OP == OP_INT4) {
+    if (!(a.group == 4096 || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
+  }
+  const size_t lds = (size_t)(a.sign_period / 4096) * 8 * 64 * 16;
+  if (lds > 32768 || a.rows > 0xFFFFFFFE) return hipErrorNotSupported;
+  hipLaunchKernelGGL(fast2p_kernel<OP>, dim3((unsigned)((a.rows + 1) / 2)), dim3(256), lds, s, a);   // two rows per workgroup
+  return hipGetLastError();
+}
+
 template <int LOGM, int OP>
 hipError_t launch2(const KernelArgs& a, hipStream_t s) {
   using S2 = Shape2<LOGM>;
@@ -263,12 +479,26 @@ hipError_t launch2(const KernelArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Row counts up to this use two waves per 4096-wide row (RHTQ_PAIR_ROWS overrides; read once).
+inline int64_t pair_rows_limit() {
+  static const int64_t v = [] {
+    const char* e = getenv("RHTQ_PAIR_ROWS");
+    return e != nullptr ? (int64_t)atoll(e) : (int64_t)4096;
+  }();
+  return v;
+}
+
 template <int OP>
 hipError_t dispatch2(const KernelArgs& a, hipStream_t s) {
   switch (a.n) {
     case 1024: return launch2<10, OP>(a, s);
     case 2048: return launch2<11, OP>(a, s);
-    case 4096: return launch2<12, OP>(a, s);
+    case 4096:
+      if (a.rows <= pair_rows_limit()) {
+        const hipError_t e = launch2p<OP>(a, s);
+        if (e != hipErrorNotSupported) return e;
+      }
+      return launch2<12, OP>(a, s);
     default: return hipErrorNotSupported;
   }
 }
