@@ -364,15 +364,31 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, const uint4* sign_
   if (!own_common) invS = __builtin_amdgcn_rcpf(So);
   // y2[hp][t][t2][i]: output element t + 2 i + 8 lc + 512 t2 + 1024 (2 hp + H)
   float y2[2][2][2][4];
+  float r16[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 rv = sh.xch[1 - H][q][lane];
+    r16[q][0] = __uint_as_float(rv.x); r16[q][1] = __uint_as_float(rv.y);
+    r16[q][2] = __uint_as_float(rv.z); r16[q][3] = __uint_as_float(rv.w);
+  }
+  // (a uniform branch, written out twice so that the rescale is one multiply per value)
+  if (own_common) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r16[q][i] *= f;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d2[q >> 1][H][q & 1][i] *= f;
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int t = q >> 1, t2 = q & 1;
-    const uint4 rv = sh.xch[1 - H][q][lane];
-    const float r4[4] = {__uint_as_float(rv.x), __uint_as_float(rv.y), __uint_as_float(rv.z), __uint_as_float(rv.w)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float own = d2[t][H][t2][i], oth = r4[i];
-      if (own_common) oth *= f; else own *= f;
+      const float own = d2[t][H][t2][i], oth = r16[q][i];
       // y[j] = (half 0) + (half 1) and y[j + 2048] = (half 0) - (half 1)
       y2[0][t][t2][i] = own + oth;
       y2[1][t][t2][i] = H == 0 ? own - oth : oth - own;
