@@ -244,7 +244,7 @@ void fast2_kernel(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Small row counts at n = 4096: two waves per row, two rows per workgroup.  With one wave per
+// Small row counts at n = 4096: two waves per row, four rows per workgroup.  With one wave per
 // row a SIMD holds only the few rows the call has and sits idle while they wait on their own
 // dependency chains; splitting each row doubles the waves and halves each chain.  Wave h takes
 // the row half j = 2048 h + [0, 2048) (fragments 4 h .. 4 h + 3): stages 1 and 2 and the
@@ -253,12 +253,16 @@ void fast2_kernel(KernelArgs a) {
 // sides go to the smaller of the two split scales (powers of two, exact).  Wave h then owns
 // the output chunks 1024 (2 h' + h) + [0, 1024), h' = 0, 1.  Per-row INT4 takes the row
 // maximum over both waves through LDS.  The sign masks are built once per workgroup in LDS
-// (shared by its two rows).  If the row count is odd the last workgroup's second pair repeats
-// the last row (identical bytes), so both pairs always pass the same barriers.
+// (shared by its rows).  Pairs past the last row repeat the last row (identical bytes), so all
+// pairs of a workgroup always pass the same barriers.
 // ---------------------------------------------------------------------------
 #ifndef RHTQ_PAIR_WAVES
 #define RHTQ_PAIR_WAVES 4
 #endif
+#ifndef RHTQ_PAIR_RPW
+#define RHTQ_PAIR_RPW 4
+#endif
+constexpr int kPairRows = RHTQ_PAIR_RPW;   // rows per workgroup (two waves each)
 
 struct PairShared {
   uint4 xch[2][4][64];   // [wave h][value quad][lane]
@@ -438,12 +442,12 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, const uint4* sign_
 }
 
 template <int OP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RHTQ_PAIR_WAVES))) void fast2p_kernel(KernelArgs a) {
+__global__ __launch_bounds__(128 * kPairRows) __attribute__((amdgpu_waves_per_eu(RHTQ_PAIR_WAVES))) void fast2p_kernel(KernelArgs a) {
   constexpr int N = 4096, NF = 8;
   extern __shared__ uint4 sign_tab[];   // [sign period / N][NF][64]
-  __shared__ PairShared sh[2];
+  __shared__ PairShared sh[kPairRows];
   const int slices = a.sign_period / N;
-  for (int k = threadIdx.x; k < slices * NF * 64; k += 256) {
+  for (int k = threadIdx.x; k < slices * NF * 64; k += 128 * kPairRows) {
     uint4 m = make_uint4(0, 0, 0, 0);
     if (a.signs) {
       const int kl = k & 63, kf = k >> 6;
@@ -458,8 +462,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RHTQ_PAIR_W
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, pair = wave >> 1;
-  int64_t row = 2 * (int64_t)blockIdx.x + pair;
-  if (row >= a.rows) row = a.rows - 1;   // odd row count: repeat the last row
+  int64_t row = kPairRows * (int64_t)blockIdx.x + pair;
+  if (row >= a.rows) row = a.rows - 1;   // past the end: repeat the last row (same bytes, same barriers)
   if (wave & 1) pair_row<OP, 1>(a, sign_tab, sh[pair], row);
   else pair_row<OP, 0>(a, sign_tab, sh[pair], row);
 }
@@ -471,7 +475,8 @@ hipError_t launch2p(const KernelArgs& a, hipStream_t s) {
   }
   const size_t lds = (size_t)(a.sign_period / 4096) * 8 * 64 * 16;
   if (lds > 32768 || a.rows > 0xFFFFFFFE) return hipErrorNotSupported;
-  hipLaunchKernelGGL(fast2p_kernel<OP>, dim3((unsigned)((a.rows + 1) / 2)), dim3(256), lds, s, a);   // two rows per workgroup
+  hipLaunchKernelGGL(fast2p_kernel<OP>, dim3((unsigned)((a.rows + kPairRows - 1) / kPairRows)), dim3(128 * kPairRows), lds, s,
+                     a);
   return hipGetLastError();
 }
 
