@@ -282,6 +282,26 @@ def test_zero_tokens_is_noop(R):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("tokens", [4095, 4096, 4097, 4099])
+def test_4096_row_count_paths(R, tokens):
+    """Width 4096 runs two waves per row up to 4096 rows and one wave per row beyond: both sides of
+    the switch, a row count that leaves workgroup slots past the last row, every format (sampled
+    rows; the NVFP4 tensor scale over all rows)."""
+    import torch
+    w = WORKLOADS["llama_4096_int4"]
+    x, s = x_to(w, tokens)
+    rows = np.unique(np.array([0, 1, 2, 3, tokens // 2, tokens - 4, tokens - 3, tokens - 2, tokens - 1]))
+    for fmt, grp, sd in [("int4", 0, "f32"), ("int4", 128, "f16"), ("nvfp4", 16, "e4m3"), ("mxfp4", 32, "e8m0")]:
+        say(f"rows={tokens} {fmt} g{grp}")
+        g_ref = None
+        if fmt == "nvfp4":
+            amax = max(float(np.max(np.abs(O.rotate(x[r0:r0 + 2048].cpu(), s)))) for r0 in range(0, tokens, 2048))
+            g_ref = np.float32(amax / 2688.0)
+        check_forward(R, x, s, fmt, grp, sd, rows=rows, g_ref=g_ref)
+    y = to_np(R.rhtq_rotate(x, s))
+    C.check_rotation(y[rows], O.rotate(x[rows].cpu(), s))
+
+
 def test_deterministic(R):
     import torch
     for name in ("llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096",
