@@ -8,6 +8,9 @@ quantisation and packing of every row; for NVFP4 also the tensor-amax pass).
 Inputs are generated on the device before timing and rotate through enough
 buffer sets (>= 512 MB) that the 256 MB Infinity Cache cannot hold them, so the
 timed region reads HBM.  Timing uses HIP events on the stream the kernels run on.
+The K timed steps are captured once into a HIP graph and the replay is timed
+(--no-graph: eager launches), so that the host's per-call cost does not stretch
+a kernel of a few microseconds; the eager time is reported beside it.
 
 Prints ONE JSON line (rank 0).  `value` is tokens/s of the headline workload
 (2048 x 4096 bf16, per-token INT4); the d=12288, KV and NVFP4 workloads are
@@ -65,7 +68,39 @@ def traffic_for(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def time_workload(R, torch, name, steps, warmup):
+def run_timed(torch, step, steps, warmup, graph):
+    """Event-timed K steps on the current stream, after W untimed ones.  Returns (ms per step as
+    reported, eager ms per step).  graph=True captures the K steps once into a HIP graph
+    (torch.cuda.CUDAGraph) and times its replay: every step is still one full call on its own
+    buffers, but the host's per-call cost (Python, ctypes) no longer stretches the measurement of
+    a kernel that runs for a few microseconds."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    def timed(run):
+        stream = torch.cuda.current_stream()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        run()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    ms_eager = timed(lambda: [step(i) for i in range(steps)])
+    if not graph:
+        return ms_eager, ms_eager
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    return timed(g.replay), ms_eager
+
+
+def time_workload(R, torch, name, steps, warmup, graph=True):
     from workloads import WORKLOADS, bytes_per_call, generate
     w = WORKLOADS[name]
     x0, signs = generate(w, "cuda")
@@ -81,30 +116,19 @@ def time_workload(R, torch, name, steps, warmup):
         scales = torch.empty((w.tokens, ng), dtype=sdt, device="cuda")
         ts = torch.zeros(1, dtype=torch.float32, device="cuda") if w.fmt == "nvfp4" else None
         outs.append((packed, scales, ts))
-    stream = torch.cuda.current_stream()
-
-    def step(i):
+    def step(i):   # on the current stream (the capture stream while a graph is recorded)
         packed, scales, ts = outs[i % sets]
         R.rhtq_forward(xs[i % sets], s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype,
-                       tensor_scale=ts, packed=packed, scales=scales, stream=stream, block=w.block or None)
+                       tensor_scale=ts, packed=packed, scales=scales, block=w.block or None)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms, ms_eager = run_timed(torch, step, steps, warmup, graph)
     tokens = w.tokens * w.tokens_per_row
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {
         "workload": name, "tokens": int(tokens), "rows": w.tokens, "n": w.n,
         "in_dtype": w.in_dtype, "fmt": w.fmt, "group": w.group, "scale_dtype": w.scale_dtype,
-        "buffer_sets": sets, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+        "buffer_sets": sets, "ms_per_step": ms, "eager_ms_per_step": ms_eager,
+        "launch": "hip-graph replay" if graph else "eager", "tokens_per_s": tokens / (ms * 1e-3),
         "rows_per_s": w.tokens / (ms * 1e-3), "bytes_per_call": nbytes, "achieved_gbs": gbs,
         "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
         "launches_per_step": 3 if w.fmt == "nvfp4" else 1,
@@ -114,7 +138,7 @@ def time_workload(R, torch, name, steps, warmup):
 INVERSE = ["kv_128_int4g128"]
 
 
-def time_inverse(R, torch, name, steps, warmup):
+def time_inverse(R, torch, name, steps, warmup, graph=True):
     """The KV-cache read path: rhtq_inverse of the workload's own codes (fp32 output)."""
     from workloads import WORKLOADS, generate
     w = WORKLOADS[name]
@@ -125,26 +149,15 @@ def time_inverse(R, torch, name, steps, warmup):
     nbytes = packed.numel() + scales.numel() * scales.element_size() + w.tokens * w.n * 4
     sets = max(1, min(8, math.ceil(CACHE_DEFEAT_BYTES / nbytes)))
     outs = [torch.empty((w.tokens, w.n), dtype=torch.float32, device="cuda") for _ in range(sets)]
-    stream = torch.cuda.current_stream()
-
     def step(i):
         R.rhtq_inverse(packed, scales, w.n, s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype,
-                       tensor_scale=ts, out=outs[i % sets], stream=stream)
+                       tensor_scale=ts, out=outs[i % sets])
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms, ms_eager = run_timed(torch, step, steps, warmup, graph)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": name + " (inverse)", "rows": w.tokens, "n": w.n, "fmt": w.fmt, "group": w.group,
-            "ms_per_step": ms, "rows_per_s": w.tokens / (ms * 1e-3), "bytes_per_call": nbytes,
+            "ms_per_step": ms, "eager_ms_per_step": ms_eager, "launch": "hip-graph replay" if graph else "eager",
+            "rows_per_s": w.tokens / (ms * 1e-3), "bytes_per_call": nbytes,
             "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
@@ -215,6 +228,7 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--only", action="store_true", help="time only --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--rocprof-summary", metavar="DIR",
@@ -242,14 +256,15 @@ def main():
         copy_calibration(torch)
         return
 
-    head = time_workload(R, torch, args.workload, args.steps, args.warmup)
+    graph = not args.no_graph
+    head = time_workload(R, torch, args.workload, args.steps, args.warmup, graph)
     also = []
     if not args.only:
         for name in OTHERS:
             if name != args.workload:
-                also.append(time_workload(R, torch, name, args.steps, args.warmup))
+                also.append(time_workload(R, torch, name, args.steps, args.warmup, graph))
         for name in INVERSE:
-            also.append(time_inverse(R, torch, name, args.steps, args.warmup))
+            also.append(time_inverse(R, torch, name, args.steps, args.warmup, graph))
 
     per_launch_ms = head["ms_per_step"] / head["launches_per_step"]
     traffic = traffic_for(args.workload)
@@ -273,6 +288,8 @@ def main():
                    "in_dtype": head["in_dtype"], "fmt": head["fmt"], "group": head["group"],
                    "scale_dtype": head["scale_dtype"], "buffer_sets": head["buffer_sets"]},
         "hbm_gbs": head["achieved_gbs"],
+        "launch": head["launch"],
+        "eager_ms_per_step": head["eager_ms_per_step"],
         "roofline": roofline,
         "also": also,
     }
