@@ -43,6 +43,10 @@
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
  *    the call returns once it is enqueued.  A fault inside a kernel surfaces at
  *    the caller's next synchronisation, as usual for HIP.
+ *  - The calls enqueue kernels only (no memset, copy or host synchronisation; the
+ *    dynamic NVFP4 path clears its tensor-scale word with a kernel), so they can be
+ *    captured into a HIP graph on a capturing stream.  The first call of each
+ *    kernel variant queries occupancy on the host: make one call before capturing.
  *  - Arguments are checked on the host before any HIP call; on error nothing is
  *    enqueued and the status says why.  tokens == 0 is a valid no-op.
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.
