@@ -1,6 +1,7 @@
-// Two-stage matrix-core kernel for bf16 rows of 1024, 2048 and 4096 elements.
+// Two-stage matrix-core kernels for bf16 rows of 1024, 2048 and 4096 elements.
 //
-// One wavefront owns one row at a time (persistent grid).  Per row:
+// fast2_kernel: one wavefront owns one row at a time (persistent grid).  fast2p_kernel (below,
+// 4096-wide rows at small row counts) splits each row over two waves.  Per row:
 //
 //  1. Coalesced 16-byte loads in the MFMA A layout (lane l loads elements
 //     512 f + 32 (l & 15) + 8 (l >> 4) + e of fragment f); random signs by XOR of bf16
