@@ -271,25 +271,16 @@ __device__ __forceinline__ void split8(const float* y, float S, uint32_t* hi, ui
 }
 
 // E4M3FN (OCP FP8) code of s >= 0: nearest value, ties to even mantissa, saturating at
-// 448 (0x7E); NaN never produced.
+// 448 (0x7E), subnormals kept; NaN never produced.  gfx950's conversion instruction does the
+// rounding; the input is clamped to 448 first so nothing overflows.  Checked on the device
+// against a bit-level definition of this encoding on every code, every midpoint between
+// neighbouring codes (and one ulp either side) and 65536 log-uniform values: no difference.
 __device__ __forceinline__ uint32_t e4m3_code(float s) {
-  if (!(s > 0.0f)) return 0u;
-  if (s >= 448.0f) return 0x7Eu;
-  const uint32_t bits = __float_as_uint(s);
-  const int ex = (int)((bits >> 23) & 0xFF) - 127;
-  if (ex < -6) return (uint32_t)__builtin_rintf(s * 512.0f);   // subnormal steps of 2^-9
-  uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);          // round mantissa to 3 bits
-  r &= ~0xFFFFFu;
-  const int e2 = (int)((r >> 23) & 0xFF) - 127;
-  const uint32_t code = (uint32_t)((e2 + 7) << 3) | ((r >> 20) & 7u);
-  return code > 0x7Eu ? 0x7Eu : code;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 0) return (float)m * (1.0f / 512.0f);
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
+// Value of an E4M3FN code 0 .. 0x7E (the conversion instruction; exact).
+__device__ __forceinline__ float e4m3_value(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
 // MX shared exponent of a 32-block with maximum bmax >= 0 (OCP MX v1.0): floor(log2(bmax))
 // minus 2 (the largest E2M1 normal is 1.5 * 2^2), clamped to [-127, 127]; -127 for a zero
