@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused randomized Hadamard rotation + 4-bit quantisation on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only] [--given]
 
 A step is one rhtq_forward call over one batch of the workload (rotation, scale,
 quantisation and packing of every row; for NVFP4 also the tensor-amax pass).
@@ -13,8 +13,10 @@ The K timed steps are captured once into a HIP graph and the replay is timed
 a kernel of a few microseconds; the eager time is reported beside it.
 
 Prints ONE JSON line (rank 0).  `value` is tokens/s of the headline workload
-(2048 x 4096 bf16, per-token INT4); the d=12288, KV and NVFP4 workloads are
-reported under "also".  The CPU oracle, timed on a bounded sample on the host,
+(2048 x 4096 bf16, per-token INT4); the d=12288, KV, NVFP4 (dynamic and with a
+given tensor scale), MXFP4, block-diagonal and d=11008 workloads and the KV
+inverse are reported under "also", and a plain 512 MiB device copy under
+"hbm_copy" as the bandwidth a streaming kernel reaches in practice.  The CPU oracle, timed on a bounded sample on the host,
 is reported as "cpu_baseline" (a baseline, not a target).
 """
 from __future__ import annotations
@@ -100,11 +102,14 @@ def run_timed(torch, step, steps, warmup, graph):
     return timed(g.replay), ms_eager
 
 
-def time_workload(R, torch, name, steps, warmup, graph=True):
+def time_workload(R, torch, name, steps, warmup, graph=True, given=False):
+    """given=True (NVFP4 only): the tensor scale is the caller's (read, not computed), so one
+    launch per step; it is set from one dynamic call on the same input before timing."""
     from workloads import WORKLOADS, bytes_per_call, generate
     w = WORKLOADS[name]
+    assert not given or w.fmt == "nvfp4"
     x0, signs = generate(w, "cuda")
-    nbytes = bytes_per_call(w)
+    nbytes = bytes_per_call(w, tensor_scale_dynamic=not given)
     sets = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / nbytes)))
     xs = [x0] + [x0.clone() for _ in range(sets - 1)]
     s_dev = torch.from_numpy(signs).to("cuda")
@@ -116,26 +121,33 @@ def time_workload(R, torch, name, steps, warmup, graph=True):
         scales = torch.empty((w.tokens, ng), dtype=sdt, device="cuda")
         ts = torch.zeros(1, dtype=torch.float32, device="cuda") if w.fmt == "nvfp4" else None
         outs.append((packed, scales, ts))
+    if given:
+        g = R.rhtq_forward(x0, s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype)[2]
+        for _, _, ts in outs:
+            ts.copy_(g)
+    mode = "given" if given else "dynamic"
     def step(i):   # on the current stream (the capture stream while a graph is recorded)
         packed, scales, ts = outs[i % sets]
         R.rhtq_forward(xs[i % sets], s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype,
-                       tensor_scale=ts, packed=packed, scales=scales, block=w.block or None)
+                       tensor_scale=ts, tensor_scale_mode=mode, packed=packed, scales=scales,
+                       block=w.block or None)
 
     ms, ms_eager = run_timed(torch, step, steps, warmup, graph)
     tokens = w.tokens * w.tokens_per_row
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {
-        "workload": name, "tokens": int(tokens), "rows": w.tokens, "n": w.n,
+        "workload": name + (" (given g)" if given else ""), "tokens": int(tokens), "rows": w.tokens, "n": w.n,
         "in_dtype": w.in_dtype, "fmt": w.fmt, "group": w.group, "scale_dtype": w.scale_dtype,
         "buffer_sets": sets, "ms_per_step": ms, "eager_ms_per_step": ms_eager,
         "launch": "hip-graph replay" if graph else "eager", "tokens_per_s": tokens / (ms * 1e-3),
         "rows_per_s": w.tokens / (ms * 1e-3), "bytes_per_call": nbytes, "achieved_gbs": gbs,
         "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
-        "launches_per_step": 3 if w.fmt == "nvfp4" else 1,
+        "launches_per_step": 3 if w.fmt == "nvfp4" and not given else 1,
     }
 
 
 INVERSE = ["kv_128_int4g128"]
+GIVEN = ["nvfp4_4096"]   # NVFP4 with the caller's tensor scale: one pass over x
 
 
 def time_inverse(R, torch, name, steps, warmup, graph=True):
@@ -183,6 +195,26 @@ def cpu_baseline(name, budget_s=10.0):
                       f"({el:.1f} s, numpy fp64, one process)"}
 
 
+def copy_bandwidth(torch, nbytes=512 << 20, reps=20):
+    """A plain device-to-device copy (torch's copy kernel) of nbytes, event-timed: read plus
+    write bytes per second, the bandwidth a streaming kernel can reach in practice on this GPU."""
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    return {"bytes": 2 * nbytes, "ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": 2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=8):
     """A plain device copy of known size (torch's elementwise negation of fp32, which reads
     and writes nbytes each): the HBM counters read under it give the factor that turns
@@ -212,6 +244,16 @@ def rocprof_summary(root, pattern):
             for c, per in cs.items():
                 xs = list(per.values())
                 print(f"PMC {c} mean_per_dispatch {sum(xs) / len(xs):.6g} dispatches {len(xs)} kernel {k}")
+    for f in sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)):
+        durs = collections.defaultdict(list)
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if pattern in r["Kernel_Name"]:
+                    durs[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        for k, ds in durs.items():
+            ds.sort()
+            q = lambda p: ds[min(len(ds) - 1, int(p * (len(ds) - 1) + 0.5))]
+            print(f"TRACE calls {len(ds)} p10_ns {q(0.1)} median_ns {q(0.5)} p90_ns {q(0.9)} kernel {k}")
     for f in sorted(glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True)):
         with open(f) as fh:
             for r in csv.DictReader(fh):
@@ -227,6 +269,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--only", action="store_true", help="time only --workload")
+    ap.add_argument("--given", action="store_true", help="NVFP4 workload with a given tensor scale")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -257,17 +300,19 @@ def main():
         return
 
     graph = not args.no_graph
-    head = time_workload(R, torch, args.workload, args.steps, args.warmup, graph)
+    head = time_workload(R, torch, args.workload, args.steps, args.warmup, graph, given=args.given)
     also = []
     if not args.only:
         for name in OTHERS:
             if name != args.workload:
                 also.append(time_workload(R, torch, name, args.steps, args.warmup, graph))
+        for name in GIVEN:
+            also.append(time_workload(R, torch, name, args.steps, args.warmup, graph, given=True))
         for name in INVERSE:
             also.append(time_inverse(R, torch, name, args.steps, args.warmup, graph))
 
     per_launch_ms = head["ms_per_step"] / head["launches_per_step"]
-    traffic = traffic_for(args.workload)
+    traffic = traffic_for(args.workload + ("_given" if args.given else ""))
     roofline = {"bound": "hbm", "achieved": head["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": head["achieved_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel_ms": per_launch_ms, "algorithmic_bytes_per_launch": head["bytes_per_call"]}
@@ -293,6 +338,8 @@ def main():
         "roofline": roofline,
         "also": also,
     }
+    if not args.only:
+        out["hbm_copy"] = copy_bandwidth(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(out), flush=True)
