@@ -376,28 +376,27 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, const uint4* sign_
     r16[q][0] = __uint_as_float(rv.x); r16[q][1] = __uint_as_float(rv.y);
     r16[q][2] = __uint_as_float(rv.z); r16[q][3] = __uint_as_float(rv.w);
   }
-  // (a uniform branch, written out twice so that the rescale is one multiply per value)
+  // y[j] = (half 0) + (half 1) and y[j + 2048] = (half 0) - (half 1), with the rescale by the
+  // power of two f folded into one FMA per output (the product is exact, so this equals the
+  // multiply-then-add); a uniform branch picks which side is rescaled
   if (own_common) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r16[q][i] *= f;
+      for (int i = 0; i < 4; ++i) {
+        const float own = d2[q >> 1][H][q & 1][i], oth = r16[q][i];
+        y2[0][q >> 1][q & 1][i] = __builtin_fmaf(oth, f, own);
+        y2[1][q >> 1][q & 1][i] = H == 0 ? __builtin_fmaf(-oth, f, own) : __builtin_fmaf(oth, f, -own);
+      }
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d2[q >> 1][H][q & 1][i] *= f;
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int t = q >> 1, t2 = q & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float own = d2[t][H][t2][i], oth = r16[q][i];
-      // y[j] = (half 0) + (half 1) and y[j + 2048] = (half 0) - (half 1)
-      y2[0][t][t2][i] = own + oth;
-      y2[1][t][t2][i] = H == 0 ? own - oth : oth - own;
-    }
+      for (int i = 0; i < 4; ++i) {
+        const float own = d2[q >> 1][H][q & 1][i], oth = r16[q][i];
+        y2[0][q >> 1][q & 1][i] = __builtin_fmaf(own, f, oth);
+        y2[1][q >> 1][q & 1][i] = H == 0 ? __builtin_fmaf(own, f, -oth) : __builtin_fmaf(-own, f, oth);
+      }
   }
 
   auto val = [&](int q, int r) -> float { return y2[q >> 1][r & 1][q & 1][r >> 1]; };
