@@ -198,6 +198,45 @@ def test_workload_full_size_sampled(R, name):
         assert not bool(((lo == 8) | (hi == 8)).any())
 
 
+# Inputs of more than 2^31 elements: every element, code and scale index is 64-bit.  Row counts
+# put element 2^31 inside the tensor; the oracle checks the rows around it, the first and the last
+# (only those rows are copied to the host).
+BEYOND_INT32 = [("llama_4096_int4", 2 ** 19 + 5), ("mxfp4_4096", 2 ** 19 + 3), ("kv_128_int4g128", 2 ** 24 + 3),
+                ("downproj_12288_int4g128", 174763), ("downproj7b_11008_int4g128", 195085)]
+
+
+@pytest.mark.parametrize("name,tokens", BEYOND_INT32)
+def test_beyond_int32_elements(R, name, tokens):
+    import torch
+    w = WORKLOADS[name].with_tokens(tokens)
+    assert tokens * w.n > 2 ** 31
+    say(f"{name} at {tokens} x {w.n} = {tokens * w.n} elements")
+    x, s = generate(w, dev())
+    rb = 2 ** 31 // w.n   # the row holding element 2^31
+    rows = np.unique(np.array([0, rb - 1, rb, rb + 1, tokens - 1]))
+    rows = rows[rows < tokens]
+    rows_t = torch.from_numpy(rows).to(dev())
+    packed, scales, _ = R.rhtq_forward(x, s, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype)
+    torch.cuda.synchronize()
+    y_ref = O.rotate(x[rows_t].cpu(), s)
+    p_rows, s_rows = to_np(packed[rows_t]), to_np(scales[rows_t])
+    if w.fmt == "int4":
+        print(C.check_int4(p_rows, s_rows, y_ref, w.group, w.scale_dtype))
+    else:
+        print(C.check_mxfp4(p_rows, s_rows, y_ref))
+    del x
+    if name.startswith("kv_"):
+        # the KV read path over the same > 2^31-element tensor
+        xh = R.rhtq_inverse(packed, scales, w.n, s, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype)
+        torch.cuda.synchronize()
+        ref = O.inverse(p_rows, s_rows, s, w.fmt, w.group, None)
+        err = np.max(np.abs(to_np(xh[rows_t]) - ref), axis=1)
+        assert np.all(err <= 1e-5 * np.max(np.abs(ref), axis=1) + 1e-30)
+        del xh
+    del packed, scales
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------
 # sweeps: every width, several token counts, signs on / off, fp32 input
 # ----------------------------------------------------------------------------
