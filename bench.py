@@ -173,9 +173,11 @@ def time_inverse(R, torch, name, steps, warmup, graph=True):
             "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
-def cpu_baseline(name, budget_s=10.0):
-    """The oracle, untouched, on the host: repeat the full workload input until the
-    budget is spent (single process; numpy's elementwise kernels use one thread)."""
+def _oracle_reps(args):
+    """One process's share of the CPU baseline: the workload's full input (drawn here from the
+    same seeds) through the oracle, untouched, repeated until the budget is spent.
+    Returns (repetitions, seconds)."""
+    name, budget_s = args
     import numpy as np
     import oracle as O
     from workloads import WORKLOADS, generate
@@ -188,11 +190,39 @@ def cpu_baseline(name, budget_s=10.0):
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    return {"value": reps * w.tokens * w.tokens_per_row / el, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{reps} x full {w.tokens}x{w.n} {w.in_dtype} input of {name} "
-                      f"({el:.1f} s, numpy fp64, one process)"}
+            return reps, el
+
+
+def cpu_baseline(name, budget_s=10.0, procs=None):
+    """The oracle, untouched, on the host: `procs` fresh single-threaded interpreters (one per
+    core this process may use, at most 16), each running the full workload input through the
+    oracle for the same budget at the same time; `value` is the sum of their rates.  The same
+    in this one process is reported beside it.  Runs before anything touches the GPU."""
+    import multiprocessing
+    from workloads import WORKLOADS
+    w = WORKLOADS[name]
+    per_input = w.tokens * w.tokens_per_row
+    reps, el = _oracle_reps((name, budget_s))
+    one = reps * per_input / el
+    procs = procs or max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                                else os.cpu_count() or 1))
+    env_before = os.environ.get("OMP_NUM_THREADS")
+    os.environ["OMP_NUM_THREADS"] = "1"   # read by the children at their NumPy import
+    try:
+        with multiprocessing.get_context("spawn").Pool(procs) as pool:
+            res = pool.map(_oracle_reps, [(name, budget_s)] * procs)
+    finally:
+        if env_before is None:
+            os.environ.pop("OMP_NUM_THREADS", None)
+        else:
+            os.environ["OMP_NUM_THREADS"] = env_before
+    pooled = sum(r * per_input / e for r, e in res)
+    return {"value": pooled, "unit": "tokens/s", "cores": procs, "kind": "oracle",
+            "sample": f"{procs} single-threaded processes at once, each repeating the numpy fp64 oracle over the "
+                      f"full {w.tokens}x{w.n} {w.in_dtype} input of {name} for {budget_s:.0f} s "
+                      f"({sum(r for r, _ in res)} repetitions in all)",
+            "single_process": {"value": one, "unit": "tokens/s", "cores": 1,
+                               "sample": f"{reps} x the full input in this process ({el:.1f} s)"}}
 
 
 def copy_bandwidth(torch, nbytes=512 << 20, reps=20):
@@ -290,6 +320,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    # the oracle's CPU baseline first, while no process has touched the GPU
+    cpu = None if (args.no_cpu_baseline or args.copy_calibration) else cpu_baseline(args.workload)
+
     import torch
     import randomized_hadamard_rotation_amd as R
     if not torch.cuda.is_available():
@@ -340,8 +373,8 @@ def main():
     }
     if not args.only:
         out["hbm_copy"] = copy_bandwidth(torch)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
