@@ -62,11 +62,19 @@ __device__ __forceinline__ void load_row(const uint16_t* x, int64_t row, int64_t
   }
 }
 
-#ifndef RHTQ_FAST2_WAVES
-#define RHTQ_FAST2_WAVES 2
-#endif
-template <int LOGM, int OP, int DEPTH>
-__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RHTQ_FAST2_WAVES)))
+// Prefetch depth (rows whose loads are in flight ahead of the current one) and the minimum waves
+// per SIMD asked of the register allocator, by width.  Measured at 16384-65536 rows (INT4, MXFP4,
+// NVFP4): without prefetch the registers leave room for three or four waves per SIMD at 4096
+// (five to eight at the narrower widths), and those waves hide the load latency better than a
+// two-row prefetch at two waves per SIMD did.
+template <int LOGM>
+struct Tune2 {
+  static constexpr int DEPTH = 0;
+  static constexpr int WAVES = LOGM == 10 ? 4 : 3;
+};
+
+template <int LOGM, int OP, int DEPTH, int WAVES>
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void fast2_kernel(KernelArgs a) {
   using S2 = Shape2<LOGM>;
   constexpr int N = S2::N, NF = S2::NF, NG = S2::NG, R = S2::R;
@@ -486,11 +494,7 @@ hipError_t launch2(const KernelArgs& a, hipStream_t s) {
   if constexpr (OP == OP_INT4) {
     if (!(a.group == S2::N || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-#ifdef RHTQ_FAST2_DEPTH
-  auto kern = fast2_kernel<LOGM, OP, RHTQ_FAST2_DEPTH>;
-#else
-  auto kern = fast2_kernel<LOGM, OP, 2>;
-#endif
+  auto kern = fast2_kernel<LOGM, OP, Tune2<LOGM>::DEPTH, Tune2<LOGM>::WAVES>;
   static const int max_blocks = resident_blocks((const void*)kern, kThreads2, S2::NF * 64 * 16);
   const int64_t want = (a.rows + kWaves2 - 1) / kWaves2;
   const int grid = (int)(want < max_blocks ? want : max_blocks);
