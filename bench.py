@@ -42,6 +42,7 @@ KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast2.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast172.hip",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_fastw.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_epilogue.h",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_inverse_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_device.h",

@@ -54,6 +54,10 @@ hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s);
 // Two-stage matrix-core kernel for 1024-, 2048- and 4096-wide rows (called by launch_fast).
 hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s);
 
+// 8192- and 16384-wide rows, 2 or 4 waves per row with the top index bits exchanged through LDS
+// (called by launch_fast).
+hipError_t launch_fastw(int op, const KernelArgs& a, hipStream_t s);
+
 // Integer matrix-core inverse for KV-cache rows (64, 128, 256) with one INT4 scale per row.
 // Returns hipErrorNotSupported for other cases (the generic kernel then runs).
 hipError_t launch_inverse_fast(const KernelArgs& a, hipStream_t s);

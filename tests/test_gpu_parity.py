@@ -281,6 +281,39 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
+@pytest.mark.parametrize("n", [8192, 16384])
+def test_wide_rows_many_per_workgroup(R, n):
+    """8192- and 16384-wide rows: 2503 rows, more than the resident workgroups, so every
+    workgroup of the persistent kernel loops over several rows, and a count no grid divides.
+    The oracle checks sampled rows (the dynamic NVFP4 tensor scale over all of them)."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(WORKLOADS["llama_4096_int4"], n=n, tokens=2503)
+    say(f"wide rows n={n} tokens={w.tokens}")
+    x, s = generate(w, dev())
+    rows = np.unique(np.concatenate([np.arange(0, w.tokens, 37), [1, w.tokens - 2, w.tokens - 1]]))
+    rows_t = torch.from_numpy(rows).to(dev())
+    y_ref = O.rotate(x[rows_t].cpu(), s)
+    y = R.rhtq_rotate(x, s)
+    torch.cuda.synchronize()
+    C.check_rotation(to_np(y[rows_t]), y_ref)
+    del y
+    for fmt, group, sd in [("int4", 0, "f32"), ("int4", 128, "f16"), ("mxfp4", 32, "e8m0"), ("nvfp4", 16, "e4m3")]:
+        say(f"wide rows n={n} {fmt} group={group}")
+        packed, scales, ts = R.rhtq_forward(x, s, fmt=fmt, group=group, scale_dtype=sd)
+        torch.cuda.synchronize()
+        p_rows, s_rows = to_np(packed[rows_t]), to_np(scales[rows_t])
+        if fmt == "int4":
+            print(C.check_int4(p_rows, s_rows, y_ref, group, sd))
+        elif fmt == "mxfp4":
+            print(C.check_mxfp4(p_rows, s_rows, y_ref))
+        else:
+            amax = 0.0
+            for r0 in range(0, w.tokens, 256):
+                amax = max(amax, float(np.max(np.abs(O.rotate(x[r0:r0 + 256].cpu(), s)))))
+            print(C.check_nvfp4(p_rows, s_rows, float(ts.item()), y_ref, np.float32(amax / 2688.0)))
+
+
 def test_nvfp4_given_tensor_scale(R):
     import torch
     w = WORKLOADS["nvfp4_4096"].with_tokens(77)
