@@ -97,7 +97,8 @@ __device__ __forceinline__ float col_max(float v) {
 // Maximum of two non-negative floats as unsigned bit patterns (no canonicalisation needed).
 __device__ __forceinline__ float nnmax(float a, float b) { return __uint_as_float(umax(__float_as_uint(a), __float_as_uint(b))); }
 
-// GC: group class, 4 (16-element groups: one run), 5 (32: two runs), 6 (64..256: whole
+// GC: group class, 0 (one INT4 group per row: the row maximum across the four waves through
+// LDS), 4 (16-element groups: one run), 5 (32: two runs), 6 (64..256: whole
 // a'-rows); SD: INT4 scale storage (RHTQ_SCALE_F32 / F16).
 template <int OP, int GC, int SD, int NT>
 __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
@@ -226,6 +227,36 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
         }
       }
 
+    // per-token INT4: one scale for the row, from the maximum over every tile of the four waves
+    // (columns a' >= 172 are zero); all waves pass this barrier, GC being uniform
+    float row_inv = 0.0f;
+    bool row_clamp = false;
+    if constexpr (OP == OP_INT4 && GC == 0) {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        float mj = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mj = fmaxf(mj, fabsf(d2a[j][r][i]));
+        m = nnmax(m, mj * invS_t[j]);
+      }
+      m = group_max(m, 64);
+      if (lane == 0) wmax[wave] = m;
+      __syncthreads();
+      float rm = wmax[0];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) rm = nnmax(rm, wmax[w]);
+      const Int4Scale sc = int4_scale(rm, cnorm, SD);
+      row_inv = sc.inv;
+      row_clamp = sc.clamp;
+      if (tid == 0) {
+        if constexpr (SD == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[row] = sc.s;
+        else static_cast<__half*>(a.scales)[row] = __float2half_rn(fminf(sc.s, 65504.0f));
+      }
+    }
+
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int ap = 16 * (wave + 4 * j) + n;
@@ -276,7 +307,10 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
         }
       };
       const int64_t e0 = rbase + 64 * ap;   // first element of this lane's a'-row
-      if constexpr (GC == 4) {   // a run per group; lane group g stores the scale of run g
+      if constexpr (GC == 0) {   // the row's scale, in this tile's split units
+        sl[0] = sl[1] = sl[2] = sl[3] = row_inv * invS;
+        clamp = row_clamp;
+      } else if constexpr (GC == 4) {   // a run per group; lane group g stores the scale of run g
 #pragma unroll
         for (int r = 0; r < 4; ++r) sl[r] = scale_of(col_max(mr[r]) * invS, (e0 + 16 * r) >> 4, valid && g == r);
       } else if constexpr (GC == 5) {   // two runs per group; lane groups 0 and 1 store
@@ -400,7 +434,8 @@ hipError_t launch172_int4(const KernelArgs& a, hipStream_t s) {
     case 16: return launch172<OP_INT4, 4, SD>(a, s);
     case 32: return launch172<OP_INT4, 5, SD>(a, s);
     case 64: case 128: case 256: return launch172<OP_INT4, 6, SD>(a, s);
-    default: return hipErrorNotSupported;   // per-row INT4: the generic kernel
+    case kN: return launch172<OP_INT4, 0, SD>(a, s);   // one group per row
+    default: return hipErrorNotSupported;
   }
 }
 

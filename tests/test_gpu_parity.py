@@ -281,10 +281,11 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n", [8192, 16384])
+@pytest.mark.parametrize("n", [8192, 16384, 11008, 12288])
 def test_wide_rows_many_per_workgroup(R, n):
-    """8192- and 16384-wide rows: 2503 rows, more than the resident workgroups, so every
-    workgroup of the persistent kernel loops over several rows, and a count no grid divides.
+    """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 12288 = 12 x 1024): 2503 rows,
+    more than the resident workgroups, so every workgroup of the persistent kernel loops over
+    several rows (per-token INT4 takes a barrier per row), and a count no grid divides.
     The oracle checks sampled rows (the dynamic NVFP4 tensor scale over all of them)."""
     import dataclasses
     import torch
