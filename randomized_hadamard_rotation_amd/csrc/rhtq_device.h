@@ -57,19 +57,23 @@ __device__ __forceinline__ Int4Scale int4_scale(float amax, float cnorm, int sca
 //  b1[t][lane]: B operand of v_mfma_f32_16x16x32_bf16 for a 32-point Sylvester Hadamard,
 //    B_t[x][n] = H32[x][2n + t] with x = 8 (lane >> 4) + e and n = lane & 15, so output
 //    column n of N-tile t is element 2n + t of the transformed 32-vector (bf16).
+//  b16[t][lane]: as b1 for 16-wide rows, the block-diagonal I2 (x) H16: element bit 4 selects
+//    the row, so B_t[x][n] = H16[x & 15][(2n + t) & 15] where x and 2n + t share bit 4, else 0.
 //  s2[t2][lane]: stage-2 B operand of v_mfma_f32_16x16x32_f16, the H32 over element bits
 //    5-9: k = 8 (lane >> 4) + e stands for bits 5,6 = e & 3, bits 7,8 = lane >> 4,
 //    bit 9 = e >> 2; column n = lane & 15 stands for output bits 5-8 and tile t2 for
 //    output bit 9 (f16).
 struct alignas(16) H32Operands {
   uint16_t b1[2][64][8];
+  uint16_t b16[2][64][8];
   uint16_t s2[2][64][8];
-  constexpr H32Operands() : b1(), s2() {
+  constexpr H32Operands() : b1(), b16(), s2() {
     for (int t = 0; t < 2; ++t)
       for (int lane = 0; lane < 64; ++lane)
         for (int e = 0; e < 8; ++e) {
           const int xk = 8 * (lane >> 4) + e, o = 2 * (lane & 15) + t;
           b1[t][lane][e] = (__builtin_popcount(xk & o) & 1) ? 0xBF80 : 0x3F80;
+          b16[t][lane][e] = ((xk ^ o) & 16) ? 0x0000 : ((__builtin_popcount(xk & o & 15) & 1) ? 0xBF80 : 0x3F80);
           const int k = (e & 3) | ((lane >> 4) << 2) | ((e >> 2) << 4), n = (lane & 15) | (t << 4);
           s2[t][lane][e] = (__builtin_popcount(k & n) & 1) ? 0xBC00 : 0x3C00;
         }
@@ -82,6 +86,12 @@ __constant__ H32Operands kH32Ops;
 __device__ __forceinline__ bf16x8 h32_operand(int lane, int t) {
   bf16x8 r;
   __builtin_memcpy(&r, &kH32Ops.b1[t][lane][0], 16);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 h16_operand(int lane, int t) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &kH32Ops.b16[t][lane][0], 16);
   return r;
 }
 

@@ -1,7 +1,7 @@
 // Register-resident kernels for bf16 input on gfx950.
 //
 // One wavefront owns one row (rows of >= 512 elements) or one 512-element block of
-// consecutive rows (128- and 256-wide rows) at a time and loops over rows
+// consecutive rows (16- to 256-wide rows) at a time and loops over rows
 // (persistent grid).  Per row:
 //
 //  1. Coalesced 16-byte loads in the MFMA A-operand layout: lane l loads the 8
@@ -9,7 +9,8 @@
 //     instruction covers 512 consecutive elements.  The random signs are applied by
 //     XOR-ing bf16 sign bits with masks kept in LDS.
 //  2. The first five index bits (0..4) are transformed by v_mfma_f32_16x16x32_bf16
-//     against a constant +-1 Sylvester H32 operand.  The input is exact bf16 and the
+//     against a constant +-1 Sylvester H32 operand (for 16-wide rows the block-diagonal
+//     I2 (x) H16, bit 4 being a row bit).  The input is exact bf16 and the
 //     matrix is +-1, so every product is exact and the sums are fp32 accumulations,
 //     the same arithmetic as the first five butterfly stages.
 //  3. The remaining bits run as fp32 butterflies in registers: bits 5-6 and the
@@ -42,7 +43,7 @@ struct Shape {
   static constexpr int M = 1 << LOGM;                  // power-of-two factor
   static constexpr int N = F * M;                      // row width
   static constexpr int UNIT = N >= 512 ? N : 512;      // elements per wave iteration
-  static constexpr int RPU = UNIT / N;                 // rows per unit (1, 2 or 4)
+  static constexpr int RPU = UNIT / N;                 // rows per unit (1, 2, 4, 8, 16 or 32)
   static constexpr int NF = UNIT / 512;                // MFMA fragments per unit
   static constexpr int FPJ = (F == 12) ? M / 512 : NF; // fragments per power-of-two sub-row
   static constexpr int LOG_FPJ = FPJ == 1 ? 0 : (FPJ == 2 ? 1 : (FPJ == 4 ? 2 : (FPJ == 8 ? 3 : 4)));
@@ -51,6 +52,8 @@ struct Shape {
   static constexpr int FPC = CHUNK / 512;              // fragments per chunk
   static constexpr int V = CHUNK / 64;                 // consecutive elements per lane after transpose
   static constexpr int TBUF = CHUNK + CHUNK / 8;       // padded chunk buffer (floats)
+  static constexpr bool BIT5 = (F == 12) || LOGM >= 6; // bit 5 inside the row
+  static constexpr bool BIT6 = (F == 12) || LOGM >= 7; // bit 6 inside the row
   static constexpr bool BIT7 = (F == 12) || LOGM >= 8; // bit 7 inside the row
   static constexpr bool BIT8 = (F == 12) || LOGM >= 9; // bit 8 inside the row
   // loads of the next unit overlap this unit's work when the registers allow it
@@ -124,7 +127,9 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     }
     sign_tab[k] = m;
   }
-  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  // stage-1 operand: H32 over element bits 0-4, or I2 (x) H16 for 16-wide rows (bit 4 = row)
+  const bf16x8 hb[2] = {LOGM == 4 ? h16_operand(lane, 0) : h32_operand(lane, 0),
+                        LOGM == 4 ? h16_operand(lane, 1) : h32_operand(lane, 1)};
   __syncthreads();
   float run_max = 0.0f;
   float gts = 0.0f, inv6g = 0.0f;
@@ -160,15 +165,19 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     if constexpr (S::PREFETCH) load_unit<S>(x, u + ustride, units, a.rows, lane, raw);
 
     // ---------------- butterflies on register bits ----------------
-    // bits 5, 6: register index i
+    // bits 5, 6: register index i (bit 5 = i & 1, bit 6 = i >> 1), where they lie inside the row
 #pragma unroll
     for (int f = 0; f < S::NF; ++f)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        bfly(v[f][t][0], v[f][t][1]);
-        bfly(v[f][t][2], v[f][t][3]);
-        bfly(v[f][t][0], v[f][t][2]);
-        bfly(v[f][t][1], v[f][t][3]);
+        if constexpr (S::BIT5) {
+          bfly(v[f][t][0], v[f][t][1]);
+          bfly(v[f][t][2], v[f][t][3]);
+        }
+        if constexpr (S::BIT6) {
+          bfly(v[f][t][0], v[f][t][2]);
+          bfly(v[f][t][1], v[f][t][3]);
+        }
       }
     // bits 9.. inside each power-of-two sub-row: fragment index
 #pragma unroll
@@ -229,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     //   j = 512 f + 128 i + 32 (lane >> 4) + 2 (lane & 15) + t
     // 256-wide rows (bit 8 = row):  j = 256 (lane >> 5) + 128 (i & 1) + 64 (i >> 1) + 32 ((lane >> 4) & 1) + 2 (lane & 15) + t
     // 128-wide rows (bits 7-8 = row): j = 128 (lane >> 4) + 32 i + 2 (lane & 15) + t
+    //   (the same for 64-, 32- and 16-wide rows, whose bits 6.., 5.. and 4.. select the row)
 
     if constexpr (OP == OP_AMAX) {
 #pragma unroll
@@ -418,6 +428,9 @@ hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
 template <int OP>
 hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
   switch (a.n) {
+    case 16: return launch_one<1, 4, OP>(a, s);
+    case 32: return launch_one<1, 5, OP>(a, s);
+    case 64: return launch_one<1, 6, OP>(a, s);
     case 128: return launch_one<1, 7, OP>(a, s);
     case 256: return launch_one<1, 8, OP>(a, s);
     case 512: return launch_one<1, 9, OP>(a, s);

@@ -315,6 +315,23 @@ def test_wide_rows_many_per_workgroup(R, n):
             print(C.check_nvfp4(p_rows, s_rows, float(ts.item()), y_ref, np.float32(amax / 2688.0)))
 
 
+@pytest.mark.parametrize("n", [16, 32, 64])
+def test_narrow_rows_ragged_units(R, n):
+    """16-, 32- and 64-wide rows share a 512-element wave unit (32, 16 or 8 rows); 4099 rows
+    leave a partial last unit.  Every row against the oracle, every format."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["kv_128_int4g128"], n=n, tokens=4099)
+    say(f"narrow rows n={n} tokens={w.tokens}")
+    x, s = generate(w, dev())
+    y_ref = O.rotate(x.cpu(), s)
+    C.check_rotation(to_np(R.rhtq_rotate(x, s)), y_ref)
+    for fmt, group, sd in [("int4", 0, "f16"), ("int4", 16, "f32"), ("nvfp4", 16, "e4m3"), ("mxfp4", 32, "e8m0")]:
+        if fmt == "mxfp4" and n < 32:
+            continue
+        say(f"narrow rows n={n} {fmt} group={group}")
+        print(check_forward(R, x, s, fmt, group, sd, y_ref=y_ref))
+
+
 def test_nvfp4_given_tensor_scale(R):
     import torch
     w = WORKLOADS["nvfp4_4096"].with_tokens(77)
