@@ -45,17 +45,23 @@ struct Shape {
   static constexpr int UNIT = N >= 512 ? N : 512;      // elements per wave iteration
   static constexpr int RPU = UNIT / N;                 // rows per unit (1, 2, 4, 8, 16 or 32)
   static constexpr int NF = UNIT / 512;                // MFMA fragments per unit
-  static constexpr int FPJ = (F == 12) ? M / 512 : NF; // fragments per power-of-two sub-row
+  // fragments per power-of-two sub-row (for 12 x 256 a sub-row is half a fragment: 1, no
+  // fragment-bit butterflies)
+  static constexpr int FPJ = (F == 12) ? (M >= 512 ? M / 512 : 1) : NF;
   static constexpr int LOG_FPJ = FPJ == 1 ? 0 : (FPJ == 2 ? 1 : (FPJ == 4 ? 2 : (FPJ == 8 ? 3 : 4)));
   static constexpr int CHUNK = M >= 1024 ? 1024 : 512; // epilogue transpose unit
   static constexpr int NCH = UNIT / CHUNK;
   static constexpr int FPC = CHUNK / 512;              // fragments per chunk
   static constexpr int V = CHUNK / 64;                 // consecutive elements per lane after transpose
   static constexpr int TBUF = CHUNK + CHUNK / 8;       // padded chunk buffer (floats)
-  static constexpr bool BIT5 = (F == 12) || LOGM >= 6; // bit 5 inside the row
-  static constexpr bool BIT6 = (F == 12) || LOGM >= 7; // bit 6 inside the row
-  static constexpr bool BIT7 = (F == 12) || LOGM >= 8; // bit 7 inside the row
-  static constexpr bool BIT8 = (F == 12) || LOGM >= 9; // bit 8 inside the row
+  static constexpr bool BIT5 = (F == 12) || LOGM >= 6; // bit 5 inside the power-of-two sub-row
+  static constexpr bool BIT6 = (F == 12) || LOGM >= 7; // bit 6 inside the power-of-two sub-row
+  static constexpr bool BIT7 = (F == 12) || LOGM >= 8; // bit 7 inside the power-of-two sub-row
+  static constexpr bool BIT8 = LOGM >= 9;              // bit 8 inside the power-of-two sub-row
+  // 12 x 256: bit 8 is the low bit of the order-12 index j1, so it is brought into registers
+  // without a butterfly and the order-12 factor runs after the lane swaps
+  static constexpr bool H12_LATE = (F == 12) && LOGM == 8;
+  static constexpr bool SWAP8 = BIT8 || H12_LATE;
   // loads of the next unit overlap this unit's work when the registers allow it
   static constexpr bool PREFETCH = NF <= 8;
 };
@@ -189,8 +195,8 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
           for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) bfly(v[f][t][i], v[f + (1 << b)][t][i]);
-    // order-12 factor across the twelve sub-rows
-    if constexpr (F == 12) {
+    // order-12 factor across the twelve sub-rows (whole fragments each)
+    if constexpr (F == 12 && !S::H12_LATE) {
 #pragma unroll
       for (int fl = 0; fl < S::FPJ; ++fl)
 #pragma unroll
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
             bfly(v[f][t][i], v[f][t][i + 1]);
           }
     }
-    if constexpr (S::BIT8) {
+    if constexpr (S::SWAP8) {
 #pragma unroll
       for (int f = 0; f < S::NF; ++f)
 #pragma unroll
@@ -231,8 +237,22 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
                                                       __float_as_uint(v[f][t][i + 2]), false, false);
             v[f][t][i] = __uint_as_float(p[0]);
             v[f][t][i + 2] = __uint_as_float(p[1]);
-            bfly(v[f][t][i], v[f][t][i + 2]);
+            if constexpr (S::BIT8) bfly(v[f][t][i], v[f][t][i + 2]);
           }
+    }
+    // 12 x 256: j = 256 j1 + j2 with j1 = 2 f + (element bit 8 = register bit i >> 1)
+    if constexpr (S::H12_LATE) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i0 = 0; i0 < 2; ++i0) {
+          float w[12];
+#pragma unroll
+          for (int j1 = 0; j1 < 12; ++j1) w[j1] = v[j1 >> 1][t][i0 | ((j1 & 1) << 1)];
+          h12_forward(w);
+#pragma unroll
+          for (int j1 = 0; j1 < 12; ++j1) v[j1 >> 1][t][i0 | ((j1 & 1) << 1)] = w[j1];
+        }
     }
     // Element held by (f, t, i) at this lane, within the unit (rows >= 512 wide):
     //   j = 512 f + 128 i + 32 (lane >> 4) + 2 (lane & 15) + t
@@ -438,6 +458,7 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
     case 2048: return launch_one<1, 11, OP>(a, s);
     case 4096: return launch_one<1, 12, OP>(a, s);
     case 8192: return launch_one<1, 13, OP>(a, s);
+    case 3072: return launch_one<12, 8, OP>(a, s);
     case 6144: return launch_one<12, 9, OP>(a, s);
     default: return hipErrorNotSupported;
   }
