@@ -458,7 +458,8 @@ def test_inverse_kv_rows(R, n):
 
 
 BLOCKED = [(4096, 128), (4096, 1024), (12288, 1024), (12288, 4096), (256, 128), (2048, 16), (8192, 2048),
-           (1024, 512), (11008, 128), (11008, 256), (5120, 1024), (384, 128)]
+           (1024, 512), (11008, 128), (11008, 256), (5120, 1024), (384, 128), (4096, 64), (384, 32),
+           (8192, 32), (16384, 8192)]
 
 
 @pytest.mark.parametrize("n,block", BLOCKED)
