@@ -18,7 +18,7 @@
 //     (K = a, N = a'), a +-1 operand held in registers.  K slot e of lane group g stands for
 //     a = 32 ks + 8 g + e.  Wave w owns the output tiles a' in [16 t, 16 t + 16),
 //     t = w, w + 4, w + 8 (11 tiles, 172 padded to 176).  Result D1[b][a']: lane l holds
-//     a' = 16 t + (l & 15) and b = 16 mt + 4 (l >> 4) + i in tile mt, register i.
+//     a' = 16 t + (l & 15) (t the tile) and b = 16 mt + 4 (l >> 4) + i in tile mt, register i.
 //  3. Stage 2, H64 = H2 (x) H32 over b: index bit 5 (mt >> 1) is a register butterfly, the
 //     other five bits one v_mfma_f32_16x16x32_f16 with A = H32 (M = b''_lo, K = b_lo) and
 //     B = the butterflied values, whose registers already are that B layout (slot e of lane
@@ -41,8 +41,16 @@
 namespace rhtq {
 namespace {
 
-constexpr int kW = 4;
+// Waves per workgroup.  Four (tiles 3, 3, 3, 2) beat eleven (one tile each, 94-100 VGPRs): every
+// wave reads the row's A fragments from LDS for its own tiles, so eleven waves read 2.75 times
+// the LDS bytes per row, and LDS bandwidth, not latency, then limits the kernel.
+#ifndef RHTQ_172_WAVES
+#define RHTQ_172_WAVES 4
+#endif
+constexpr int kTiles = 11;                       // 16-wide a'-tiles: 172 padded to 176
+constexpr int kW = RHTQ_172_WAVES;               // waves per workgroup: wave w owns tiles w, w + kW, ..
 constexpr int kT = 64 * kW;
+constexpr int kNT = (kTiles + kW - 1) / kW;      // tiles of the busiest wave
 constexpr int kN = 11008;                        // 172 x 64
 constexpr int kPitch = 528;                      // LDS bytes per b-row: 192 bf16, shift, pad
 constexpr int kXBytes = 64 * kPitch;
@@ -111,7 +119,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand(lane, wave + 4 * j, ks);
+    for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand(lane, wave + kW * j, ks);
   const f16x8 ha[2] = {h32_b_operand(lane, 0), h32_b_operand(lane, 1)};
 
   float gts = 0.0f, inv6g = 0.0f;
@@ -134,9 +142,8 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   int64_t row = blockIdx.x;
   load(row);
 
-  // this thread's chunks c = tid + 256 k hold a = (tid >> 3) + 32 k (a >> 3 = wave + 4 k) and
-  // b = 8 (tid & 7) + e
-  uint8_t* wbase = xs + xrow(8 * (tid & 7)) + 16 * wave + 2 * ((tid >> 3) & 7);
+  // this thread's chunks c = tid + kT k hold a = (tid >> 3) + (kT / 8) k and b = 8 (tid & 7) + e
+  uint8_t* wbase = xs + xrow(8 * (tid & 7)) + 2 * (tid >> 3);
   // fragment (ks, mt) of this lane: row b = 16 mt + n, a = 32 ks + 8 g .. + 7
   const uint8_t* rbase_l[4];
 #pragma unroll
@@ -151,7 +158,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
         const uint32_t w[4] = {raw[k].x ^ m.x, raw[k].y ^ m.y, raw[k].z ^ m.z, raw[k].w ^ m.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(wbase + e * kPitch + 64 * k) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          *reinterpret_cast<uint16_t*>(wbase + e * kPitch + (kT / 4) * k) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
       }
     }
   };
@@ -259,7 +266,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int ap = 16 * (wave + 4 * j) + n;
+      const int ap = 16 * (wave + kW * j) + n;
       const bool valid = ap < 172;
       const float invS = invS_t[j];
       const auto& d2 = d2a[j];
@@ -398,7 +405,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 }
 
 template <int OP, int GC, int SD>
-__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fast172_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 : 4))) void fast172_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
   __shared__ uint4 sgn[kChunks];
   __shared__ float wmax[kW];
@@ -415,8 +422,13 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fa
     sgn[c] = m;
   }
   for (int c = tid; c < kXBytes / 16; c += kT) reinterpret_cast<uint4*>(xs)[c] = make_uint4(0, 0, 0, 0);   // a >= 172 stays 0
-  if ((tid >> 6) < 3) rows172<OP, GC, SD, 3>(a, xs, sgn, wmax);
-  else rows172<OP, GC, SD, 2>(a, xs, sgn, wmax);
+  // waves with a tile fewer than the busiest (kTiles not a multiple of kW) take the smaller copy
+  if constexpr (kTiles % kW == 0) {
+    rows172<OP, GC, SD, kNT>(a, xs, sgn, wmax);
+  } else {
+    if ((tid >> 6) < kTiles % kW) rows172<OP, GC, SD, kNT>(a, xs, sgn, wmax);
+    else rows172<OP, GC, SD, kNT - 1>(a, xs, sgn, wmax);
+  }
 }
 
 template <int OP, int GC, int SD>
