@@ -41,6 +41,13 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python randomized_hadamard_rotation_amd/build.py`")
+    # torch ships its own HIP runtime: load it first, so that the library binds to that runtime
+    # rather than starting a second one from /opt/rocm (kernels enqueued on torch's streams from
+    # another runtime fail to launch)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
     ci = ctypes.c_int

@@ -16,6 +16,7 @@ from workloads import WORKLOADS, generate, special_rows, splitmix64_signs
 
 pytestmark = pytest.mark.gpu
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tiny_128_int4.txt")
 
 
@@ -330,6 +331,29 @@ def test_narrow_rows_ragged_units(R, n):
             continue
         say(f"narrow rows n={n} {fmt} group={group}")
         print(check_forward(R, x, s, fmt, group, sd, y_ref=y_ref))
+
+
+def test_package_imported_before_torch():
+    """A fresh process that imports the package before torch still launches on torch's
+    runtime and stream, and gets the same bytes as this process."""
+    import subprocess
+    import torch
+    import randomized_hadamard_rotation_amd as R
+    say("package imported before torch, in a subprocess")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import randomized_hadamard_rotation_amd as R\n"
+            "import torch\n"
+            "from workloads import WORKLOADS, generate\n"
+            "x, s = generate(WORKLOADS['llama_4096_int4'].with_tokens(33), 'cuda')\n"
+            "p, sc, _ = R.rhtq_forward(x, s, fmt='int4')\n"
+            "torch.cuda.synchronize()\n"
+            "print(int(p.to(torch.int64).sum()), float(sc.double().sum()))\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    x, s = generate(WORKLOADS["llama_4096_int4"].with_tokens(33), dev())
+    p, sc, _ = R.rhtq_forward(x, s, fmt="int4")
+    torch.cuda.synchronize()
+    assert r.stdout.split()[-2:] == [str(int(p.to(torch.int64).sum())), str(float(sc.double().sum()))]
 
 
 def test_nvfp4_given_tensor_scale(R):
