@@ -15,9 +15,10 @@
 //     adds 8 * 64 to output 0 of each block only (the columns of H64 sum to zero except the first),
 //     which one subtraction removes.
 //  3. Index bits 6.. (128: one, 256: two) are int32 butterflies between registers.
-//  4. fp32 conversion, multiplication by scale / sqrt(n), the random signs by XOR of fp32 sign bits
-//     held in registers (a lane always serves the same columns), and 16-byte stores: each wave
-//     store covers 256 contiguous bytes per row.
+//  4. fp32 conversion, multiplication by scale / sqrt(n) (the scales are loaded with the codes, so
+//     no load follows a store in a wave step and the stores never wait), the random signs by XOR
+//     of fp32 sign bits held in registers (a lane always serves the same columns), and 16-byte
+//     stores: each wave store covers 256 contiguous bytes per row.
 #include <hip/hip_fp16.h>
 
 #include "rhtq.h"
@@ -51,7 +52,9 @@ __device__ __forceinline__ i32x4 h64_i8_operand(int lane, int tau) {
   return r;
 }
 
-template <int L>
+// SD: scale storage (RHTQ_SCALE_F32 / F16), a template parameter so that the scale loads of a
+// wave step carry no branch and issue together with the codes
+template <int L, int SD>
 __global__ __launch_bounds__(kThreadsI) void inv_kv_kernel(KernelArgs a) {
   constexpr int N = 1 << L;
   constexpr int HB = L - 6;                 // index bits above the 64-block: 0, 1 or 2
@@ -81,6 +84,17 @@ __global__ __launch_bounds__(kThreadsI) void inv_kv_kernel(KernelArgs a) {
   const int64_t units = (a.rows + RPU - 1) / RPU;
   for (int64_t u = (int64_t)blockIdx.x * kWavesI + wave; u < units; u += (int64_t)gridDim.x * kWavesI) {
     const int64_t row0 = u * RPU;
+    // scales of the rows this lane stores, issued first and together with the codes: a load issued
+    // after this unit's stores would wait for them (the memory counter is in order), once per row
+    constexpr int RL = 4 >> HB;                // rows per lane: output rows (4 g + i) >> HB, i = 0..3
+    float rs[RL];
+#pragma unroll
+    for (int k = 0; k < RL; ++k) {
+      int64_t rr = row0 + ((4 * g) >> HB) + k;
+      rr = rr < a.rows ? rr : a.rows - 1;      // in bounds; rows past the end are not stored
+      if constexpr (SD == RHTQ_SCALE_F32) rs[k] = static_cast<const float*>(a.in_scales)[rr] * cnorm;
+      else rs[k] = __half2float(static_cast<const __half*>(a.in_scales)[rr]) * cnorm;
+    }
     u32x2 c = {0x88888888u, 0x88888888u};   // codes of absent rows: q = -8 (never stored)
     if (row0 + lrow < a.rows)
       c = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.in_packed + row0 * (N / 2) + load_off));
@@ -116,15 +130,18 @@ __global__ __launch_bounds__(kThreadsI) void inv_kv_kernel(KernelArgs a) {
             d[tau][i | (1 << b)] = s0 - s1;
           }
 
+    // the scales have arrived before the first store: a wait for them between the stores would
+    // also wait for the stores already issued
+    if constexpr (RL == 1) asm volatile("" ::"v"(rs[0]) : "memory");
+    else if constexpr (RL == 2) asm volatile("" ::"v"(rs[0]), "v"(rs[1]) : "memory");
+    else asm volatile("" ::"v"(rs[0]), "v"(rs[1]), "v"(rs[2]), "v"(rs[3]) : "memory");
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (4 * g + i) >> HB;       // row within the step
       const int hi = (4 * g + i) & ((1 << HB) - 1);
       const int64_t row = row0 + r;
       if (row >= a.rows) continue;
-      const float s = (a.scale_dtype == RHTQ_SCALE_F32 ? static_cast<const float*>(a.in_scales)[row]
-                                                       : __half2float(static_cast<const __half*>(a.in_scales)[row])) *
-                      cnorm;
+      const float s = rs[i >> HB];
       float o[4];
 #pragma unroll
       for (int tau = 0; tau < 4; ++tau) o[tau] = __uint_as_float(__float_as_uint((float)d[tau][i] * s) ^ smask[hi][tau]);
@@ -133,9 +150,9 @@ __global__ __launch_bounds__(kThreadsI) void inv_kv_kernel(KernelArgs a) {
   }
 }
 
-template <int L>
+template <int L, int SD>
 hipError_t launch_inv(const KernelArgs& a, hipStream_t s) {
-  auto kern = inv_kv_kernel<L>;
+  auto kern = inv_kv_kernel<L, SD>;
   static const int max_blocks = resident_blocks((const void*)kern, kThreadsI, 0);
   constexpr int RPU = kUnit / (1 << L);
   const int64_t units = (a.rows + RPU - 1) / RPU;
@@ -150,10 +167,11 @@ hipError_t launch_inv(const KernelArgs& a, hipStream_t s) {
 hipError_t launch_inverse_fast(const KernelArgs& a, hipStream_t s) {
   if (a.inv_fmt != RHTQ_FMT_INT4 || a.group != a.n || a.sign_period != a.n) return hipErrorNotSupported;
   if (reinterpret_cast<uintptr_t>(a.in_packed) & 7) return hipErrorNotSupported;
+  const bool f32 = a.scale_dtype == RHTQ_SCALE_F32;
   switch (a.n) {
-    case 64: return launch_inv<6>(a, s);
-    case 128: return launch_inv<7>(a, s);
-    case 256: return launch_inv<8>(a, s);
+    case 64: return f32 ? launch_inv<6, RHTQ_SCALE_F32>(a, s) : launch_inv<6, RHTQ_SCALE_F16>(a, s);
+    case 128: return f32 ? launch_inv<7, RHTQ_SCALE_F32>(a, s) : launch_inv<7, RHTQ_SCALE_F16>(a, s);
+    case 256: return f32 ? launch_inv<8, RHTQ_SCALE_F32>(a, s) : launch_inv<8, RHTQ_SCALE_F16>(a, s);
     default: return hipErrorNotSupported;
   }
 }
