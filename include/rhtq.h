@@ -74,6 +74,9 @@ extern "C" {
 #define RHTQ_EINVAL       1   /* bad argument: null pointer, negative size, alignment */
 #define RHTQ_EUNSUPPORTED 2   /* valid but unsupported width / format / group combo */
 #define RHTQ_EHIP         3   /* a HIP runtime call failed while enqueueing         */
+/* The environment variable RHTQ_TEST_FAIL_LAUNCH=1 (read once per process) makes every entry point
+   return RHTQ_EHIP where it would first call HIP, after all argument checks, having enqueued
+   nothing: a test hook for the launch-error path. */
 
 /* Input element types. */
 #define RHTQ_IN_BF16 0

@@ -105,6 +105,7 @@ int rotate_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t 
   a.signs = signs;
   a.group = a.n;
   a.y = y_out;
+  if (rhtq::getenv_test_fail_launch()) return RHTQ_EHIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (in_dtype == RHTQ_IN_BF16) {
     hipError_t e = rhtq::launch_fast(rhtq::OP_ROTATE, a, s);
@@ -139,6 +140,7 @@ int forward_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t
   a.packed = packed_out;
   a.scales = scales_out;
   a.tensor_scale = tensor_scale;
+  if (rhtq::getenv_test_fail_launch()) return RHTQ_EHIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   auto run = [&](int op) -> hipError_t {
@@ -181,6 +183,7 @@ int inverse_impl(const uint8_t* packed, const void* scales, const float* tensor_
   a.in_scales = scales;
   a.in_tensor_scale = tensor_scale;
   a.inv_fmt = fmt;
+  if (rhtq::getenv_test_fail_launch()) return RHTQ_EHIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!rhtq::getenv_fast_disabled()) {
     const hipError_t e = rhtq::launch_inverse_fast(a, s);

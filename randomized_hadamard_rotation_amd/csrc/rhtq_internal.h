@@ -71,6 +71,17 @@ inline bool getenv_fast_disabled() {
   return v;
 }
 
+// RHTQ_TEST_FAIL_LAUNCH=1 makes every entry point stop where it would first call HIP, after all
+// argument checks, and report a runtime error: the launch-error path, testable without a failing
+// launch (read once).
+inline bool getenv_test_fail_launch() {
+  static const bool v = [] {
+    const char* e = getenv("RHTQ_TEST_FAIL_LAUNCH");
+    return e != nullptr && e[0] == '1';
+  }();
+  return v;
+}
+
 // RHTQ_DISABLE_FAST2=1 keeps 1024..4096-wide rows on the single-stage kernel (read once).
 inline bool getenv_fast2_disabled() {
   static const bool v = [] {

@@ -356,6 +356,46 @@ def test_package_imported_before_torch():
     assert r.stdout.split()[-2:] == [str(int(p.to(torch.int64).sum())), str(float(sc.double().sum()))]
 
 
+def test_forced_launch_failure_reports_and_writes_nothing():
+    """RHTQ_TEST_FAIL_LAUNCH=1 (fresh process): every entry point passes its argument checks,
+    reports RHTQ_EHIP where it would launch, and leaves the outputs as they were; a bad argument
+    still reports RHTQ_EINVAL first."""
+    import subprocess
+    say("forced launch failure, in a subprocess")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import torch\n"
+            "import randomized_hadamard_rotation_amd as R\n"
+            "x = torch.ones(8, 4096, dtype=torch.bfloat16, device='cuda')\n"
+            "p = torch.full((8, 2048), 0xA5, dtype=torch.uint8, device='cuda')\n"
+            "sc = torch.full((8, 1), 3.0, dtype=torch.float32, device='cuda')\n"
+            "y = torch.full((8, 4096), 7.0, dtype=torch.float32, device='cuda')\n"
+            "st = []\n"
+            "for f in (lambda: R.rhtq_forward(x, None, fmt='int4', packed=p, scales=sc),\n"
+            "          lambda: R.rhtq_rotate(x, None, out=y),\n"
+            "          lambda: R.rhtq_inverse(p, sc, 4096, None, fmt='int4', out=y)):\n"
+            "    try:\n"
+            "        f(); st.append(0)\n"
+            "    except R.RhtqError as e:\n"
+            "        st.append(e.status)\n"
+            "try:\n"
+            "    R.rhtq_forward(x[:, :4000], None, fmt='int4'); st.append(0)\n"
+            "except R.RhtqError as e:\n"
+            "    st.append(e.status)\n"
+            "except ValueError:\n"
+            "    st.append(-1)\n"
+            "torch.cuda.synchronize()\n"
+            "ok = bool((p == 0xA5).all()) and bool((sc == 3.0).all()) and bool((y == 7.0).all())\n"
+            "print(st, ok)\n") % ROOT
+    env = dict(os.environ, RHTQ_TEST_FAIL_LAUNCH="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0, r.stderr[-2000:]
+    statuses, ok = r.stdout.strip().splitlines()[-1].rsplit(" ", 1)
+    st = [int(v) for v in statuses.strip("[]").split(",")]
+    assert st[:3] == [3, 3, 3], r.stdout
+    assert st[3] != 3, r.stdout   # rejected before the hook (unsupported width or bad argument)
+    assert ok == "True", r.stdout
+
+
 def test_nvfp4_given_tensor_scale(R):
     import torch
     w = WORKLOADS["nvfp4_4096"].with_tokens(77)
