@@ -103,13 +103,17 @@ def run_timed(torch, step, steps, warmup, graph):
     return timed(g.replay), ms_eager
 
 
-def time_workload(R, torch, name, steps, warmup, graph=True, given=False):
+def time_workload(R, torch, name, steps, warmup, graph=True, given=False, sha=False):
     """given=True (NVFP4 only): the tensor scale is the caller's (read, not computed), so one
     launch per step; it is set from one dynamic call on the same input before timing."""
     from workloads import WORKLOADS, bytes_per_call, generate
     w = WORKLOADS[name]
     assert not given or w.fmt == "nvfp4"
     x0, signs = generate(w, "cuda")
+    input_sha = None
+    if sha:
+        from workloads import sha256_of
+        input_sha = sha256_of(x0)
     nbytes = bytes_per_call(w, tensor_scale_dynamic=not given)
     sets = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / nbytes)))
     xs = [x0] + [x0.clone() for _ in range(sets - 1)]
@@ -144,6 +148,7 @@ def time_workload(R, torch, name, steps, warmup, graph=True, given=False):
         "rows_per_s": w.tokens / (ms * 1e-3), "bytes_per_call": nbytes, "achieved_gbs": gbs,
         "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
         "launches_per_step": 3 if w.fmt == "nvfp4" and not given else 1,
+        **({"input_sha256": input_sha} if input_sha else {}),
     }
 
 
@@ -334,7 +339,7 @@ def main():
         return
 
     graph = not args.no_graph
-    head = time_workload(R, torch, args.workload, args.steps, args.warmup, graph, given=args.given)
+    head = time_workload(R, torch, args.workload, args.steps, args.warmup, graph, given=args.given, sha=True)
     also = []
     if not args.only:
         for name in OTHERS:
@@ -365,7 +370,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": head["tokens"], "n": head["n"],
                    "in_dtype": head["in_dtype"], "fmt": head["fmt"], "group": head["group"],
-                   "scale_dtype": head["scale_dtype"], "buffer_sets": head["buffer_sets"]},
+                   "scale_dtype": head["scale_dtype"], "buffer_sets": head["buffer_sets"],
+                   "input_sha256": head["input_sha256"]},
         "hbm_gbs": head["achieved_gbs"],
         "launch": head["launch"],
         "eager_ms_per_step": head["eager_ms_per_step"],
