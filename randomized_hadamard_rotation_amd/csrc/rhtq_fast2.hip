@@ -261,9 +261,10 @@ void fast2_kernel(KernelArgs a) {
 // its partial sums for output chunks with bit 10 = h, sends the others through LDS, and both
 // sides go to the smaller of the two split scales (powers of two, exact).  Wave h then owns
 // the output chunks 1024 (2 h' + h) + [0, 1024), h' = 0, 1.  Per-row INT4 takes the row
-// maximum over both waves through LDS.  The sign masks are built once per workgroup in LDS
-// (shared by its rows).  Pairs past the last row repeat the last row (identical bytes), so all
-// pairs of a workgroup always pass the same barriers.
+// maximum over both waves through LDS.  Each lane loads its 32 signs from L2 together with
+// its row fragments and turns them into sign-bit masks itself, so no workgroup table or
+// barrier stands before the row loads.  Pairs past the last row repeat the last row
+// (identical bytes), so all pairs of a workgroup always pass the same barriers.
 // ---------------------------------------------------------------------------
 #ifndef RHTQ_PAIR_WAVES
 #define RHTQ_PAIR_WAVES 4
@@ -280,18 +281,27 @@ struct PairShared {
 };
 
 // Wave H's half of one row (H a template parameter so every register array is indexed by
-// constants).  sign_tab: [sign period / N][8 fragments][64 lanes] masks, as fast2_kernel.
+// constants).
 template <int OP, int H>
-__device__ __forceinline__ void pair_row(const KernelArgs& a, const uint4* sign_tab, PairShared& sh, int64_t row) {
+__device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, int64_t row) {
   constexpr int N = 4096, NF = 8;
   const int lane = threadIdx.x & 63;
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)N));
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const int lcol = 32 * (lane & 15) + 8 * (lane >> 4);   // this lane's 8 elements within a fragment
 
+  // the row's fragments and this lane's 32 signs go out together: the signs come from L2 (every
+  // row shares them), and no workgroup table or barrier stands before the row loads
+  const int slices = a.sign_period / N;
+  const int slice = slices > 1 ? (int)(row % slices) : 0;
   uint4 raw[4];
 #pragma unroll
   for (int fl = 0; fl < 4; ++fl) raw[fl] = ld_stream(x + row * N + 512 * (4 * H + fl) + lcol);
+  uint2 sv[4] = {};
+  if (a.signs) {
+#pragma unroll
+    for (int fl = 0; fl < 4; ++fl) sv[fl] = *reinterpret_cast<const uint2*>(a.signs + N * slice + 512 * (4 * H + fl) + lcol);
+  }
   const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
   const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
   int G = 0;
@@ -301,14 +311,15 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, const uint4* sign_
   const int lc = (lane >> 4) | ((lane & 15) << 2);
 
   // ---------------- stage 1 (fragments 4 H .. 4 H + 3) ----------------
-  const int slices = a.sign_period / N;
-  const int slice = slices > 1 ? (int)(row % slices) : 0;
   float d1[4][2][4];
 #pragma unroll
   for (int fl = 0; fl < 4; ++fl) {
     uint4 r = raw[fl];
-    const uint4 m = sign_tab[(slice * NF + 4 * H + fl) * 64 + lane];
-    r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
+    // bf16 sign-bit masks of the lane's 8 elements: bit 15 / bit 31 of each pair from byte bit 7
+    r.x ^= __builtin_amdgcn_perm(0u, sv[fl].x, 0x010C000Cu) & 0x80008000u;
+    r.y ^= __builtin_amdgcn_perm(0u, sv[fl].x, 0x030C020Cu) & 0x80008000u;
+    r.z ^= __builtin_amdgcn_perm(0u, sv[fl].y, 0x010C000Cu) & 0x80008000u;
+    r.w ^= __builtin_amdgcn_perm(0u, sv[fl].y, 0x030C020Cu) & 0x80008000u;
     bf16x8 av;
     __builtin_memcpy(&av, &r, 16);
     const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -451,29 +462,12 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, const uint4* sign_
 
 template <int OP>
 __global__ __launch_bounds__(128 * kPairRows) __attribute__((amdgpu_waves_per_eu(RHTQ_PAIR_WAVES))) void fast2p_kernel(KernelArgs a) {
-  constexpr int N = 4096, NF = 8;
-  extern __shared__ uint4 sign_tab[];   // [sign period / N][NF][64]
   __shared__ PairShared sh[kPairRows];
-  const int slices = a.sign_period / N;
-  for (int k = threadIdx.x; k < slices * NF * 64; k += 128 * kPairRows) {
-    uint4 m = make_uint4(0, 0, 0, 0);
-    if (a.signs) {
-      const int kl = k & 63, kf = k >> 6;
-      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + N * (kf / NF) + 512 * (kf % NF) + 32 * (kl & 15) +
-                                                       8 * (kl >> 4));
-      m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
-      m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
-      m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
-      m.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
-    }
-    sign_tab[k] = m;
-  }
-  __syncthreads();
   const int wave = threadIdx.x >> 6, pair = wave >> 1;
   int64_t row = kPairRows * (int64_t)blockIdx.x + pair;
   if (row >= a.rows) row = a.rows - 1;   // past the end: repeat the last row (same bytes, same barriers)
-  if (wave & 1) pair_row<OP, 1>(a, sign_tab, sh[pair], row);
-  else pair_row<OP, 0>(a, sign_tab, sh[pair], row);
+  if (wave & 1) pair_row<OP, 1>(a, sh[pair], row);
+  else pair_row<OP, 0>(a, sh[pair], row);
 }
 
 template <int OP>
@@ -481,9 +475,8 @@ hipError_t launch2p(const KernelArgs& a, hipStream_t s) {
   if constexpr (OP == OP_INT4) {
     if (!(a.group == 4096 || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-  const size_t lds = (size_t)(a.sign_period / 4096) * 8 * 64 * 16;
-  if (lds > 32768 || a.rows > 0xFFFFFFFE) return hipErrorNotSupported;
-  hipLaunchKernelGGL(fast2p_kernel<OP>, dim3((unsigned)((a.rows + kPairRows - 1) / kPairRows)), dim3(128 * kPairRows), lds, s,
+  if (a.rows > 0xFFFFFFFE) return hipErrorNotSupported;
+  hipLaunchKernelGGL(fast2p_kernel<OP>, dim3((unsigned)((a.rows + kPairRows - 1) / kPairRows)), dim3(128 * kPairRows), 0, s,
                      a);
   return hipGetLastError();
 }
