@@ -253,7 +253,8 @@ void fast2_kernel(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Small row counts at n = 4096: two waves per row, four rows per workgroup.  With one wave per
+// Small row counts at n = 4096: two waves per row, one row per workgroup (the workgroup barrier
+// of the exchange then waits for the row's own two waves only).  With one wave per
 // row a SIMD holds only the few rows the call has and sits idle while they wait on their own
 // dependency chains; splitting each row doubles the waves and halves each chain.  Wave h takes
 // the row half j = 2048 h + [0, 2048) (fragments 4 h .. 4 h + 3): stages 1 and 2 and the
@@ -270,7 +271,7 @@ void fast2_kernel(KernelArgs a) {
 #define RHTQ_PAIR_WAVES 4
 #endif
 #ifndef RHTQ_PAIR_RPW
-#define RHTQ_PAIR_RPW 4
+#define RHTQ_PAIR_RPW 1
 #endif
 constexpr int kPairRows = RHTQ_PAIR_RPW;   // rows per workgroup (two waves each)
 
