@@ -316,6 +316,21 @@ def test_wide_rows_many_per_workgroup(R, n):
             print(C.check_nvfp4(p_rows, s_rows, float(ts.item()), y_ref, np.float32(amax / 2688.0)))
 
 
+@pytest.mark.parametrize("group", [0, 16, 32, 64, 128, 256, 512])
+def test_12288_every_int4_group(R, group):
+    """12288 = 12 x 1024 rows, every INT4 group the two-wave kernel takes (16 .. 512: the
+    group maxima run over 8 values per lane, lane swaps and 0-4 DPP steps) and per-token
+    scales (a row maximum across both waves).  Every row against the oracle, both scale
+    types."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["downproj_12288_int4g128"], tokens=67)
+    x, s = generate(w, dev())
+    y_ref = O.rotate(x.cpu(), s)
+    for sd in ("f32", "f16"):
+        say(f"12288 int4 group={group} scale={sd}")
+        print(check_forward(R, x, s, "int4", group, sd, y_ref=y_ref))
+
+
 @pytest.mark.parametrize("n", [16, 32, 64])
 def test_narrow_rows_ragged_units(R, n):
     """16-, 32- and 64-wide rows share a 512-element wave unit (32, 16 or 8 rows); 4099 rows
