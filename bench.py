@@ -322,7 +322,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: rows are independent, so the path shards "
-              "by rows with no exchange; multi-GPU runs are not part of this build.",
+              "by rows with no exchange, and this benchmark measures one GPU's share.",
               file=sys.stderr)
         sys.exit(2)
 
