@@ -40,6 +40,7 @@ OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_409
           "downproj7b_11008_int4g128"]
 KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_fast24.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast2.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast172.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fastw.hip",

@@ -256,29 +256,44 @@ __device__ __forceinline__ void split_scale(uint32_t mb, float& S, float& invS) 
 // v_fma_mixlo/mixhi_f16 so that each half costs one instruction and lo reads hi through
 // op_sel; the order keeps every half-register write at least one instruction away from
 // its reader, and the closing s_nop covers the VALU-write to matrix-core-read distance.
+// The compiler places no wait states ahead of an asm block, so where y comes straight from
+// a v_mfma result (no ordinary VALU instruction has read it first), AFTER_MFMA opens the
+// block with 12 of them: gfx950 needs 8 between a 16x16x32 result and a VALU read.
+#define RHTQ_SPLIT8_BODY                                                       \
+  "v_fma_mixlo_f16 %0, %8, %16, 0\n\t"                                        \
+  "v_fma_mixlo_f16 %1, %10, %16, 0\n\t"                                       \
+  "v_fma_mixlo_f16 %2, %12, %16, 0\n\t"                                       \
+  "v_fma_mixlo_f16 %3, %14, %16, 0\n\t"                                       \
+  "v_fma_mixhi_f16 %0, %9, %16, 0\n\t"                                        \
+  "v_fma_mixhi_f16 %1, %11, %16, 0\n\t"                                       \
+  "v_fma_mixhi_f16 %2, %13, %16, 0\n\t"                                       \
+  "v_fma_mixhi_f16 %3, %15, %16, 0\n\t"                                       \
+  "v_fma_mixlo_f16 %4, %8, %16, -%0 op_sel_hi:[0,0,1]\n\t"                    \
+  "v_fma_mixlo_f16 %5, %10, %16, -%1 op_sel_hi:[0,0,1]\n\t"                   \
+  "v_fma_mixlo_f16 %6, %12, %16, -%2 op_sel_hi:[0,0,1]\n\t"                   \
+  "v_fma_mixlo_f16 %7, %14, %16, -%3 op_sel_hi:[0,0,1]\n\t"                   \
+  "v_fma_mixhi_f16 %4, %9, %16, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"     \
+  "v_fma_mixhi_f16 %5, %11, %16, -%1 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"    \
+  "v_fma_mixhi_f16 %6, %13, %16, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"    \
+  "v_fma_mixhi_f16 %7, %15, %16, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"    \
+  "s_nop 1"
+template <bool AFTER_MFMA = false>
 __device__ __forceinline__ void split8(const float* y, float S, uint32_t* hi, uint32_t* lo) {
-  asm("v_fma_mixlo_f16 %0, %8, %16, 0\n\t"
-      "v_fma_mixlo_f16 %1, %10, %16, 0\n\t"
-      "v_fma_mixlo_f16 %2, %12, %16, 0\n\t"
-      "v_fma_mixlo_f16 %3, %14, %16, 0\n\t"
-      "v_fma_mixhi_f16 %0, %9, %16, 0\n\t"
-      "v_fma_mixhi_f16 %1, %11, %16, 0\n\t"
-      "v_fma_mixhi_f16 %2, %13, %16, 0\n\t"
-      "v_fma_mixhi_f16 %3, %15, %16, 0\n\t"
-      "v_fma_mixlo_f16 %4, %8, %16, -%0 op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixlo_f16 %5, %10, %16, -%1 op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixlo_f16 %6, %12, %16, -%2 op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixlo_f16 %7, %14, %16, -%3 op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %4, %9, %16, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %5, %11, %16, -%1 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %6, %13, %16, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %7, %15, %16, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
-      "s_nop 1"
-      : "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]),
-        "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3])
-      : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]),
-        "v"(S));
+  if constexpr (AFTER_MFMA) {
+    asm("s_nop 7\n\ts_nop 3\n\t" RHTQ_SPLIT8_BODY
+        : "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]),
+          "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3])
+        : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]),
+          "v"(S));
+  } else {
+    asm(RHTQ_SPLIT8_BODY
+        : "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]),
+          "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3])
+        : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]),
+          "v"(S));
+  }
 }
+#undef RHTQ_SPLIT8_BODY
 
 // E4M3FN (OCP FP8) code of s >= 0: nearest value, ties to even mantissa, saturating at
 // 448 (0x7E), subnormals kept; NaN never produced.  gfx950's conversion instruction does the

@@ -48,6 +48,9 @@ hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
 // Two-wave kernel for 12288-wide rows (called by launch_fast).
 hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s);
 
+// Four-wave kernel for 24576-wide rows, H12 (x) H2048 (called by launch_fast).
+hipError_t launch_fast24(int op, const KernelArgs& a, hipStream_t s);
+
 // Matrix-core kernel for 11008-wide rows, H172 (x) H64 (called by launch_fast).
 hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s);
 

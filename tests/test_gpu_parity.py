@@ -203,13 +203,18 @@ def test_workload_full_size_sampled(R, name):
 # put element 2^31 inside the tensor; the oracle checks the rows around it, the first and the last
 # (only those rows are copied to the host).
 BEYOND_INT32 = [("llama_4096_int4", 2 ** 19 + 5), ("mxfp4_4096", 2 ** 19 + 3), ("kv_128_int4g128", 2 ** 24 + 3),
-                ("downproj_12288_int4g128", 174763), ("downproj7b_11008_int4g128", 195085)]
+                ("downproj_12288_int4g128", 174763), ("downproj7b_11008_int4g128", 195085),
+                ("downproj_12288_int4g128:n=24576", 87385)]
 
 
 @pytest.mark.parametrize("name,tokens", BEYOND_INT32)
 def test_beyond_int32_elements(R, name, tokens):
+    import dataclasses
     import torch
-    w = WORKLOADS[name].with_tokens(tokens)
+    base, _, n = name.partition(":n=")
+    w = WORKLOADS[base].with_tokens(tokens)
+    if n:
+        w = dataclasses.replace(w, n=int(n))
     assert tokens * w.n > 2 ** 31
     say(f"{name} at {tokens} x {w.n} = {tokens * w.n} elements")
     x, s = generate(w, dev())
@@ -282,9 +287,9 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n", [8192, 16384, 11008, 12288])
+@pytest.mark.parametrize("n", [8192, 16384, 11008, 12288, 24576])
 def test_wide_rows_many_per_workgroup(R, n):
-    """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 12288 = 12 x 1024): 2503 rows,
+    """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 12288 = 12 x 1024, 24576 = 12 x 2048): 2503 rows,
     more than the resident workgroups, so every workgroup of the persistent kernel loops over
     several rows (per-token INT4 takes a barrier per row), and a count no grid divides.
     The oracle checks sampled rows (the dynamic NVFP4 tensor scale over all of them)."""
@@ -316,18 +321,19 @@ def test_wide_rows_many_per_workgroup(R, n):
             print(C.check_nvfp4(p_rows, s_rows, float(ts.item()), y_ref, np.float32(amax / 2688.0)))
 
 
+@pytest.mark.parametrize("n", [12288, 24576])
 @pytest.mark.parametrize("group", [0, 16, 32, 64, 128, 256, 512])
-def test_12288_every_int4_group(R, group):
-    """12288 = 12 x 1024 rows, every INT4 group the two-wave kernel takes (16 .. 512: the
-    group maxima run over 8 values per lane, lane swaps and 0-4 DPP steps) and per-token
-    scales (a row maximum across both waves).  Every row against the oracle, both scale
-    types."""
+def test_12m_every_int4_group(R, n, group):
+    """12288 = 12 x 1024 (two waves per row) and 24576 = 12 x 2048 (four waves per row), every
+    INT4 group their kernels take (16 .. 512: the group maxima run over 8 values per lane, lane
+    swaps and 0-4 DPP steps) and per-token scales (a row maximum across the waves).  Every
+    row against the oracle, both scale types."""
     import dataclasses
-    w = dataclasses.replace(WORKLOADS["downproj_12288_int4g128"], tokens=67)
+    w = dataclasses.replace(WORKLOADS["downproj_12288_int4g128"], n=n, tokens=67)
     x, s = generate(w, dev())
     y_ref = O.rotate(x.cpu(), s)
     for sd in ("f32", "f16"):
-        say(f"12288 int4 group={group} scale={sd}")
+        say(f"{n} int4 group={group} scale={sd}")
         print(check_forward(R, x, s, "int4", group, sd, y_ref=y_ref))
 
 
