@@ -7,9 +7,10 @@
 // commute.  The four waves of a workgroup share one row; wave h holds the sub-rows
 // j1 = 3h .. 3h + 2 (96 values per lane).  Per row:
 //
-//  1. 16-byte loads in the MFMA A layout, issued during the previous row's exchange; random
-//     signs by XOR of bf16 sign bits, the masks built per row from the lane's own 96 sign
-//     bits (three registers).
+//  1. 16-byte loads in the MFMA A layout, issued during the previous row's exchange (all
+//     three sub-rows for rotate, MXFP4 and the amax pass; one for INT4 and NVFP4, the rest at
+//     the top of the row); random signs by XOR of bf16 sign bits, the masks built per row from
+//     the lane's own 96 sign bits (three registers).
 //  2. Bits 0-4 of every 512-element fragment on v_mfma_f32_16x16x32_bf16.  The row's largest
 //     stage-1 value over all four waves (first barrier) sets one power-of-two split scale S;
 //     that pass keeps only the maximum, and each sub-row's stage 1 runs again before its split.
