@@ -48,7 +48,9 @@ KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_inverse_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_device.h",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_generic.hip",
-                  "randomized_hadamard_rotation_amd/csrc/rhtq_api.cpp"]
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_internal.h",
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_api.cpp",
+                  "include/rhtq.h"]
 
 
 def kernel_source_hash() -> str:

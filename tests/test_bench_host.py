@@ -49,6 +49,15 @@ def test_rocprof_summary_percentiles_and_counters(tmp_path, capsys):
     assert not any("other" in l for l in out)
 
 
+def test_kernel_hash_covers_every_source():
+    """Every file the library is built from enters the hash that ties stored counters to the
+    kernels they were taken on."""
+    csrc = os.path.join(ROOT, "randomized_hadamard_rotation_amd", "csrc")
+    built = {os.path.join("randomized_hadamard_rotation_amd", "csrc", f) for f in os.listdir(csrc)}
+    built.add(os.path.join("include", "rhtq.h"))
+    assert built <= set(bench.KERNEL_SOURCES)
+
+
 def test_traffic_is_null_when_sources_changed(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
@@ -58,6 +67,7 @@ def test_traffic_is_null_when_sources_changed(tmp_path, monkeypatch):
     (prof / "w_stale_traffic.json").write_text(json.dumps(stale))
     src = tmp_path / "randomized_hadamard_rotation_amd" / "csrc"
     src.mkdir(parents=True)
+    (tmp_path / "include").mkdir()
     for p in bench.KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             (tmp_path / p).write_bytes(f.read())
