@@ -1,6 +1,7 @@
 // Matrix-core kernel for bf16 rows of 11008 = 172 x 64 elements, the Llama 2 7B intermediate
 // width (QuaRot reviews, review 2 Questions: its non-power-of-two part 172 makes the rotation
-// costly).  Element j = 64 a + b (a < 172, b < 64) and
+// costly), and of 5504 = 172 x 32 taken two rows at a time (see rows172).  Element
+// j = 64 a + b (a < 172, b < 64) and
 //
 //     Y[a'][b''] = sum_a sum_b H172[a'][a] H64[b''][b] s[a][b] x[a][b] / sqrt(11008).
 //
@@ -105,14 +106,25 @@ __device__ __forceinline__ float col_max(float v) {
 // Maximum of two non-negative floats as unsigned bit patterns (no canonicalisation needed).
 __device__ __forceinline__ float nnmax(float a, float b) { return __uint_as_float(umax(__float_as_uint(a), __float_as_uint(b))); }
 
+// P: rows of 11008 / P = 172 x (64 / P) elements per 11008-element work row (1 or 2).  With
+// P = 2 two consecutive 5504-wide rows share a work row: b = 32 r + b' holds element 32 a + b'
+// of row r of the pair.  Stage 1 is per column b and unchanged; stage 2 drops the bit-5
+// butterfly (H1 (x) H32 instead of H2 (x) H32) and gives each row its own split scale; the
+// epilogue maps runs 0-1 to the first row of the pair and runs 2-3 to the second.
 // GC: group class, 0 (one INT4 group per row: the row maximum across the four waves through
 // LDS), 4 (16-element groups: one run), 5 (32: two runs), 6 (64..256: whole
 // a'-rows); SD: INT4 scale storage (RHTQ_SCALE_F32 / F16).
-template <int OP, int GC, int SD, int NT>
+template <int P, int OP, int GC, int SD, int NT>
 __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
+  static_assert(P == 1 || P == 2, "one or two rows per work row");
+  constexpr int kPn = kN / P;     // elements per row
+  constexpr int kM = 64 / P;      // b' per row (elements per a'-row)
+  constexpr int RPP = 4 / P;      // output runs of 16 per row
+  constexpr int LM = P == 1 ? 6 : 5;   // log2 kM
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
-  const float cnorm = (float)(1.0 / __builtin_sqrt((double)kN));
+  const float cnorm = (float)(1.0 / __builtin_sqrt((double)kPn));
+  const int64_t vrows = (a.rows + P - 1) / P;   // work rows
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
 
   bf16x8 hb[NT][6];
@@ -132,11 +144,21 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 
   uint4 raw[kLoads];
   auto load = [&](int64_t row) {
-    if (row >= a.rows) return;
+    if (row >= vrows) return;
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = tid + kT * k;
-      if (c < kChunks) raw[k] = ld_stream(x + row * kN + 8 * c);
+      if (c < kChunks) {
+        if constexpr (P == 1) {
+          raw[k] = ld_stream(x + row * kN + 8 * c);
+        } else {
+          // chunk c: a = c >> 3, b = 8 (c & 7) .. + 7 of the work row, i.e. row P row + b / kM
+          // of the call, elements kM a + b % kM; a row past the end reads as zeros
+          const int b0 = 8 * (c & 7);
+          const int64_t prow = row * P + b0 / kM;
+          raw[k] = prow < a.rows ? ld_stream(x + prow * kPn + kM * (c >> 3) + b0 % kM) : make_uint4(0, 0, 0, 0);
+        }
+      }
     }
   };
   int64_t row = blockIdx.x;
@@ -163,13 +185,13 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
     }
   };
   __syncthreads();   // sign masks and zeroed rows
-  if (row < a.rows) write_lds();
+  if (row < vrows) write_lds();
   load(row + gridDim.x);
   __syncthreads();
   // per row: stage 1 reads the row from LDS; after the barrier that ends those reads the next
   // row goes into LDS (its loads were issued one row earlier) and the loads of the row after
   // it are issued, then stage 2 and the epilogue of this row run from registers
-  for (; row < a.rows; row += gridDim.x) {
+  for (; row < vrows; row += gridDim.x) {
     // ---------------- stage 1: H172 over a ----------------
     f32x4 acc[NT][4];
 #pragma unroll
@@ -186,31 +208,55 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
         }
     }
     __syncthreads();   // every wave has read this row
-    if (row + gridDim.x < a.rows) write_lds();
+    if (row + gridDim.x < vrows) write_lds();
     load(row + 2 * (int64_t)gridDim.x);
 
-    const int64_t rbase = row * kN;
-    // ---------------- stage 2: H2 by butterfly, H32 on the matrix cores ----------------
+    // ---------------- stage 2: H2 by butterfly (P = 1), H32 on the matrix cores ----------------
     // (each step runs over all of this wave's tiles before the next, so that the tiles'
     // independent chains interleave)
-    float u[NT][2][2][4];   // [tile][hb][mt & 1][i], b_lo = 16 (mt & 1) + 4 g + i
-    float S[NT], invS_t[NT];
+    float u[NT][2][2][4];       // [tile][hb][mt & 1][i], b_lo = 16 (mt & 1) + 4 g + i
+    float S[NT][2], invS_t[NT][2];   // split scale of each half hb (one value for both when P = 1)
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      float m = 0.0f;
+      if constexpr (P == 1) {
+        float m = 0.0f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = acc[j][h][i], q = acc[j][h + 2][i];
-          u[j][0][h][i] = p + q;
-          u[j][1][h][i] = p - q;
-          m = fmaxf(m, fmaxf(fabsf(p + q), fabsf(p - q)));
+          for (int i = 0; i < 4; ++i) {
+            const float p = acc[j][h][i], q = acc[j][h + 2][i];
+            u[j][0][h][i] = p + q;
+            u[j][1][h][i] = p - q;
+            m = fmaxf(m, fmaxf(fabsf(p + q), fabsf(p - q)));
+          }
+        S[j][0] = m;
+      } else {
+        // half hb is row hb of the pair: no butterfly, a split scale of its own
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          float m = 0.0f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              u[j][hb][h][i] = acc[j][2 * hb + h][i];
+              m = fmaxf(m, fabsf(acc[j][2 * hb + h][i]));
+            }
+          S[j][hb] = m;
         }
-      S[j] = m;
+      }
     }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) split_scale(__float_as_uint(col_max(S[j])), S[j], invS_t[j]);
+    for (int j = 0; j < NT; ++j) {
+      if constexpr (P == 1) {
+        split_scale(__float_as_uint(col_max(S[j][0])), S[j][0], invS_t[j][0]);
+        S[j][1] = S[j][0];
+        invS_t[j][1] = invS_t[j][0];
+      } else {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) split_scale(__float_as_uint(col_max(S[j][hb])), S[j][hb], invS_t[j][hb]);
+      }
+    }
     float d2a[NT][4][4];   // [tile][run r = 2 hb + mt2][i]: b'' = 16 r + 4 g + i
 #pragma unroll
     for (int j = 0; j < NT; ++j)
@@ -220,7 +266,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
         for (int e = 0; e < 8; ++e) ys[e] = u[j][h][e >> 2][e & 3];
         uint32_t hw[4], lw[4];
-        split8(ys, S[j], hw, lw);
+        split8(ys, S[j][h], hw, lw);
         f16x8 bh, bl;
         __builtin_memcpy(&bh, hw, 16);
         __builtin_memcpy(&bl, lw, 16);
@@ -234,33 +280,40 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
         }
       }
 
-    // per-token INT4: one scale for the row, from the maximum over every tile of the four waves
+    // per-token INT4: one scale per row, from the maximum over every tile of the four waves
     // (columns a' >= 172 are zero); all waves pass this barrier, GC being uniform
-    float row_inv = 0.0f;
+    float row_inv[P] = {};
     bool row_clamp = false;
     if constexpr (OP == OP_INT4 && GC == 0) {
-      float m = 0.0f;
+      float m[P] = {};
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        float mj = 0.0f;
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r) {
+          float mj = 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) mj = fmaxf(mj, fabsf(d2a[j][r][i]));
-        m = nnmax(m, mj * invS_t[j]);
-      }
-      m = group_max(m, 64);
-      if (lane == 0) wmax[wave] = m;
-      __syncthreads();
-      float rm = wmax[0];
+          m[r / RPP] = nnmax(m[r / RPP], mj * invS_t[j][r >> 1]);
+        }
 #pragma unroll
-      for (int w = 1; w < kW; ++w) rm = nnmax(rm, wmax[w]);
-      const Int4Scale sc = int4_scale(rm, cnorm, SD);
-      row_inv = sc.inv;
-      row_clamp = sc.clamp;
-      if (tid == 0) {
-        if constexpr (SD == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[row] = sc.s;
-        else static_cast<__half*>(a.scales)[row] = __float2half_rn(fminf(sc.s, 65504.0f));
+      for (int hh = 0; hh < P; ++hh) {
+        m[hh] = group_max(m[hh], 64);
+        if (lane == 0) wmax[P * wave + hh] = m[hh];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int hh = 0; hh < P; ++hh) {
+        float rm = wmax[hh];
+#pragma unroll
+        for (int w = 1; w < kW; ++w) rm = nnmax(rm, wmax[P * w + hh]);
+        const Int4Scale sc = int4_scale(rm, cnorm, SD);
+        row_inv[hh] = sc.inv;
+        row_clamp |= sc.clamp;
+        const int64_t prow = row * P + hh;
+        if (tid == 0 && prow < a.rows) {
+          if constexpr (SD == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[prow] = sc.s;
+          else static_cast<__half*>(a.scales)[prow] = __float2half_rn(fminf(sc.s, 65504.0f));
+        }
       }
     }
 
@@ -268,14 +321,16 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
     for (int j = 0; j < NT; ++j) {
       const int ap = 16 * (wave + kW * j) + n;
       const bool valid = ap < 172;
-      const float invS = invS_t[j];
       const auto& d2 = d2a[j];
-      const int64_t ebase = rbase + 64 * ap + 4 * g;   // element of run 0, i = 0
+      // run r: row P row + r / RPP of the call, its elements rstart(r) + 4 g + i
+      auto prow_of = [&](int r) -> int64_t { return row * P + r / RPP; };
+      auto rstart = [&](int r) -> int64_t { return prow_of(r) * kPn + kM * ap + 16 * (r % RPP); };
+      auto rvalid = [&](int r) -> bool { return valid && (P == 1 || prow_of(r) < a.rows); };
       if constexpr (OP == OP_ROTATE) {
-        if (valid) {
-          const float f = invS * cnorm;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) st_stream(a.y + ebase + 16 * r, d2[r][0] * f, d2[r][1] * f, d2[r][2] * f, d2[r][3] * f);
+        for (int r = 0; r < 4; ++r) {
+          const float f = invS_t[j][r >> 1] * cnorm;
+          if (rvalid(r)) st_stream(a.y + rstart(r) + 4 * g, d2[r][0] * f, d2[r][1] * f, d2[r][2] * f, d2[r][3] * f);
         }
         continue;
       }
@@ -284,7 +339,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       for (int r = 0; r < 4; ++r)
         mr[r] = fmaxf(fmaxf(fabsf(d2[r][0]), fabsf(d2[r][1])), fmaxf(fabsf(d2[r][2]), fabsf(d2[r][3])));
       if constexpr (OP == OP_AMAX) {
-        run_max = nnmax(run_max, nnmax(nnmax(mr[0], mr[1]), nnmax(mr[2], mr[3])) * invS);
+        run_max = nnmax(run_max, nnmax(nnmax(mr[0], mr[1]) * invS_t[j][0], nnmax(mr[2], mr[3]) * invS_t[j][1]));
         continue;
       }
 
@@ -292,7 +347,8 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       // sl[r]: factor from split units to code units for run r (0 for an all-zero group)
       float sl[4];
       bool clamp = false;
-      auto scale_of = [&](float bm, int64_t gi, bool writer) -> float {   // bm: true units, before 1/sqrt(n)
+      // bm: true units, before 1/sqrt(n); invS: the split units of the runs the factor is for
+      auto scale_of = [&](float bm, int64_t gi, bool writer, float invS) -> float {
         if constexpr (OP == OP_INT4) {
           const Int4Scale sc = int4_scale(bm, cnorm, SD);
           clamp |= sc.clamp;
@@ -313,24 +369,38 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
           return bt > 0.0f ? __builtin_ldexpf(invS * cnorm, -ex) : 0.0f;
         }
       };
-      const int64_t e0 = rbase + 64 * ap;   // first element of this lane's a'-row
-      if constexpr (GC == 0) {   // the row's scale, in this tile's split units
-        sl[0] = sl[1] = sl[2] = sl[3] = row_inv * invS;
+      if constexpr (GC == 0) {   // the row's scale, in the runs' split units
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sl[r] = row_inv[r / RPP] * invS_t[j][r >> 1];
         clamp = row_clamp;
       } else if constexpr (GC == 4) {   // a run per group; lane group g stores the scale of run g
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sl[r] = scale_of(col_max(mr[r]) * invS, (e0 + 16 * r) >> 4, valid && g == r);
+        for (int r = 0; r < 4; ++r)
+          sl[r] = scale_of(col_max(mr[r]) * invS_t[j][r >> 1], rstart(r) >> 4, rvalid(r) && g == r, invS_t[j][r >> 1]);
       } else if constexpr (GC == 5) {   // two runs per group; lane groups 0 and 1 store
-        const float s0 = scale_of(col_max(nnmax(mr[0], mr[1])) * invS, e0 >> 5, valid && g == 0);
-        const float s1 = scale_of(col_max(nnmax(mr[2], mr[3])) * invS, (e0 + 32) >> 5, valid && g == 1);
+        const float s0 = scale_of(col_max(nnmax(mr[0], mr[1])) * invS_t[j][0], rstart(0) >> 5, rvalid(0) && g == 0,
+                                  invS_t[j][0]);
+        const float s1 = scale_of(col_max(nnmax(mr[2], mr[3])) * invS_t[j][1], rstart(2) >> 5, rvalid(2) && g == 1,
+                                  invS_t[j][1]);
         sl[0] = sl[1] = s0;
         sl[2] = sl[3] = s1;
-      } else {   // 1, 2 or 4 whole a'-rows per group; lane group 0 of the group's first a' stores
-        float mm = col_max(nnmax(nnmax(mr[0], mr[1]), nnmax(mr[2], mr[3]))) * invS;
+      } else if constexpr (P == 1) {   // 1, 2 or 4 whole a'-rows per group; lane group 0 of the group's first a' stores
+        float mm = col_max(nnmax(nnmax(mr[0], mr[1]), nnmax(mr[2], mr[3]))) * invS_t[j][0];
         if (LG >= 7) mm = dpp_max<0xB1>(mm);   // a' pairs (lane xor 1)
         if (LG >= 8) mm = dpp_max<0x4E>(mm);   // a' quads (lane xor 2)
-        const float s0 = scale_of(mm, e0 >> LG, valid && g == 0 && (ap & ((1 << (LG - 6)) - 1)) == 0);
+        const float s0 = scale_of(mm, rstart(0) >> LG, valid && g == 0 && (ap & ((1 << (LG - 6)) - 1)) == 0,
+                                  invS_t[j][0]);
         sl[0] = sl[1] = sl[2] = sl[3] = s0;
+      } else {   // P = 2: 2 or 4 whole 32-element a'-rows of one row per group
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float mm = col_max(nnmax(mr[2 * hh], mr[2 * hh + 1])) * invS_t[j][hh];
+          mm = dpp_max<0xB1>(mm);                 // a' pairs (lane xor 1)
+          if (LG >= 7) mm = dpp_max<0x4E>(mm);    // a' quads (lane xor 2)
+          const float sh = scale_of(mm, rstart(2 * hh) >> LG,
+                                    rvalid(2 * hh) && g == 0 && (ap & ((1 << (LG - LM)) - 1)) == 0, invS_t[j][hh]);
+          sl[2 * hh] = sl[2 * hh + 1] = sh;
+        }
       }
 
       // ---------------- codes: runs 0,1 -> p01, runs 2,3 -> p23 (run in 16-bit halves) ----------------
@@ -386,7 +456,11 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       const uint32_t send2 = upper ? w0 : w1;
       auto pr2 = __builtin_amdgcn_permlane32_swap(send2, send2, false, false);
       const uint32_t recv2 = upper ? pr2[0] : pr2[1];
-      if (valid) st_stream(a.packed + ((rbase + 64 * ap) >> 1) + 8 * g, upper ? recv2 : w0, upper ? w1 : recv2);
+      // lane group g: bytes 8 g .. 8 g + 7 of the work row's 32-byte a'-row, i.e. of row P row + g / (4 / P)
+      const int rg = g / (4 / P);
+      if (rvalid(RPP * rg))
+        st_stream(a.packed + ((prow_of(RPP * rg) * kPn + kM * ap) >> 1) + 8 * (g % (4 / P)), upper ? recv2 : w0,
+                  upper ? w1 : recv2);
     }
     __syncthreads();   // the next row is in LDS
   }
@@ -404,16 +478,19 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   }
 }
 
-template <int OP, int GC, int SD>
+template <int P, int OP, int GC, int SD>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 : 4))) void fast172_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
   __shared__ uint4 sgn[kChunks];
-  __shared__ float wmax[kW];
+  __shared__ float wmax[kW * P];
   const int tid = threadIdx.x;
   for (int c = tid; c < kChunks; c += kT) {
     uint4 m = make_uint4(0, 0, 0, 0);
     if (a.signs) {
-      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + 8 * c);
+      // chunk c of the work row: elements kM a + b % kM of one row of the pair (rows share the signs)
+      constexpr int kM = 64 / P;
+      const int b0 = 8 * (c & 7);
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + kM * (c >> 3) + b0 % kM);
       m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
       m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
       m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
@@ -424,29 +501,45 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 
   for (int c = tid; c < kXBytes / 16; c += kT) reinterpret_cast<uint4*>(xs)[c] = make_uint4(0, 0, 0, 0);   // a >= 172 stays 0
   // waves with a tile fewer than the busiest (kTiles not a multiple of kW) take the smaller copy
   if constexpr (kTiles % kW == 0) {
-    rows172<OP, GC, SD, kNT>(a, xs, sgn, wmax);
+    rows172<P, OP, GC, SD, kNT>(a, xs, sgn, wmax);
   } else {
-    if ((tid >> 6) < kTiles % kW) rows172<OP, GC, SD, kNT>(a, xs, sgn, wmax);
-    else rows172<OP, GC, SD, kNT - 1>(a, xs, sgn, wmax);
+    if ((tid >> 6) < kTiles % kW) rows172<P, OP, GC, SD, kNT>(a, xs, sgn, wmax);
+    else rows172<P, OP, GC, SD, kNT - 1>(a, xs, sgn, wmax);
   }
 }
 
-template <int OP, int GC, int SD>
+template <int P, int OP, int GC, int SD>
 hipError_t launch172(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast172_kernel<OP, GC, SD>;
+  auto kern = fast172_kernel<P, OP, GC, SD>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
-  const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
+  const int64_t vrows = (a.rows + P - 1) / P;
+  const int grid = (int)(vrows < max_blocks ? vrows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int SD>
+template <int P, int SD>
 hipError_t launch172_int4(const KernelArgs& a, hipStream_t s) {
+  if (a.group == kN / P) return launch172<P, OP_INT4, 0, SD>(a, s);   // one group per row
   switch (a.group) {
-    case 16: return launch172<OP_INT4, 4, SD>(a, s);
-    case 32: return launch172<OP_INT4, 5, SD>(a, s);
-    case 64: case 128: case 256: return launch172<OP_INT4, 6, SD>(a, s);
-    case kN: return launch172<OP_INT4, 0, SD>(a, s);   // one group per row
+    case 16: return launch172<P, OP_INT4, 4, SD>(a, s);
+    case 32: return launch172<P, OP_INT4, 5, SD>(a, s);
+    case 64: case 128: return launch172<P, OP_INT4, 6, SD>(a, s);
+    case 256: return P == 1 ? launch172<P, OP_INT4, 6, SD>(a, s) : hipErrorNotSupported;
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <int P>
+hipError_t launch172_p(int op, const KernelArgs& a, hipStream_t s) {
+  switch (op) {
+    case OP_ROTATE: return launch172<P, OP_ROTATE, 6, 0>(a, s);
+    case OP_INT4:
+      return a.scale_dtype == RHTQ_SCALE_F32 ? launch172_int4<P, RHTQ_SCALE_F32>(a, s)
+                                             : launch172_int4<P, RHTQ_SCALE_F16>(a, s);
+    case OP_NVFP4: return launch172<P, OP_NVFP4, 4, 0>(a, s);
+    case OP_MXFP4: return launch172<P, OP_MXFP4, 5, 0>(a, s);
+    case OP_AMAX: return launch172<P, OP_AMAX, 6, 0>(a, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -454,17 +547,11 @@ hipError_t launch172_int4(const KernelArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s) {
-  if (a.n != kN || a.sign_period != kN) return hipErrorNotSupported;
   if (reinterpret_cast<uintptr_t>(a.x) & 15) return hipErrorNotSupported;
-  switch (op) {
-    case OP_ROTATE: return launch172<OP_ROTATE, 6, 0>(a, s);
-    case OP_INT4:
-      return a.scale_dtype == RHTQ_SCALE_F32 ? launch172_int4<RHTQ_SCALE_F32>(a, s) : launch172_int4<RHTQ_SCALE_F16>(a, s);
-    case OP_NVFP4: return launch172<OP_NVFP4, 4, 0>(a, s);
-    case OP_MXFP4: return launch172<OP_MXFP4, 5, 0>(a, s);
-    case OP_AMAX: return launch172<OP_AMAX, 6, 0>(a, s);
-    default: return hipErrorNotSupported;
-  }
+  if (a.n == kN && a.sign_period == kN) return launch172_p<1>(op, a, s);
+  // 5504 = 172 x 32, two rows per work row
+  if (a.n == kN / 2 && a.sign_period == kN / 2) return launch172_p<2>(op, a, s);
+  return hipErrorNotSupported;
 }
 
 }  // namespace rhtq

@@ -115,7 +115,8 @@ def test_e2_exact_example(R):
 
 
 @pytest.mark.parametrize("n,k", [(16, 3), (128, 77), (4096, 1234), (12288, 7000), (3072, 2049),
-                                 (16384, 9999), (24576, 123), (11008, 9000), (2752, 43), (22016, 21999)])
+                                 (16384, 9999), (24576, 123), (11008, 9000), (5504, 4321), (2752, 43),
+                                 (22016, 21999)])
 def test_e3_closed_form(R, n, k):
     say(f"E3 n={n} k={k}")
     import torch
@@ -287,9 +288,10 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n", [8192, 16384, 11008, 12288, 24576])
+@pytest.mark.parametrize("n", [8192, 16384, 11008, 5504, 12288, 24576])
 def test_wide_rows_many_per_workgroup(R, n):
-    """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 12288 = 12 x 1024, 24576 = 12 x 2048): 2503 rows,
+    """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 5504 = 172 x 32 two rows at a time,
+    12288 = 12 x 1024, 24576 = 12 x 2048): 2503 rows (for 5504 the last pair holds one row),
     more than the resident workgroups, so every workgroup of the persistent kernel loops over
     several rows (per-token INT4 takes a barrier per row), and a count no grid divides.
     The oracle checks sampled rows (the dynamic NVFP4 tensor scale over all of them)."""
@@ -321,13 +323,17 @@ def test_wide_rows_many_per_workgroup(R, n):
             print(C.check_nvfp4(p_rows, s_rows, float(ts.item()), y_ref, np.float32(amax / 2688.0)))
 
 
-@pytest.mark.parametrize("n", [12288, 24576])
-@pytest.mark.parametrize("group", [0, 16, 32, 64, 128, 256, 512])
-def test_12m_every_int4_group(R, n, group):
-    """12288 = 12 x 1024 (two waves per row) and 24576 = 12 x 2048 (four waves per row), every
-    INT4 group their kernels take (16 .. 512: the group maxima run over 8 values per lane, lane
-    swaps and 0-4 DPP steps) and per-token scales (a row maximum across the waves).  Every
-    row against the oracle, both scale types."""
+INT4_GROUPS = ([(n, g) for n in (12288, 24576) for g in (0, 16, 32, 64, 128, 256, 512)]
+               + [(11008, g) for g in (0, 16, 32, 64, 128, 256)] + [(5504, g) for g in (0, 16, 32, 64, 128)])
+
+
+@pytest.mark.parametrize("n,group", INT4_GROUPS)
+def test_wide_every_int4_group(R, n, group):
+    """Every INT4 group the wide kernels take, and per-token scales (a row maximum across the
+    waves): 12288 = 12 x 1024 (two waves per row) and 24576 = 12 x 2048 (four), groups 16 .. 512
+    from 8 values per lane, lane swaps and 0-4 DPP steps; 11008 = 172 x 64 and 5504 = 172 x 32
+    (two rows per work row), groups of runs, a'-rows and a'-row pairs or quads.  Every row
+    against the oracle, both scale types."""
     import dataclasses
     w = dataclasses.replace(WORKLOADS["downproj_12288_int4g128"], n=n, tokens=67)
     x, s = generate(w, dev())
