@@ -295,6 +295,32 @@ __device__ __forceinline__ void split8(const float* y, float S, uint32_t* hi, ui
 }
 #undef RHTQ_SPLIT8_BODY
 
+// split8 with a scale of its own for each half: elements 0-3 under S0, elements 4-7 under S1
+// (words 0-1 and 2-3 of hi / lo), for eight values drawn from two independent rows.
+__device__ __forceinline__ void split8x2(const float* y, float S0, float S1, uint32_t* hi, uint32_t* lo) {
+  asm("v_fma_mixlo_f16 %0, %8, %16, 0\n\t"
+      "v_fma_mixlo_f16 %1, %10, %16, 0\n\t"
+      "v_fma_mixlo_f16 %2, %12, %17, 0\n\t"
+      "v_fma_mixlo_f16 %3, %14, %17, 0\n\t"
+      "v_fma_mixhi_f16 %0, %9, %16, 0\n\t"
+      "v_fma_mixhi_f16 %1, %11, %16, 0\n\t"
+      "v_fma_mixhi_f16 %2, %13, %17, 0\n\t"
+      "v_fma_mixhi_f16 %3, %15, %17, 0\n\t"
+      "v_fma_mixlo_f16 %4, %8, %16, -%0 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %5, %10, %16, -%1 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %6, %12, %17, -%2 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %7, %14, %17, -%3 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %4, %9, %16, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %5, %11, %16, -%1 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %6, %13, %17, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %7, %15, %17, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]),
+        "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3])
+      : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]),
+        "v"(S0), "v"(S1));
+}
+
 // E4M3FN (OCP FP8) code of s >= 0: nearest value, ties to even mantissa, saturating at
 // 448 (0x7E), subnormals kept; NaN never produced.  gfx950's conversion instruction does the
 // rounding; the input is clamped to 448 first so nothing overflows.  Checked on the device

@@ -470,7 +470,7 @@ hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s) {
   if (getenv_fast_disabled()) return hipErrorNotSupported;
   if (a.n == 12288) return launch_fast12(op, a, s);
   if (a.n == 24576) return launch_fast24(op, a, s);
-  if (a.n == 11008 || a.n == 5504) return launch_fast172(op, a, s);
+  if (a.n == 11008 || a.n == 5504 || a.n == 2752) return launch_fast172(op, a, s);
   if (a.n == 8192 || a.n == 16384) {
     const hipError_t e = launch_fastw(op, a, s);
     if (e != hipErrorNotSupported) return e;

@@ -1,6 +1,7 @@
 // Matrix-core kernel for bf16 rows of 11008 = 172 x 64 elements, the Llama 2 7B intermediate
 // width (QuaRot reviews, review 2 Questions: its non-power-of-two part 172 makes the rotation
-// costly), and of 5504 = 172 x 32 taken two rows at a time (see rows172).  Element
+// costly), and of 5504 = 172 x 32 and 2752 = 172 x 16 taken two and four rows at a time (see
+// rows172).  Element
 // j = 64 a + b (a < 172, b < 64) and
 //
 //     Y[a'][b''] = sum_a sum_b H172[a'][a] H64[b''][b] s[a][b] x[a][b] / sqrt(11008).
@@ -80,14 +81,16 @@ __device__ bf16x8 h172t_operand(int lane, int t, int ks) {
 }
 
 // Stage-2 A operand for M-tile mt2: row m = lane & 15 stands for b''_lo = 16 mt2 + m, slot e
-// of lane group g for b_lo = 16 (e >> 2) + 4 g + (e & 3); entry H32[b''_lo][b_lo] as f16.
+// of lane group g for b_lo = 16 (e >> 2) + 4 g + (e & 3); entry H32[b''_lo][b_lo] as f16, or with
+// I2 == true the block-diagonal I2 (x) H16 (zero where bit 4 of b''_lo and b_lo differ).
+template <bool I2 = false>
 __device__ f16x8 h32_b_operand(int lane, int mt2) {
   const int m = 16 * mt2 + (lane & 15), g = lane >> 4;
   uint16_t bits[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int k = 16 * (e >> 2) + 4 * g + (e & 3);
-    bits[e] = (__builtin_popcount(m & k) & 1) ? 0xBC00 : 0x3C00;
+    bits[e] = (I2 && ((m ^ k) & 16)) ? 0 : ((__builtin_popcount(m & k & (I2 ? 15 : 31)) & 1) ? 0xBC00 : 0x3C00);
   }
   f16x8 r;
   __builtin_memcpy(&r, bits, 16);
@@ -106,21 +109,24 @@ __device__ __forceinline__ float col_max(float v) {
 // Maximum of two non-negative floats as unsigned bit patterns (no canonicalisation needed).
 __device__ __forceinline__ float nnmax(float a, float b) { return __uint_as_float(umax(__float_as_uint(a), __float_as_uint(b))); }
 
-// P: rows of 11008 / P = 172 x (64 / P) elements per 11008-element work row (1 or 2).  With
-// P = 2 two consecutive 5504-wide rows share a work row: b = 32 r + b' holds element 32 a + b'
-// of row r of the pair.  Stage 1 is per column b and unchanged; stage 2 drops the bit-5
-// butterfly (H1 (x) H32 instead of H2 (x) H32) and gives each row its own split scale; the
-// epilogue maps runs 0-1 to the first row of the pair and runs 2-3 to the second.
+// P: rows of 11008 / P = 172 x (64 / P) elements per 11008-element work row (1, 2 or 4).  With
+// P > 1, P consecutive rows share a work row: b = (64 / P) r + b' holds element (64 / P) a + b'
+// of row r of the set.  Stage 1 is per column b and unchanged.  Stage 2 drops the bit-5 butterfly
+// (H1 (x) H32 for P = 2) and, for P = 4, also splits the matrix-core product into I2 (x) H16; every
+// row gets its own split scale.  The epilogue maps output run r (16 b'' values) to row
+// r / (4 / P) of the set.
 // GC: group class, 0 (one INT4 group per row: the row maximum across the four waves through
 // LDS), 4 (16-element groups: one run), 5 (32: two runs), 6 (64..256: whole
 // a'-rows); SD: INT4 scale storage (RHTQ_SCALE_F32 / F16).
 template <int P, int OP, int GC, int SD, int NT>
 __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
-  static_assert(P == 1 || P == 2, "one or two rows per work row");
+  static_assert(P == 1 || P == 2 || P == 4, "one, two or four rows per work row");
   constexpr int kPn = kN / P;     // elements per row
   constexpr int kM = 64 / P;      // b' per row (elements per a'-row)
   constexpr int RPP = 4 / P;      // output runs of 16 per row
-  constexpr int LM = P == 1 ? 6 : 5;   // log2 kM
+  constexpr int LM = P == 1 ? 6 : (P == 2 ? 5 : 4);   // log2 kM
+  // split scale of run r: one per work row (P = 1), per half (P = 2) or per run (P = 4)
+  auto sidx = [](int r) { return P == 1 ? 0 : (P == 2 ? (r >> 1) : r); };
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)kPn));
@@ -132,7 +138,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand(lane, wave + kW * j, ks);
-  const f16x8 ha[2] = {h32_b_operand(lane, 0), h32_b_operand(lane, 1)};
+  const f16x8 ha[2] = {h32_b_operand<P == 4>(lane, 0), h32_b_operand<P == 4>(lane, 1)};
 
   float gts = 0.0f, inv6g = 0.0f;
   if constexpr (OP == OP_NVFP4) {
@@ -215,7 +221,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
     // (each step runs over all of this wave's tiles before the next, so that the tiles'
     // independent chains interleave)
     float u[NT][2][2][4];       // [tile][hb][mt & 1][i], b_lo = 16 (mt & 1) + 4 g + i
-    float S[NT][2], invS_t[NT][2];   // split scale of each half hb (one value for both when P = 1)
+    float S[NT][4], invS_t[NT][4];   // split scale of run group sidx(r)
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       if constexpr (P == 1) {
@@ -230,7 +236,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
             m = fmaxf(m, fmaxf(fabsf(p + q), fabsf(p - q)));
           }
         S[j][0] = m;
-      } else {
+      } else if constexpr (P == 2) {
         // half hb is row hb of the pair: no butterfly, a split scale of its own
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -244,17 +250,29 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
             }
           S[j][hb] = m;
         }
+      } else {
+        // M-tile 2 hb + h is row 2 hb + h of the set, with a split scale of its own
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              u[j][hb][h][i] = acc[j][2 * hb + h][i];
+              m = fmaxf(m, fabsf(acc[j][2 * hb + h][i]));
+            }
+            S[j][2 * hb + h] = m;
+          }
       }
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       if constexpr (P == 1) {
         split_scale(__float_as_uint(col_max(S[j][0])), S[j][0], invS_t[j][0]);
-        S[j][1] = S[j][0];
-        invS_t[j][1] = invS_t[j][0];
       } else {
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) split_scale(__float_as_uint(col_max(S[j][hb])), S[j][hb], invS_t[j][hb]);
+        for (int q = 0; q < P; ++q) split_scale(__float_as_uint(col_max(S[j][q])), S[j][q], invS_t[j][q]);
       }
     }
     float d2a[NT][4][4];   // [tile][run r = 2 hb + mt2][i]: b'' = 16 r + 4 g + i
@@ -266,7 +284,8 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
         for (int e = 0; e < 8; ++e) ys[e] = u[j][h][e >> 2][e & 3];
         uint32_t hw[4], lw[4];
-        split8(ys, S[j][h], hw, lw);
+        if constexpr (P == 4) split8x2(ys, S[j][2 * h], S[j][2 * h + 1], hw, lw);
+        else split8(ys, S[j][sidx(2 * h)], hw, lw);
         f16x8 bh, bl;
         __builtin_memcpy(&bh, hw, 16);
         __builtin_memcpy(&bl, lw, 16);
@@ -293,7 +312,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
           float mj = 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) mj = fmaxf(mj, fabsf(d2a[j][r][i]));
-          m[r / RPP] = nnmax(m[r / RPP], mj * invS_t[j][r >> 1]);
+          m[r / RPP] = nnmax(m[r / RPP], mj * invS_t[j][sidx(r)]);
         }
 #pragma unroll
       for (int hh = 0; hh < P; ++hh) {
@@ -329,7 +348,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       if constexpr (OP == OP_ROTATE) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float f = invS_t[j][r >> 1] * cnorm;
+          const float f = invS_t[j][sidx(r)] * cnorm;
           if (rvalid(r)) st_stream(a.y + rstart(r) + 4 * g, d2[r][0] * f, d2[r][1] * f, d2[r][2] * f, d2[r][3] * f);
         }
         continue;
@@ -339,7 +358,8 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       for (int r = 0; r < 4; ++r)
         mr[r] = fmaxf(fmaxf(fabsf(d2[r][0]), fabsf(d2[r][1])), fmaxf(fabsf(d2[r][2]), fabsf(d2[r][3])));
       if constexpr (OP == OP_AMAX) {
-        run_max = nnmax(run_max, nnmax(nnmax(mr[0], mr[1]) * invS_t[j][0], nnmax(mr[2], mr[3]) * invS_t[j][1]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) run_max = nnmax(run_max, mr[r] * invS_t[j][sidx(r)]);
         continue;
       }
 
@@ -371,17 +391,26 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       };
       if constexpr (GC == 0) {   // the row's scale, in the runs' split units
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sl[r] = row_inv[r / RPP] * invS_t[j][r >> 1];
+        for (int r = 0; r < 4; ++r) sl[r] = row_inv[r / RPP] * invS_t[j][sidx(r)];
         clamp = row_clamp;
       } else if constexpr (GC == 4) {   // a run per group; lane group g stores the scale of run g
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          sl[r] = scale_of(col_max(mr[r]) * invS_t[j][r >> 1], rstart(r) >> 4, rvalid(r) && g == r, invS_t[j][r >> 1]);
+          sl[r] = scale_of(col_max(mr[r]) * invS_t[j][sidx(r)], rstart(r) >> 4, rvalid(r) && g == r, invS_t[j][sidx(r)]);
+      } else if constexpr (P == 4) {   // 2 or 4 whole 16-element a'-rows of one row; lane group r stores for run r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float mm = col_max(mr[r]) * invS_t[j][r];
+          mm = dpp_max<0xB1>(mm);                 // a' pairs (lane xor 1)
+          if (LG >= 6) mm = dpp_max<0x4E>(mm);    // a' quads (lane xor 2)
+          sl[r] = scale_of(mm, rstart(r) >> LG, rvalid(r) && g == r && (ap & ((1 << (LG - LM)) - 1)) == 0,
+                           invS_t[j][r]);
+        }
       } else if constexpr (GC == 5) {   // two runs per group; lane groups 0 and 1 store
-        const float s0 = scale_of(col_max(nnmax(mr[0], mr[1])) * invS_t[j][0], rstart(0) >> 5, rvalid(0) && g == 0,
-                                  invS_t[j][0]);
-        const float s1 = scale_of(col_max(nnmax(mr[2], mr[3])) * invS_t[j][1], rstart(2) >> 5, rvalid(2) && g == 1,
-                                  invS_t[j][1]);
+        const float s0 = scale_of(col_max(nnmax(mr[0], mr[1])) * invS_t[j][sidx(0)], rstart(0) >> 5,
+                                  rvalid(0) && g == 0, invS_t[j][sidx(0)]);
+        const float s1 = scale_of(col_max(nnmax(mr[2], mr[3])) * invS_t[j][sidx(2)], rstart(2) >> 5,
+                                  rvalid(2) && g == 1, invS_t[j][sidx(2)]);
         sl[0] = sl[1] = s0;
         sl[2] = sl[3] = s1;
       } else if constexpr (P == 1) {   // 1, 2 or 4 whole a'-rows per group; lane group 0 of the group's first a' stores
@@ -394,11 +423,12 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
       } else {   // P = 2: 2 or 4 whole 32-element a'-rows of one row per group
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          float mm = col_max(nnmax(mr[2 * hh], mr[2 * hh + 1])) * invS_t[j][hh];
+          float mm = col_max(nnmax(mr[2 * hh], mr[2 * hh + 1])) * invS_t[j][sidx(2 * hh)];
           mm = dpp_max<0xB1>(mm);                 // a' pairs (lane xor 1)
           if (LG >= 7) mm = dpp_max<0x4E>(mm);    // a' quads (lane xor 2)
           const float sh = scale_of(mm, rstart(2 * hh) >> LG,
-                                    rvalid(2 * hh) && g == 0 && (ap & ((1 << (LG - LM)) - 1)) == 0, invS_t[j][hh]);
+                                    rvalid(2 * hh) && g == 0 && (ap & ((1 << (LG - LM)) - 1)) == 0,
+                                    invS_t[j][sidx(2 * hh)]);
           sl[2 * hh] = sl[2 * hh + 1] = sh;
         }
       }
@@ -524,7 +554,8 @@ hipError_t launch172_int4(const KernelArgs& a, hipStream_t s) {
   switch (a.group) {
     case 16: return launch172<P, OP_INT4, 4, SD>(a, s);
     case 32: return launch172<P, OP_INT4, 5, SD>(a, s);
-    case 64: case 128: return launch172<P, OP_INT4, 6, SD>(a, s);
+    case 64: return launch172<P, OP_INT4, 6, SD>(a, s);
+    case 128: return P <= 2 ? launch172<P, OP_INT4, 6, SD>(a, s) : hipErrorNotSupported;
     case 256: return P == 1 ? launch172<P, OP_INT4, 6, SD>(a, s) : hipErrorNotSupported;
     default: return hipErrorNotSupported;
   }
@@ -549,8 +580,9 @@ hipError_t launch172_p(int op, const KernelArgs& a, hipStream_t s) {
 hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s) {
   if (reinterpret_cast<uintptr_t>(a.x) & 15) return hipErrorNotSupported;
   if (a.n == kN && a.sign_period == kN) return launch172_p<1>(op, a, s);
-  // 5504 = 172 x 32, two rows per work row
+  // 5504 = 172 x 32 and 2752 = 172 x 16: two and four rows per work row
   if (a.n == kN / 2 && a.sign_period == kN / 2) return launch172_p<2>(op, a, s);
+  if (a.n == kN / 4 && a.sign_period == kN / 4) return launch172_p<4>(op, a, s);
   return hipErrorNotSupported;
 }
 

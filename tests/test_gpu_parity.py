@@ -288,10 +288,11 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n", [8192, 16384, 11008, 5504, 12288, 24576])
+@pytest.mark.parametrize("n", [8192, 16384, 11008, 5504, 2752, 12288, 24576])
 def test_wide_rows_many_per_workgroup(R, n):
-    """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 5504 = 172 x 32 two rows at a time,
-    12288 = 12 x 1024, 24576 = 12 x 2048): 2503 rows (for 5504 the last pair holds one row),
+    """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 5504 and 2752 = 172 x 32 and 16 two
+    and four rows at a time, 12288 = 12 x 1024, 24576 = 12 x 2048): 2503 rows (the last set of
+    5504 or 2752 rows is partial),
     more than the resident workgroups, so every workgroup of the persistent kernel loops over
     several rows (per-token INT4 takes a barrier per row), and a count no grid divides.
     The oracle checks sampled rows (the dynamic NVFP4 tensor scale over all of them)."""
@@ -307,7 +308,8 @@ def test_wide_rows_many_per_workgroup(R, n):
     torch.cuda.synchronize()
     C.check_rotation(to_np(y[rows_t]), y_ref)
     del y
-    for fmt, group, sd in [("int4", 0, "f32"), ("int4", 128, "f16"), ("mxfp4", 32, "e8m0"), ("nvfp4", 16, "e4m3")]:
+    g128 = 128 if n % 128 == 0 else 64   # 2752 = 64 x 43
+    for fmt, group, sd in [("int4", 0, "f32"), ("int4", g128, "f16"), ("mxfp4", 32, "e8m0"), ("nvfp4", 16, "e4m3")]:
         say(f"wide rows n={n} {fmt} group={group}")
         packed, scales, ts = R.rhtq_forward(x, s, fmt=fmt, group=group, scale_dtype=sd)
         torch.cuda.synchronize()
@@ -324,16 +326,17 @@ def test_wide_rows_many_per_workgroup(R, n):
 
 
 INT4_GROUPS = ([(n, g) for n in (12288, 24576) for g in (0, 16, 32, 64, 128, 256, 512)]
-               + [(11008, g) for g in (0, 16, 32, 64, 128, 256)] + [(5504, g) for g in (0, 16, 32, 64, 128)])
+               + [(11008, g) for g in (0, 16, 32, 64, 128, 256)] + [(5504, g) for g in (0, 16, 32, 64, 128)]
+               + [(2752, g) for g in (0, 16, 32, 64)])
 
 
 @pytest.mark.parametrize("n,group", INT4_GROUPS)
 def test_wide_every_int4_group(R, n, group):
     """Every INT4 group the wide kernels take, and per-token scales (a row maximum across the
     waves): 12288 = 12 x 1024 (two waves per row) and 24576 = 12 x 2048 (four), groups 16 .. 512
-    from 8 values per lane, lane swaps and 0-4 DPP steps; 11008 = 172 x 64 and 5504 = 172 x 32
-    (two rows per work row), groups of runs, a'-rows and a'-row pairs or quads.  Every row
-    against the oracle, both scale types."""
+    from 8 values per lane, lane swaps and 0-4 DPP steps; 11008 = 172 x 64, 5504 = 172 x 32 and
+    2752 = 172 x 16 (two and four rows per work row), groups of runs, a'-rows and a'-row pairs or
+    quads.  Every row against the oracle, both scale types."""
     import dataclasses
     w = dataclasses.replace(WORKLOADS["downproj_12288_int4g128"], n=n, tokens=67)
     x, s = generate(w, dev())
