@@ -426,6 +426,53 @@ def test_forced_launch_failure_reports_and_writes_nothing():
     assert ok == "True", r.stdout
 
 
+GENERIC_WIDTHS = [16, 128, 1024, 4096, 8192, 3072, 12288, 24576, 2752, 5504, 11008]
+
+
+def test_generic_kernel_on_fast_widths(tmp_path):
+    """RHTQ_FORCE_GENERIC=1 (fresh process) sends bf16 rows of widths that normally take a fast
+    kernel through the generic LDS-staged kernel, the fallback for every other case: rotation,
+    INT4 g16, NVFP4 (dynamic g) and MXFP4 against the oracle, 9 rows each."""
+    import subprocess
+    import torch
+    say("generic kernel on the fast widths, in a subprocess")
+    out = str(tmp_path / "generic.npz")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import numpy as np, torch\n"
+            "import randomized_hadamard_rotation_amd as R\n"
+            "from workloads import splitmix64_signs\n"
+            "res = {}\n"
+            "for n in %r:\n"
+            "    g = torch.Generator().manual_seed(n)\n"
+            "    x = (torch.randn(9, n, generator=g) * torch.exp(torch.randn(n, generator=g))).to(torch.bfloat16).cuda()\n"
+            "    s = splitmix64_signs(4, n)\n"
+            "    res[f'x{n}'] = x.float().cpu().numpy()\n"
+            "    res[f'y{n}'] = R.rhtq_rotate(x, s).cpu().numpy()\n"
+            "    for fmt, grp, sd in (('int4', 16, 'f16'), ('nvfp4', 16, 'e4m3'), ('mxfp4', 32, 'e8m0')):\n"
+            "        if fmt == 'mxfp4' and n < 32: continue\n"
+            "        p, sc, ts = R.rhtq_forward(x, s, fmt=fmt, group=grp, scale_dtype=sd)\n"
+            "        res[f'p{fmt}{n}'] = p.cpu().numpy(); res[f's{fmt}{n}'] = sc.cpu().numpy()\n"
+            "        if ts is not None: res[f't{fmt}{n}'] = ts.cpu().numpy()\n"
+            "torch.cuda.synchronize()\n"
+            "np.savez(%r, **res)\n"
+            "print('done')\n") % (ROOT, GENERIC_WIDTHS, out)
+    env = dict(os.environ, RHTQ_FORCE_GENERIC="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env, cwd=ROOT)
+    assert r.returncode == 0 and r.stdout.strip().endswith("done"), r.stderr[-2000:]
+    d = np.load(out)
+    for n in GENERIC_WIDTHS:
+        say(f"generic kernel n={n}")
+        s = splitmix64_signs(4, n)
+        y_ref = O.rotate(torch.from_numpy(d[f"x{n}"]).to(torch.bfloat16), s)
+        C.check_rotation(d[f"y{n}"], y_ref)
+        C.check_int4(d[f"pint4{n}"], d[f"sint4{n}"], y_ref, 16, "f16")
+        amax = float(np.max(np.abs(y_ref)))
+        C.check_nvfp4(d[f"pnvfp4{n}"], d[f"snvfp4{n}"], float(d[f"tnvfp4{n}"].reshape(-1)[0]), y_ref,
+                      np.float32(amax / 2688.0))
+        if n >= 32:
+            C.check_mxfp4(d[f"pmxfp4{n}"], d[f"smxfp4{n}"], y_ref)
+
+
 def test_nvfp4_given_tensor_scale(R):
     import torch
     w = WORKLOADS["nvfp4_4096"].with_tokens(77)
