@@ -205,7 +205,7 @@ def test_workload_full_size_sampled(R, name):
 # (only those rows are copied to the host).
 BEYOND_INT32 = [("llama_4096_int4", 2 ** 19 + 5), ("mxfp4_4096", 2 ** 19 + 3), ("kv_128_int4g128", 2 ** 24 + 3),
                 ("downproj_12288_int4g128", 174763), ("downproj7b_11008_int4g128", 195085),
-                ("downproj_12288_int4g128:n=24576", 87385)]
+                ("downproj_12288_int4g128:n=24576", 87385), ("downproj7b_11008_int4g128:n=5504", 390170)]
 
 
 @pytest.mark.parametrize("name,tokens", BEYOND_INT32)
