@@ -577,6 +577,29 @@ def test_inverse_round_trip(R, name):
     assert np.allclose(O.inverse_rotate(to_np(y), s), xr, rtol=0, atol=1e-5 * np.abs(xr).max())
 
 
+@pytest.mark.parametrize("n", [24576, 5504, 2752, 3072, 22016])
+def test_inverse_round_trip_widths(R, n):
+    """Inverse of the device's own codes at the 12 x 2^k and 172 x 2^k widths outside the bench
+    workloads (INT4 g16 and MXFP4), against the oracle's inverse of the same codes; the rotation
+    alone inverts to fp32 precision."""
+    import torch
+    g = torch.Generator().manual_seed(7 * n)
+    x = (torch.randn(13, n, generator=g) * torch.exp(torch.randn(n, generator=g))).to(torch.bfloat16).to(dev())
+    s = splitmix64_signs(6, n)
+    for fmt, grp, sd in (("int4", 16, "f16"), ("mxfp4", 32, "e8m0")):
+        say(f"inverse n={n} {fmt}")
+        packed, scales, _ = R.rhtq_forward(x, s, fmt=fmt, group=grp, scale_dtype=sd)
+        xh = R.rhtq_inverse(packed, scales, n, s, fmt=fmt, group=grp, scale_dtype=sd)
+        torch.cuda.synchronize()
+        ref = O.inverse(to_np(packed), to_np(scales), s, fmt, grp, None)
+        err = np.max(np.abs(to_np(xh) - ref), axis=1)
+        assert np.all(err <= 1e-5 * np.max(np.abs(ref), axis=1) + 1e-30)
+    y = R.rhtq_rotate(x, s)
+    torch.cuda.synchronize()
+    xr = to_np(x)
+    assert np.allclose(O.inverse_rotate(to_np(y), s), xr, rtol=0, atol=1e-5 * np.abs(xr).max())
+
+
 @pytest.mark.parametrize("n", [64, 128, 256])
 def test_inverse_kv_rows(R, n):
     """KV-cache read path (one INT4 scale per row, head dims 64 / 128 / 256): the device inverse of
