@@ -278,6 +278,14 @@ def pin_nvfp4_invariants(O):
     half_step = np.where(av < 2, 0.25, np.where(av < 4, 0.5, 1.0))
     half_step = np.where(av > 6, av - 6 + 0.0, half_step)
     _check(np.all(np.abs(yhat - y) <= half_step * seff * (1 + 1e-9) + 1e-300), "E2M1 dequant bound")
+    # every block whose scale is a normal E4M3 value below 448 carries its maximum b to
+    # b / (dec(s_b) g) within E4M3's half step of 6: the scale is b / (6 g) to 2^-4 relative
+    bmax = np.max(np.abs(y.reshape(8, 16, 16)), axis=-1)
+    dec = O.e4m3_decode(out["scales"])
+    normal = (dec >= 2.0 ** -6) & (dec < 448.0) & (bmax > 0)
+    r = bmax[normal] / (dec[normal] * np.float64(g))
+    _check(normal.sum() > 64 and np.all((r >= 6 / (1 + 2.0 ** -4)) & (r <= 6 / (1 - 2.0 ** -4))),
+           "block maxima must land near E2M1 6")
 
 
 def pin_mxfp4_closed_form(O):
@@ -362,10 +370,68 @@ def pin_blocked_rotation(O):
     _check(np.array_equal(O.rotate_blocked(x, s, 1024), O.rotate(x, s)), "block = n is the full rotation")
 
 
+def pin_nvfp4_block_scale_closed_form(O):
+    """NVFP4 block scales from a given tensor scale g ("Methodology checks for NVFP4 W4A4 on
+    Qwen3-8B", NVFP4 results: E2M1 codes under E4M3 block scales).  A block's maximum b must
+    map to the largest E2M1 magnitude 6, so its scale is b / (6 g), rounded to E4M3.  With
+    g = 0.5 and block maxima b = 3 sigma, sigma exactly representable, the scale codes follow
+    from the E4M3 layout alone (code = e << 3 | m, value (1 + m/8) 2^(e - 7), subnormal
+    m 2^-9): 1.0 -> 0x38, 0.125 -> 0x20, 2.5 -> 0x42, 416 -> 0x7D, 3 * 2^-9 -> 0x03;
+    the midpoints 1.0625 and 1.1875 round to the even mantissa (0x38, 0x3A).  Inside a
+    block the values y / (dec(s_b) g) are chosen on the E2M1 grid and on its ties."""
+    g = 0.5
+    sigmas = [1.0, 0.125, 2.5, 416.0, 3 * 2.0 ** -9, 1.0625, 1.1875]
+    want_sc = [0x38, 0x20, 0x42, 0x7D, 0x03, 0x38, 0x3A]
+    # in units of dec(s_b) * g; the first entry (6 sigma / dec(s_b)) is the block maximum
+    body = [-4.0, 3.0, 1.5, 0.5, 0.25, -0.75, 5.0, 2.5, -1.25, 0.0, 1.0, -2.0, 0.1, 3.5, 4.0]
+    body_codes = [0b1110, 0b0101, 0b0011, 0b0001, 0b0000, 0b1010, 0b0110, 0b0100, 0b1010,
+                  0b0000, 0b0010, 0b1100, 0b0000, 0b0110, 0b0110]
+    dec = {0x38: 1.0, 0x20: 0.125, 0x42: 2.5, 0x7D: 416.0, 0x03: 3 * 2.0 ** -9, 0x3A: 1.25}
+    y = np.zeros((1, 16 * len(sigmas)))
+    want_codes = np.zeros(y.shape, dtype=np.int64)
+    for b, (sig, sc) in enumerate(zip(sigmas, want_sc)):
+        unit = dec[sc] * g
+        y[0, 16 * b] = 6.0 * g * sig                 # block maximum b = 6 g sigma
+        y[0, 16 * b + 1:16 * b + 16] = np.array(body) * unit
+        v0 = 6.0 * sig / dec[sc]                     # the maximum in scale units
+        want_codes[0, 16 * b] = int(O.e2m1_encode(np.array([v0]))[0])
+        want_codes[0, 16 * b + 1:16 * b + 16] = body_codes
+    # the maximum itself: 6 on exact blocks; 6.375 -> 6 and 5.7 -> 6 on the tie blocks
+    _check(list(want_codes[0, ::16]) == [7] * 7, "block maxima land on E2M1 6")
+    codes, sc, gg, _ = O.quantize_nvfp4(y, tensor_scale=g)
+    _check(gg == np.float32(g), "given tensor scale is used as is")
+    _check(list(sc[0]) == want_sc, f"NVFP4 block scales b/(6g): {[hex(int(c)) for c in sc[0]]}")
+    _check(np.array_equal(codes, want_codes), "NVFP4 block codes")
+    # dynamic g of the same tensor: g = fl32(A / 2688) with A = 6 * 0.5 * 416 = 1248
+    codes_d, sc_d, g_d, _ = O.quantize_nvfp4(y)
+    _check(g_d == np.float32(1248.0 / 2688.0), "dynamic g")
+    _check(sc_d[0, 3] == 0x7E, "the tensor-maximum block takes E4M3 448")
+
+
+def pin_int4_clamp_saturated_scale(O):
+    """INT4 codes clamp to [-8, 7] (the tiny workload's definition: round half to even, clamp
+    [-8, 7]).  Under absmax the clamp only acts when the stored scale is smaller than amax / 7:
+    an fp16 scale saturates at 65504, so a group with amax 9 * 65504 is quantised in units of
+    65504 and its values -9, -7.5, 9, 7.5, 3.5 (units) give -8, -8, 7, 7, 4."""
+    u = 65504.0
+    y = np.zeros((2, 32))
+    y[0, :6] = np.array([-9.0, -7.5, 9.0, 7.5, 3.5, -6.5]) * u
+    y[1, :4] = np.array([1.0, -7.0, 2.5, -0.5])    # an ordinary group next to it
+    q, s, _ = O.quantize_int4(y, 16, "f16")
+    _check(s[0, 0] == np.float16(65504) and s[0, 1] == 0, "saturated fp16 scale")
+    _check(list(q[0, :6]) == [-8, -8, 7, 7, 4, -6] and not np.any(q[0, 6:]), f"clamped codes {q[0, :6]}")
+    _check(float(s[1, 0]) == float(np.float16(1.0)), "scale 7/7 in the ordinary group")
+    _check(list(q[1, :4]) == [1, -7, 2, 0], "ordinary group codes")
+    # fp32 storage never saturates here: the same row gives +-7 at the maximum
+    q32, s32, _ = O.quantize_int4(y[:1], 16, "f32")
+    _check(list(q32[0, :3]) == [-7, -6, 7], "fp32 scale: the maximum maps to +-7")
+
+
 ALL_PINS = [
     pin_sylvester_matches_scipy, pin_orthogonality, pin_h172_williamson, pin_fwht_equals_dense,
     pin_rotate_matches_scipy_definition, pin_parseval_and_roundtrip, pin_e3_closed_form,
     pin_e1_worked_example, pin_e2_worked_example, pin_int4_rounding, pin_fp16_storage,
     pin_e2m1, pin_e4m3, pin_nvfp4_invariants, pin_mxfp4_closed_form, pin_mxfp4_worked_block,
-    pin_mxfp4_invariants, pin_blocked_rotation,
+    pin_mxfp4_invariants, pin_blocked_rotation, pin_nvfp4_block_scale_closed_form,
+    pin_int4_clamp_saturated_scale,
 ]

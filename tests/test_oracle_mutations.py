@@ -207,11 +207,37 @@ def _blocked_signs_tiled(O):
     O.rotate_blocked = bad
 
 
+def _nvfp4_block_scale_over_4(O):
+    """block scale b / (4 g) instead of b / (6 g): block maxima land on E2M1 4"""
+    def q(y, tensor_scale=None):
+        y = np.asarray(y, dtype=np.float64)
+        T, n = y.shape
+        g = O.nvfp4_tensor_scale(y) if tensor_scale is None else np.float32(tensor_scale)
+        if g == 0:
+            return (np.zeros((T, n), np.uint8), np.zeros((T, n // 16), np.uint8), g, np.zeros((T, n)))
+        bmax = np.max(np.abs(y.reshape(T, n // 16, 16)), axis=-1)
+        sc = O.e4m3_encode(bmax / (4.0 * np.float64(g)))
+        codes, v = O.nvfp4_codes_from_scales(y, sc, g)
+        return codes, sc, g, v
+    O.quantize_nvfp4 = q
+
+
+def _int4_symmetric_clamp(O):
+    """INT4 codes clamped to [-7, 7] instead of [-8, 7]"""
+    orig = O.int4_codes
+
+    def codes(y, stored_scale, group):
+        q, v = orig(y, stored_scale, group)
+        return np.maximum(q, -7).astype(np.int8), v
+    O.int4_codes = codes
+
+
 MUTATIONS = [_no_norm, _signs_after, _h12_transposed_in_rotate, _h12_typo, _round_half_away,
              _swap_nibbles, _scale_over_8, _fp16_truncation, _nvfp4_wrong_constant,
              _e2m1_ties_up, _e4m3_truncate, _fwht_skip_stage, _inverse_without_transpose,
              _mxfp4_emax_one, _mxfp4_ceil, _mxfp4_bias_128, _blocked_norm_sqrt_n, _blocked_signs_tiled,
-             _h172_transposed_in_rotate, _h172_coset_sign, _h172_array_sign]
+             _h172_transposed_in_rotate, _h172_coset_sign, _h172_array_sign, _nvfp4_block_scale_over_4,
+             _int4_symmetric_clamp]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
