@@ -131,7 +131,10 @@ int rhtq_rotate(const void* x, int in_dtype, int64_t tokens, int32_t n,
  *   scales_out  [tokens][n/group] (group 0: [tokens][1]); s = max|y|/7 over the group,
  *               rounded to the storage type (nearest even; fp16 saturates at 65504)
  *   codes       q = clamp(round_half_even(y / s_stored), -8, 7); a zero group stores
- *               s = 0 and codes 0.  Codes never reach -8 (|y| <= 7 s).
+ *               s = 0 and codes 0.  While the stored scale is a normal number of its
+ *               type, |y| <= 7 s and codes stay in [-7, 7].  When an fp16 scale
+ *               saturates at 65504 (amax / 7 above it) or is subnormal, y / s can
+ *               exceed 7 in magnitude and the clamp applies: codes may then be -8.
  *   tensor_scale, tensor_scale_mode: ignored (may be NULL / 0)
  *
  * NVFP4-style (fmt RHTQ_FMT_NVFP4; NVFP4 methodology thread):

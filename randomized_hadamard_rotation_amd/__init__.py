@@ -95,17 +95,45 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _resolve_stream(stream):
+    """(stream object, whether it differs from torch's current stream).  Copies and fills
+    this wrapper makes are enqueued on the current stream, so another stream first waits for
+    the current one."""
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    cur = torch.cuda.current_stream()
+    if stream is None or stream.cuda_stream == cur.cuda_stream:
+        return cur, False
+    stream.wait_stream(cur)
+    return stream, True
+
+
+def _keep_for(stream, other, *ts):
+    """Tensors this wrapper allocated (copies, signs, outputs) are used by work enqueued on
+    `stream`; when that is not torch's current stream, tell the caching allocator so their
+    memory is not handed out again before that work has run."""
+    if other:
+        for t in ts:
+            if t is not None:
+                t.record_stream(stream)
 
 
 def _need_device(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
             raise ValueError("rhtq runs on the GPU only: pass device tensors")
+
+
+def _expect(t, name, dtype, shape, device=None):
+    """A caller-supplied buffer must match what the kernels will write or read: the C ABI
+    takes bare pointers and cannot check sizes.  The device is checked last."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _signs_tensor(signs, n, device):
@@ -117,7 +145,7 @@ def _signs_tensor(signs, n, device):
         signs = torch.from_numpy(np.ascontiguousarray(signs.astype(np.int8)))
     if signs.dtype != torch.int8 or signs.numel() != n:
         raise ValueError("signs must be int8 with n entries")
-    return signs.to(device).contiguous()
+    return signs.reshape(n).to(device).contiguous()
 
 
 def _in_dtype(x):
@@ -127,6 +155,19 @@ def _in_dtype(x):
     if x.dtype == torch.float32:
         return RHTQ_IN_F32
     raise ValueError("x must be bfloat16 or float32")
+
+
+def _rows(x):
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [tokens][n]")
+    return x.shape
+
+
+def _scale_torch_dtype(scale_dtype):
+    torch = _torch()
+    if scale_dtype not in _SCALE:
+        raise ValueError(f"unknown scale_dtype {scale_dtype!r}")
+    return {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8, "e8m0": torch.uint8}[scale_dtype]
 
 
 def rhtq_abi_version() -> int:
@@ -148,27 +189,45 @@ def rhtq_signs_from_seed(seed: int, n: int) -> np.ndarray:
     return out
 
 
+def _same_device(dev, **ts):
+    _need_device(*ts.values())
+    for name, t in ts.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
 def rhtq_rotate(x, signs=None, out=None, stream=None, block=None):
     """y = H_n diag(signs) x / sqrt(n) per row, fp32 [tokens][n].  With block = b < n the
-    rotation is block-diagonal: (I (x) H_b) diag(signs) x / sqrt(b)."""
+    rotation is block-diagonal: (I (x) H_b) diag(signs) x / sqrt(b).  An `out` passed in must
+    be contiguous fp32 [tokens][n] on x's device."""
     torch = _torch()
-    _need_device(x)
-    x = x.contiguous()
-    tokens, n = x.shape
-    s = _signs_tensor(signs, n, x.device)
-    if out is None:
-        out = torch.empty((tokens, n), dtype=torch.float32, device=x.device)
+    tokens, n = _rows(x)
+    in_dtype = _in_dtype(x)
+    if out is not None:
+        _expect(out, "out", torch.float32, (tokens, n))
+    _same_device(x.device, x=x, out=out)
+    xc = x.contiguous()                  # bound to a local: it must outlive the call
+    s = _signs_tensor(signs, n, xc.device)
+    st, other = _resolve_stream(stream)
+    own = out is None
+    if own:
+        out = torch.empty((tokens, n), dtype=torch.float32, device=xc.device)
+    sp = ctypes.c_void_p(st.cuda_stream)
     if block is None or block == n:
-        _check(lib.rhtq_rotate(_ptr(x), _in_dtype(x), tokens, n, _ptr(s), _ptr(out), _stream(stream)),
-               "rhtq_rotate")
+        status = lib.rhtq_rotate(_ptr(xc), in_dtype, tokens, n, _ptr(s), _ptr(out), sp)
+        where = "rhtq_rotate"
     else:
-        _check(lib.rhtq_rotate_blocked(_ptr(x), _in_dtype(x), tokens, n, block, _ptr(s), _ptr(out),
-                                       _stream(stream)), "rhtq_rotate_blocked")
+        status = lib.rhtq_rotate_blocked(_ptr(xc), in_dtype, tokens, n, block, _ptr(s), _ptr(out), sp)
+        where = "rhtq_rotate_blocked"
+    _check(status, where)
+    _keep_for(st, other, xc if xc is not x else None, s, out if own else None)
     return out
 
 
 def scale_shape(tokens: int, n: int, fmt: str, group: int):
     g = n if group == 0 else group
+    if g <= 0 or n % g:
+        raise ValueError(f"group {group} does not divide n = {n}")
     return (tokens, n // g)
 
 
@@ -181,54 +240,112 @@ def rhtq_forward(x, signs=None, fmt: str = "int4", group: int = 0, scale_dtype: 
     NVFP4: scales uint8 E4M3 [tokens][n/16]; tensor_scale a device float32 [1]
     (written in 'dynamic' mode, read in 'given' mode).
     MXFP4: scales uint8 E8M0 [tokens][n/32].
-    block = b < n: block-diagonal rotation (groups inside a block)."""
+    block = b < n: block-diagonal rotation (groups inside a block).
+    Buffers passed in (packed, scales, tensor_scale) must have exactly these dtypes and
+    shapes, be contiguous and live on x's device; anything else raises ValueError before
+    any work is enqueued."""
     torch = _torch()
-    _need_device(x)
-    x = x.contiguous()
-    tokens, n = x.shape
+    if fmt not in _FMT:
+        raise ValueError(f"unknown fmt {fmt!r}")
+    if tensor_scale_mode not in ("dynamic", "given"):
+        raise ValueError("tensor_scale_mode must be 'dynamic' or 'given'")
+    tokens, n = _rows(x)
+    in_dtype = _in_dtype(x)
     if scale_dtype is None:
         scale_dtype = _DEFAULT_SCALE[fmt]
     if group == 0:
         group = _DEFAULT_GROUP.get(fmt, 0)
-    s = _signs_tensor(signs, n, x.device)
-    if packed is None:
-        packed = torch.empty((tokens, n // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        sdt = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8, "e8m0": torch.uint8}[scale_dtype]
-        scales = torch.empty(scale_shape(tokens, n, fmt, group), dtype=sdt, device=x.device)
-    if fmt == "nvfp4" and tensor_scale is None:
-        tensor_scale = torch.zeros(1, dtype=torch.float32, device=x.device)
+    sdt = _scale_torch_dtype(scale_dtype)
+    sshape = scale_shape(tokens, n, fmt, group)
+    if packed is not None:
+        _expect(packed, "packed", torch.uint8, (tokens, n // 2))
+    if scales is not None:
+        _expect(scales, "scales", sdt, sshape)
+    if fmt == "nvfp4":
+        if tensor_scale is not None:
+            _expect(tensor_scale, "tensor_scale", torch.float32, (1,))
+        elif tensor_scale_mode == "given":
+            raise ValueError("tensor_scale_mode 'given' needs a tensor_scale")
+    _same_device(x.device, x=x, packed=packed, scales=scales, tensor_scale=tensor_scale)
+    xc = x.contiguous()                  # bound to a local: it must outlive the call
+    s = _signs_tensor(signs, n, xc.device)
+    st, other = _resolve_stream(stream)
+    own_p, own_s = packed is None, scales is None
+    own_t = fmt == "nvfp4" and tensor_scale is None
+    if own_p:
+        packed = torch.empty((tokens, n // 2), dtype=torch.uint8, device=xc.device)
+    if own_s:
+        scales = torch.empty(sshape, dtype=sdt, device=xc.device)
+    if own_t:
+        tensor_scale = torch.zeros(1, dtype=torch.float32, device=xc.device)
     mode = RHTQ_TENSOR_SCALE_DYNAMIC if tensor_scale_mode == "dynamic" else RHTQ_TENSOR_SCALE_GIVEN
+    ts_ptr = _ptr(tensor_scale) if fmt == "nvfp4" else None
+    sp = ctypes.c_void_p(st.cuda_stream)
     if block is None or block == n:
-        _check(lib.rhtq_forward(_ptr(x), _in_dtype(x), tokens, n, _ptr(s), _FMT[fmt], group,
-                                _SCALE[scale_dtype], _ptr(packed), _ptr(scales), _ptr(tensor_scale),
-                                mode, _stream(stream)), "rhtq_forward")
+        status = lib.rhtq_forward(_ptr(xc), in_dtype, tokens, n, _ptr(s), _FMT[fmt], group,
+                                  _SCALE[scale_dtype], _ptr(packed), _ptr(scales), ts_ptr, mode, sp)
+        where = "rhtq_forward"
     else:
-        _check(lib.rhtq_forward_blocked(_ptr(x), _in_dtype(x), tokens, n, block, _ptr(s), _FMT[fmt], group,
-                                        _SCALE[scale_dtype], _ptr(packed), _ptr(scales), _ptr(tensor_scale),
-                                        mode, _stream(stream)), "rhtq_forward_blocked")
+        status = lib.rhtq_forward_blocked(_ptr(xc), in_dtype, tokens, n, block, _ptr(s), _FMT[fmt], group,
+                                          _SCALE[scale_dtype], _ptr(packed), _ptr(scales), ts_ptr, mode, sp)
+        where = "rhtq_forward_blocked"
+    _check(status, where)
+    _keep_for(st, other, xc if xc is not x else None, s, packed if own_p else None,
+              scales if own_s else None, tensor_scale if own_t else None)
     return packed, scales, tensor_scale
 
 
 def rhtq_inverse(packed, scales, n: int, signs=None, fmt: str = "int4", group: int = 0,
                  scale_dtype: str | None = None, tensor_scale=None, out=None, stream=None, block=None):
-    """Dequantise and undo the rotation: x_hat fp32 [tokens][n]."""
+    """Dequantise and undo the rotation: x_hat fp32 [tokens][n].  packed, scales and
+    tensor_scale (NVFP4) must have the dtypes and shapes rhtq_forward returns for the same
+    (tokens, n, fmt, group, scale_dtype); non-contiguous ones are read through contiguous
+    copies.  An `out` passed in must be contiguous fp32 [tokens][n]."""
     torch = _torch()
-    _need_device(packed, scales, tensor_scale)
+    if fmt not in _FMT:
+        raise ValueError(f"unknown fmt {fmt!r}")
+    if packed.dim() != 2:
+        raise ValueError("packed must be 2-D [tokens][n/2]")
     tokens = packed.shape[0]
     if scale_dtype is None:
         scale_dtype = _DEFAULT_SCALE[fmt]
     if group == 0:
         group = _DEFAULT_GROUP.get(fmt, 0)
-    s = _signs_tensor(signs, n, packed.device)
-    if out is None:
-        out = torch.empty((tokens, n), dtype=torch.float32, device=packed.device)
+    sdt = _scale_torch_dtype(scale_dtype)
+    if packed.dtype != torch.uint8 or tuple(packed.shape) != (tokens, n // 2):
+        raise ValueError(f"packed: {packed.dtype} {tuple(packed.shape)}, expected uint8 {(tokens, n // 2)}")
+    sshape = scale_shape(tokens, n, fmt, group)
+    if scales.dtype != sdt or tuple(scales.shape) != tuple(sshape):
+        raise ValueError(f"scales: {scales.dtype} {tuple(scales.shape)}, expected {sdt} {sshape}")
+    if fmt == "nvfp4":
+        if tensor_scale is None:
+            raise ValueError("NVFP4 needs its tensor_scale")
+        if tensor_scale.dtype != torch.float32 or tensor_scale.numel() != 1:
+            raise ValueError("tensor_scale must be one float32")
+    if out is not None:
+        _expect(out, "out", torch.float32, (tokens, n))
+    dev = packed.device
+    _same_device(dev, packed=packed, scales=scales, tensor_scale=tensor_scale if fmt == "nvfp4" else None,
+                 out=out)
+    # contiguous copies are bound to locals so that they outlive the call
+    pc = packed.contiguous()
+    sc = scales.contiguous()
+    tc = tensor_scale.reshape(1).contiguous() if fmt == "nvfp4" else None
+    s = _signs_tensor(signs, n, dev)
+    st, other = _resolve_stream(stream)
+    own = out is None
+    if own:
+        out = torch.empty((tokens, n), dtype=torch.float32, device=dev)
+    sp = ctypes.c_void_p(st.cuda_stream)
     if block is None or block == n:
-        _check(lib.rhtq_inverse(_ptr(packed.contiguous()), _ptr(scales.contiguous()), _ptr(tensor_scale),
-                                tokens, n, _ptr(s), _FMT[fmt], group, _SCALE[scale_dtype], _ptr(out),
-                                _stream(stream)), "rhtq_inverse")
+        status = lib.rhtq_inverse(_ptr(pc), _ptr(sc), _ptr(tc), tokens, n, _ptr(s), _FMT[fmt], group,
+                                  _SCALE[scale_dtype], _ptr(out), sp)
+        where = "rhtq_inverse"
     else:
-        _check(lib.rhtq_inverse_blocked(_ptr(packed.contiguous()), _ptr(scales.contiguous()), _ptr(tensor_scale),
-                                        tokens, n, block, _ptr(s), _FMT[fmt], group, _SCALE[scale_dtype],
-                                        _ptr(out), _stream(stream)), "rhtq_inverse_blocked")
+        status = lib.rhtq_inverse_blocked(_ptr(pc), _ptr(sc), _ptr(tc), tokens, n, block, _ptr(s), _FMT[fmt],
+                                          group, _SCALE[scale_dtype], _ptr(out), sp)
+        where = "rhtq_inverse_blocked"
+    _check(status, where)
+    _keep_for(st, other, pc if pc is not packed else None, sc if sc is not scales else None,
+              tc if (tc is not None and tc is not tensor_scale) else None, s, out if own else None)
     return out

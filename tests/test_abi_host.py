@@ -142,3 +142,40 @@ def test_blocked_host_validation(R):
     IB = lambda *a: lib.rhtq_inverse_blocked(*a)
     assert IB(fake, fake, None, 4, 4096, 128, None, 2, 16, 3, fake, s) == R.RHTQ_EUNSUPPORTED      # mxfp4 group 16
     assert IB(None, fake, None, 4, 4096, 128, None, 2, 32, 3, fake, s) == R.RHTQ_EINVAL
+
+
+def test_python_binding_checks_caller_buffers(R):
+    """Caller-supplied outputs and inverse inputs are checked for dtype, shape and contiguity
+    before anything touches a device (the C ABI takes bare pointers and cannot)."""
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    bad = [
+        dict(fmt="int4", scale_dtype="f32", scales=torch.empty(4, 1, dtype=torch.float16)),    # fp16 for f32
+        dict(fmt="int4", group=128, scale_dtype="f16", scales=torch.empty(4, 1, dtype=torch.float16)),  # too few
+        dict(fmt="int4", packed=torch.empty(4, 256, dtype=torch.uint8)),                       # n, not n/2
+        dict(fmt="int4", packed=torch.empty(128, 4, dtype=torch.uint8).t()),                   # not contiguous
+        dict(fmt="nvfp4", tensor_scale=torch.empty(2, dtype=torch.float32)),
+        dict(fmt="nvfp4", tensor_scale_mode="given"),                                         # no g given
+        dict(fmt="mxfp4", scales=torch.empty(4, 16, dtype=torch.uint8)),                       # blocks of 16
+        dict(fmt="int4", group=96),                                                           # does not divide
+        dict(fmt="fp4"),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            R.rhtq_forward(x, **kw)
+    with pytest.raises(ValueError):
+        R.rhtq_rotate(x, out=torch.empty(4, 256, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        R.rhtq_rotate(torch.zeros(4, 2, 128, dtype=torch.bfloat16))
+    p = torch.empty(4, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError):   # fp16 scales where the default is fp32
+        R.rhtq_inverse(p, torch.empty(4, 1, dtype=torch.float16), 256)
+    with pytest.raises(ValueError):   # scales for a different group
+        R.rhtq_inverse(p, torch.empty(4, 1, dtype=torch.float16), 256, group=128, scale_dtype="f16")
+    with pytest.raises(ValueError):   # NVFP4 without its tensor scale
+        R.rhtq_inverse(p, torch.empty(4, 16, dtype=torch.uint8), 256, fmt="nvfp4")
+    with pytest.raises(ValueError):   # packed for another width
+        R.rhtq_inverse(p, torch.empty(4, 1, dtype=torch.float32), 512)
+    # well-formed CPU buffers get through the checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU only"):
+        R.rhtq_inverse(p, torch.empty(4, 1, dtype=torch.float32), 256)

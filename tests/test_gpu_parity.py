@@ -661,3 +661,33 @@ def test_blocked_rotation_and_quantisation(R, n, block):
             ref = O.inverse(p, sc, s, fmt, grp, None if ts is None else float(ts.item()), block=block)
             err = np.max(np.abs(to_np(xh) - ref), axis=1)
             assert np.all(err <= 1e-5 * np.max(np.abs(ref), axis=1) + 1e-30)
+
+
+def test_binding_noncontiguous_and_side_stream(R):
+    """The binding reads non-contiguous inputs through contiguous copies that live past the
+    call, and work on a non-current stream gives the same bytes as on the current one."""
+    import torch
+    say("binding: non-contiguous x / packed / scales, side stream")
+    w = WORKLOADS["llama_4096_int4"].with_tokens(64)
+    x, s = x_to(w)
+    xt = x.t().contiguous().t()
+    assert not xt.is_contiguous() and torch.equal(xt, x)
+    p0, s0, _ = R.rhtq_forward(x, s, fmt="int4", group=128, scale_dtype="f16")
+    p1, s1, _ = R.rhtq_forward(xt, s, fmt="int4", group=128, scale_dtype="f16")
+    side = torch.cuda.Stream()
+    p2, s2, _ = R.rhtq_forward(xt, s, fmt="int4", group=128, scale_dtype="f16", stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(p0, p1) and torch.equal(s0, s1)
+    assert torch.equal(p0, p2) and torch.equal(s0, s2)
+    pn, sn = p0.t().contiguous().t(), s0.t().contiguous().t()
+    assert not pn.is_contiguous()
+    xh0 = R.rhtq_inverse(p0, s0, 4096, s, group=128, scale_dtype="f16")
+    xh1 = R.rhtq_inverse(pn, sn, 4096, s, group=128, scale_dtype="f16", stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(xh0, xh1)
+    # a caller's output buffers of the wrong size are refused before any launch
+    with pytest.raises(ValueError):
+        R.rhtq_forward(x, s, fmt="int4", group=128, scale_dtype="f16",
+                       scales=torch.empty(64, 16, dtype=torch.float16, device=dev()))
