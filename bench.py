@@ -79,7 +79,8 @@ def run_timed(torch, step, steps, warmup, graph):
     reported, eager ms per step).  graph=True captures the K steps once into a HIP graph
     (torch.cuda.CUDAGraph) and times its replay: every step is still one full call on its own
     buffers, but the host's per-call cost (Python, ctypes) no longer stretches the measurement of
-    a kernel that runs for a few microseconds."""
+    a kernel that runs for a few microseconds.  The graph is replayed untimed for about 25 ms
+    before the timed replay, so that the timed steps run at the GPU's steady clocks."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -101,8 +102,15 @@ def run_timed(torch, step, steps, warmup, graph):
     with torch.cuda.graph(g):
         for i in range(steps):
             step(i)
-    g.replay()
-    torch.cuda.synchronize()
+    # untimed replays for about 25 ms first: a timed region of a few dozen microseconds right
+    # after start-up otherwise catches the GPU before its clocks have settled, and run-to-run
+    # spread then exceeds the differences being measured
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 > 0.025:
+            break
     return timed(g.replay), ms_eager
 
 

@@ -178,4 +178,89 @@ __device__ __forceinline__ void quant_epilogue(const KernelArgs& a, const int64_
   }
 }
 
+// The same epilogue for the linear layout of the paired 4096 kernel: in chunk q this lane holds
+// the eight consecutive outputs cbase(q) + 8 lane + r, so element bits 0-2 are the register
+// index and bits 3-8 the lane.  A group of 2^G elements (G = 4 .. 9) spans 2^(G - 3) aligned
+// lanes, reduced by group_max; every lane of a group computes the group's scale and the
+// group's first lane stores it.  Codes go out as 4-byte stores, one dword per lane and chunk,
+// so each wave store covers 256 contiguous bytes in lane order.
+template <int OP, int R, typename ValF, typename BaseF, typename RowMaxF>
+__device__ __forceinline__ void quant_epilogue_lin(const KernelArgs& a, const int64_t row, const int64_t relem0,
+                                                   const int G, const float invS, const float cnorm, const float gts,
+                                                   const float inv6g, const int lane, const bool row_writer, ValF val,
+                                                   BaseF cbase, RowMaxF rowmax) {
+  float mq[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    float m = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(val(q, r)));
+    mq[q] = m;
+  }
+  float inv[R];
+  bool clamp = false;
+  if (OP == OP_INT4 && G == 0) {
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < R; ++q) m = fmaxf(m, mq[q]);
+    const Int4Scale sc = int4_scale(rowmax(m * invS), cnorm, a.scale_dtype);
+    clamp = sc.clamp;
+#pragma unroll
+    for (int q = 0; q < R; ++q) inv[q] = sc.inv * invS;
+    if (row_writer) store_int4_scale(a.scales, a.scale_dtype, row, sc.s);
+  } else {
+    // a group of 2^G elements spans 2^(G - 3) lanes (G = 4 .. 9)
+    const int gl = 1 << (G - 3);
+    const bool writer = (lane & (gl - 1)) == 0;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const float bmx = group_max(mq[q], gl) * invS;   // group maximum, true units (unnormalised)
+      const int64_t gi = (relem0 + cbase(q) + 8 * lane) >> G;
+      if constexpr (OP == OP_NVFP4) {
+        const uint32_t code = e4m3_code((bmx * cnorm) * inv6g);
+        const float seff = e4m3_value(code) * gts;
+        inv[q] = seff > 0.0f ? (cnorm * __builtin_amdgcn_rcpf(seff)) * invS : 0.0f;
+        if (writer) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)code;
+      } else if constexpr (OP == OP_MXFP4) {
+        const float bm = bmx * cnorm;
+        const int ex = mx_exponent(bm);
+        inv[q] = bm > 0.0f ? __builtin_ldexpf(invS * cnorm, -ex) : 0.0f;
+        if (writer) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)(ex + 127);
+      } else {
+        const Int4Scale sc = int4_scale(bmx, cnorm, a.scale_dtype);
+        inv[q] = sc.inv * invS;
+        clamp |= sc.clamp;
+        if (writer) store_int4_scale(a.scales, a.scale_dtype, gi, sc.s);
+      }
+    }
+  }
+  uint8_t* prow = a.packed + (relem0 >> 1);
+  if constexpr (OP == OP_INT4) {
+    const bool any_clamp = __builtin_amdgcn_ballot_w64(clamp) != 0;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      uint32_t qb[8];
+      if (!any_clamp) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) qb[r] = __float_as_uint(__builtin_fmaf(val(q, r), inv[q], 12582912.0f));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          qb[r] = __float_as_uint(__builtin_amdgcn_fmed3f(val(q, r) * inv[q], -8.0f, 7.0f) + 12582912.0f);
+      }
+      st_stream(prow + (cbase(q) >> 1) + 4 * lane, pack8_nibbles(qb));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const float s = inv[q];
+      uint32_t w = 0;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(q, 0) * s, val(q, 1) * s, 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(q, 2) * s, val(q, 3) * s, 1.0f, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(q, 4) * s, val(q, 5) * s, 1.0f, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(q, 6) * s, val(q, 7) * s, 1.0f, 3);
+      st_stream(prow + (cbase(q) >> 1) + 4 * lane, s > 0.0f ? w : 0u);
+    }
+  }
+}
 }  // namespace rhtq

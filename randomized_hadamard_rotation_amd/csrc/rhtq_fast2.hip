@@ -256,16 +256,28 @@ void fast2_kernel(KernelArgs a) {
 // Small row counts at n = 4096: two waves per row, one row per workgroup (the workgroup barrier
 // of the exchange then waits for the row's own two waves only).  With one wave per
 // row a SIMD holds only the few rows the call has and sits idle while they wait on their own
-// dependency chains; splitting each row doubles the waves and halves each chain.  Wave h takes
-// the row half j = 2048 h + [0, 2048) (fragments 4 h .. 4 h + 3): stages 1 and 2 and the
-// bit-10 butterfly as above, in its own split units.  Bit 11 pairs the halves: wave h keeps
-// its partial sums for output chunks with bit 10 = h, sends the others through LDS, and both
-// sides go to the smaller of the two split scales (powers of two, exact).  Wave h then owns
-// the output chunks 1024 (2 h' + h) + [0, 1024), h' = 0, 1.  Per-row INT4 takes the row
-// maximum over both waves through LDS.  Each lane loads its 32 signs from L2 together with
-// its row fragments and turns them into sign-bit masks itself, so no workgroup table or
-// barrier stands before the row loads.  Pairs past the last row repeat the last row
-// (identical bytes), so all pairs of a workgroup always pass the same barriers.
+// dependency chains; splitting each row doubles the waves and halves each chain.
+//
+// Linear layout: wave h takes the row half j = 2048 h + [0, 2048) as four 512-element
+// fragments, and lane l loads the 16 bytes 512 f + 8 l of fragment f, so every wave load and
+// store covers contiguous bytes in lane order.  In the MFMA A layout (row = lane & 15,
+// k = 8 (lane >> 4) + e) that puts element bits 3-6 in the row and bits {0, 1, 2, 7, 8} in k:
+// stage 1 transforms those five bits, stage 2 (same operand tables) bits {3, 4, 5, 6, 9}, and
+// afterwards lane l holds the eight consecutive outputs 8 l + [0, 8) of every 512-element
+// chunk.  (Any assignment of index bits to the stages gives the same Sylvester transform: the
+// transform is a product of independent butterflies, one per bit.)
+//
+// Order of work: the constant operands and the signs (L2 hits) go out first, then the row's
+// four fragments; each fragment's stage 1 runs as soon as it lands, with its share of the
+// split-scale maximum.  Bit 10 (the fragment pair) is folded into stage 2 on the matrix
+// cores: the outputs with bit 10 = 0 are A0 B + A1 B and those with bit 10 = 1 are A0 B - A1 B,
+// so the two products share the A0 B partial and the second uses the negated operand.
+// Bit 11 pairs the halves: wave h keeps its partial sums for the output chunks with bit 10 = h,
+// sends the others through LDS, and both sides go to the smaller of the two split scales
+// (powers of two, exact).  Wave h then owns the output chunks 1024 (2 h' + h) + [0, 1024),
+// h' = 0, 1.  Per-row INT4 takes the row maximum over both waves through LDS.  Pairs past the
+// last row repeat the last row (identical bytes), so all pairs of a workgroup always pass the
+// same barriers.
 // ---------------------------------------------------------------------------
 #ifndef RHTQ_PAIR_WAVES
 #define RHTQ_PAIR_WAVES 4
@@ -274,6 +286,9 @@ void fast2_kernel(KernelArgs a) {
 #define RHTQ_PAIR_RPW 1
 #endif
 constexpr int kPairRows = RHTQ_PAIR_RPW;   // rows per workgroup (two waves each)
+
+// Stands in for an absent sign vector (all +1: no sign bits), so the sign loads need no branch.
+__device__ __align__(16) int8_t kNoSigns[4096];
 
 struct PairShared {
   uint4 xch[2][4][64];   // [wave h][value quad][lane]
@@ -285,34 +300,36 @@ struct PairShared {
 // constants).
 template <int OP, int H>
 __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, int64_t row) {
-  constexpr int N = 4096, NF = 8;
+  constexpr int N = 4096;
   const int lane = threadIdx.x & 63;
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)N));
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  const int lcol = 32 * (lane & 15) + 8 * (lane >> 4);   // this lane's 8 elements within a fragment
+  const int lcol = 8 * lane;   // this lane's 8 elements within a fragment
 
-  // the row's fragments and this lane's 32 signs go out together: the signs come from L2 (every
-  // row shares them), and no workgroup table or barrier stands before the row loads
-  const int slices = a.sign_period / N;
-  const int slice = slices > 1 ? (int)(row % slices) : 0;
-  uint4 raw[4];
-#pragma unroll
-  for (int fl = 0; fl < 4; ++fl) raw[fl] = ld_stream(x + row * N + 512 * (4 * H + fl) + lcol);
-  uint2 sv[4] = {};
-  if (a.signs) {
-#pragma unroll
-    for (int fl = 0; fl < 4; ++fl) sv[fl] = *reinterpret_cast<const uint2*>(a.signs + N * slice + 512 * (4 * H + fl) + lcol);
-  }
+  // constant operands and signs first (L2 hits), then the row's fragments; the scheduling
+  // barriers keep that order, so each fragment's wait covers only the loads ahead of it
   const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
   const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
+  const int slices = a.sign_period / N;
+  const int slice = slices > 1 ? (int)(row % slices) : 0;
+  const int8_t* sg = (a.signs ? a.signs + N * slice : kNoSigns) + 2048 * H + lcol;
+  uint2 sv[4];
+#pragma unroll
+  for (int fl = 0; fl < 4; ++fl) sv[fl] = *reinterpret_cast<const uint2*>(sg + 512 * fl);
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 raw[4];
+#pragma unroll
+  for (int fl = 0; fl < 4; ++fl) raw[fl] = ld_stream(x + row * N + 2048 * H + 512 * fl + lcol);
+  __builtin_amdgcn_sched_barrier(0);
   int G = 0;
   if constexpr (OP == OP_INT4) G = a.group == N ? 0 : __builtin_ctz((unsigned)a.group);
   if constexpr (OP == OP_NVFP4) G = 4;
   if constexpr (OP == OP_MXFP4) G = 5;
-  const int lc = (lane >> 4) | ((lane & 15) << 2);
 
-  // ---------------- stage 1 (fragments 4 H .. 4 H + 3) ----------------
+  // ---------------- stage 1, fragment by fragment as the loads land ----------------
+  // d1[f][t][i]: output column lane & 15 of tile t, row 4 (lane >> 4) + i
   float d1[4][2][4];
+  float m1 = 0.0f;
 #pragma unroll
   for (int fl = 0; fl < 4; ++fl) {
     uint4 r = raw[fl];
@@ -328,23 +345,37 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
     const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { d1[fl][0][i] = p0[i]; d1[fl][1][i] = p1[i]; }
+    // the previous fragment's maximum while this one's products run
+    if (fl > 0) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fabsf(d1[fl - 1][t][i]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  float m1 = 0.0f;
 #pragma unroll
-  for (int fl = 0; fl < 4; ++fl)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fabsf(d1[fl][t][i]));
+    for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fabsf(d1[3][t][i]));
   m1 = group_max(m1, 64);
   float S, invS;
   split_scale(__float_as_uint(m1), S, invS);
 
-  // ---------------- stage 2 + bit 10 ----------------
-  // d2[t][gl][t2][i2]: element t + 2 i2 + 8 lc + 512 t2 + 1024 gl of this half
+  // ---------------- stage 2 with bit 10 ----------------
+  // d2[t][gl][t2][i2]: element t + 2 i2 + 8 lane + 512 t2 + 1024 gl of this half
+  f16x8 hn[2];   // the stage-2 operands negated (f16 sign bits)
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+    u32x4 w;
+    __builtin_memcpy(&w, &hc[t2], 16);
+    w ^= 0x80008000u;
+    __builtin_memcpy(&hn[t2], &w, 16);
+  }
   float d2[2][2][2][4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 2; ++t) {
+    f16x8 ah[2], al[2];
 #pragma unroll
     for (int gl = 0; gl < 2; ++gl) {
       float ys[8];
@@ -352,24 +383,22 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
       for (int e = 0; e < 8; ++e) ys[e] = d1[2 * gl + (e >> 2)][t][e & 3];
       uint32_t hw[4], lw[4];
       split8(ys, S, hw, lw);
-      f16x8 ah, al;
-      __builtin_memcpy(&ah, hw, 16);
-      __builtin_memcpy(&al, lw, 16);
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, hc[t2], z, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, hc[t2], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d2[t][gl][t2][i] = acc[i];
-      }
+      __builtin_memcpy(&ah[gl], hw, 16);
+      __builtin_memcpy(&al[gl], lw, 16);
     }
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[0], hc[t2], z, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[0], hc[t2], p, 0, 0, 0);
+      f32x4 q0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[1], hc[t2], p, 0, 0, 0);
+      q0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[1], hc[t2], q0, 0, 0, 0);
+      f32x4 q1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[1], hn[t2], p, 0, 0, 0);
+      q1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[1], hn[t2], q1, 0, 0, 0);
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bfly(d2[t][0][t2][i], d2[t][1][t2][i]);
+      for (int i = 0; i < 4; ++i) { d2[t][0][t2][i] = q0[i]; d2[t][1][t2][i] = q1[i]; }
+    }
+  }
 
   // ---------------- bit 11: exchange halves ----------------
   // sent: the partial sums with bit-10 index 1 - H, as quads q = 2 t + t2
@@ -387,7 +416,7 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
   const bool own_common = S <= So;
   const float f = own_common ? S * __builtin_amdgcn_rcpf(So) : So * invS;   // power of two <= 1
   if (!own_common) invS = __builtin_amdgcn_rcpf(So);
-  // y2[hp][t][t2][i]: output element t + 2 i + 8 lc + 512 t2 + 1024 (2 hp + H)
+  // y2[hp][t][t2][i]: output element t + 2 i + 8 lane + 512 t2 + 1024 (2 hp + H)
   float y2[2][2][2][4];
   float r16[4][4];
 #pragma unroll
@@ -441,7 +470,7 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
       float o[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) o[r] = (val(q, r) * invS) * cnorm;
-      float* p = a.y + ebase + cbase(q) + 8 * lc;
+      float* p = a.y + ebase + cbase(q) + 8 * lane;
       st_stream(p, o[0], o[1], o[2], o[3]);
       st_stream(p + 4, o[4], o[5], o[6], o[7]);
     }
@@ -451,7 +480,7 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
       gts = a.tensor_scale[0];
       inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
     }
-    quant_epilogue<OP, 4>(a, row, ebase, G, invS, cnorm, gts, inv6g, lane, lane == 0 && H == 0, val, cbase,
+    quant_epilogue_lin<OP, 4>(a, row, ebase, G, invS, cnorm, gts, inv6g, lane, lane == 0 && H == 0, val, cbase,
                           [&](float m) {
                             const float wm = group_max(m, 64);
                             if (lane == 0) sh.rmax[H] = wm;
