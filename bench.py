@@ -235,6 +235,9 @@ def cpu_baseline(name, budget_s=10.0, procs=None):
             os.environ["OMP_NUM_THREADS"] = env_before
     pooled = sum(r * per_input / e for r, e in res)
     return {"value": pooled, "unit": "tokens/s", "cores": procs, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(),
+            "cores_note": "the pool is capped at 16 processes: the GPU host's share of CPU per GPU is 16 "
+                          "cores, whatever os.cpu_count() reports for the whole machine",
             "sample": f"{procs} single-threaded processes at once, each repeating the numpy fp64 oracle over the "
                       f"full {w.tokens}x{w.n} {w.in_dtype} input of {name} for {budget_s:.0f} s "
                       f"({sum(r for r, _ in res)} repetitions in all)",

@@ -67,7 +67,8 @@ struct alignas(16) H32Operands {
   uint16_t b1[2][64][8];
   uint16_t b16[2][64][8];
   uint16_t s2[2][64][8];
-  constexpr H32Operands() : b1(), b16(), s2() {
+  uint16_t s2n[2][64][8];   // s2 negated
+  constexpr H32Operands() : b1(), b16(), s2(), s2n() {
     for (int t = 0; t < 2; ++t)
       for (int lane = 0; lane < 64; ++lane)
         for (int e = 0; e < 8; ++e) {
@@ -76,6 +77,7 @@ struct alignas(16) H32Operands {
           b16[t][lane][e] = ((xk ^ o) & 16) ? 0x0000 : ((__builtin_popcount(xk & o & 15) & 1) ? 0xBF80 : 0x3F80);
           const int k = (e & 3) | ((lane >> 4) << 2) | ((e >> 2) << 4), n = (lane & 15) | (t << 4);
           s2[t][lane][e] = (__builtin_popcount(k & n) & 1) ? 0xBC00 : 0x3C00;
+          s2n[t][lane][e] = (uint16_t)(s2[t][lane][e] ^ 0x8000);
         }
   }
 };
@@ -206,6 +208,13 @@ __device__ __forceinline__ float group_max(float v, int G) {
 __device__ __forceinline__ f16x8 h32_stage2_operand(int lane, int t2) {
   f16x8 r;
   __builtin_memcpy(&r, &kH32Ops.s2[t2][lane][0], 16);
+  return r;
+}
+
+// The stage-2 operand negated.
+__device__ __forceinline__ f16x8 h32_stage2_operand_neg(int lane, int t2) {
+  f16x8 r;
+  __builtin_memcpy(&r, &kH32Ops.s2n[t2][lane][0], 16);
   return r;
 }
 

@@ -234,7 +234,7 @@ __device__ __forceinline__ void quant_epilogue_lin(const KernelArgs& a, const in
       }
     }
   }
-  uint8_t* prow = a.packed + (relem0 >> 1);
+  uint8_t* const pl = a.packed + (relem0 >> 1) + 4 * lane;   // this lane's dword of chunk 0
   if constexpr (OP == OP_INT4) {
     const bool any_clamp = __builtin_amdgcn_ballot_w64(clamp) != 0;
 #pragma unroll
@@ -248,7 +248,7 @@ __device__ __forceinline__ void quant_epilogue_lin(const KernelArgs& a, const in
         for (int r = 0; r < 8; ++r)
           qb[r] = __float_as_uint(__builtin_amdgcn_fmed3f(val(q, r) * inv[q], -8.0f, 7.0f) + 12582912.0f);
       }
-      st_stream(prow + (cbase(q) >> 1) + 4 * lane, pack8_nibbles(qb));
+      st_stream(pl + (cbase(q) >> 1), pack8_nibbles(qb));
     }
   } else {
 #pragma unroll
@@ -259,7 +259,7 @@ __device__ __forceinline__ void quant_epilogue_lin(const KernelArgs& a, const in
       w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(q, 2) * s, val(q, 3) * s, 1.0f, 1);
       w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(q, 4) * s, val(q, 5) * s, 1.0f, 2);
       w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(q, 6) * s, val(q, 7) * s, 1.0f, 3);
-      st_stream(prow + (cbase(q) >> 1) + 4 * lane, s > 0.0f ? w : 0u);
+      st_stream(pl + (cbase(q) >> 1), s > 0.0f ? w : 0u);
     }
   }
 }

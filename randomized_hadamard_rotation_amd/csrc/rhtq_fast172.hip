@@ -60,23 +60,27 @@ __host__ __device__ constexpr int xrow(int b) { return b * kPitch + 16 * ((b >> 
 constexpr int kChunks = kN / 8;                  // 16-byte chunks per row
 constexpr int kLoads = (kChunks + kT - 1) / kT;  // loads per thread and row
 
-__constant__ H172Bits<false> kH172Rows;
-
-// Stage-1 B operand for output tile t and K-step ks: slot e of lane group g stands for
-// a = 32 ks + 8 g + e, column n = lane & 15 for a' = 16 t + n; H172[a'][a] as bf16 +-1,
-// zero outside 172 x 172.
-__device__ bf16x8 h172t_operand(int lane, int t, int ks) {
-  const int ap = 16 * t + (lane & 15), g = lane >> 4;
-  uint16_t bits[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int k = 32 * ks + 8 * g + e;
-    uint16_t v = 0;
-    if (k < 172 && ap < 172) v = ((kH172Rows.w[ap][k >> 5] >> (k & 31)) & 1u) ? 0xBF80 : 0x3F80;
-    bits[e] = v;
+// Stage-1 B operand for output tile t and K-step ks, as a compile-time table (one 16-byte load
+// per operand; built lane by lane from bits, each entry cost a dependent load at kernel start):
+// slot e of lane group g stands for a = 32 ks + 8 g + e, column n = lane & 15 for
+// a' = 16 t + n; H172[a'][a] as bf16 +-1, zero outside 172 x 172.
+struct H172TOperands {
+  uint16_t v[kTiles][6][64][8];
+  constexpr H172TOperands() : v() {
+    for (int t = 0; t < kTiles; ++t)
+      for (int ks = 0; ks < 6; ++ks)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int e = 0; e < 8; ++e) {
+            const int ap = 16 * t + (lane & 15), k = 32 * ks + 8 * (lane >> 4) + e;
+            v[t][ks][lane][e] = (k < 172 && ap < 172) ? (h172_entry(ap, k) < 0 ? 0xBF80 : 0x3F80) : 0;
+          }
   }
+};
+__constant__ H172TOperands kH172TOps;
+
+__device__ __forceinline__ bf16x8 h172t_operand(int lane, int t, int ks) {
   bf16x8 r;
-  __builtin_memcpy(&r, bits, 16);
+  __builtin_memcpy(&r, &kH172TOps.v[t][ks][lane][0], 16);
   return r;
 }
 

@@ -298,7 +298,7 @@ struct PairShared {
 
 // Wave H's half of one row (H a template parameter so every register array is indexed by
 // constants).
-template <int OP, int H>
+template <int OP, int H, bool SLICED>
 __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, int64_t row) {
   constexpr int N = 4096;
   const int lane = threadIdx.x & 63;
@@ -310,8 +310,11 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
   // barriers keep that order, so each fragment's wait covers only the loads ahead of it
   const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
   const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
-  const int slices = a.sign_period / N;
-  const int slice = slices > 1 ? (int)(row % slices) : 0;
+  const f16x8 hn[2] = {h32_stage2_operand_neg(lane, 0), h32_stage2_operand_neg(lane, 1)};
+  // SLICED: the rows are blocks of longer rows, and the block's slice of the sign vector
+  // depends on the row (a 64-bit remainder, kept out of the plain call's code)
+  int slice = 0;
+  if constexpr (SLICED) slice = (int)(row % (a.sign_period / N));
   const int8_t* sg = (a.signs ? a.signs + N * slice : kNoSigns) + 2048 * H + lcol;
   uint2 sv[4];
 #pragma unroll
@@ -364,14 +367,6 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
 
   // ---------------- stage 2 with bit 10 ----------------
   // d2[t][gl][t2][i2]: element t + 2 i2 + 8 lane + 512 t2 + 1024 gl of this half
-  f16x8 hn[2];   // the stage-2 operands negated (f16 sign bits)
-#pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2) {
-    u32x4 w;
-    __builtin_memcpy(&w, &hc[t2], 16);
-    w ^= 0x80008000u;
-    __builtin_memcpy(&hn[t2], &w, 16);
-  }
   float d2[2][2][2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -490,14 +485,14 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
   }
 }
 
-template <int OP>
+template <int OP, bool SLICED>
 __global__ __launch_bounds__(128 * kPairRows) __attribute__((amdgpu_waves_per_eu(RHTQ_PAIR_WAVES))) void fast2p_kernel(KernelArgs a) {
   __shared__ PairShared sh[kPairRows];
   const int wave = threadIdx.x >> 6, pair = wave >> 1;
   int64_t row = kPairRows * (int64_t)blockIdx.x + pair;
   if (row >= a.rows) row = a.rows - 1;   // past the end: repeat the last row (same bytes, same barriers)
-  if (wave & 1) pair_row<OP, 1>(a, sh[pair], row);
-  else pair_row<OP, 0>(a, sh[pair], row);
+  if (wave & 1) pair_row<OP, 1, SLICED>(a, sh[pair], row);
+  else pair_row<OP, 0, SLICED>(a, sh[pair], row);
 }
 
 template <int OP>
@@ -506,8 +501,9 @@ hipError_t launch2p(const KernelArgs& a, hipStream_t s) {
     if (!(a.group == 4096 || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
   if (a.rows > 0xFFFFFFFE) return hipErrorNotSupported;
-  hipLaunchKernelGGL(fast2p_kernel<OP>, dim3((unsigned)((a.rows + kPairRows - 1) / kPairRows)), dim3(128 * kPairRows), 0, s,
-                     a);
+  const dim3 grid((unsigned)((a.rows + kPairRows - 1) / kPairRows));
+  if (a.sign_period == 4096) hipLaunchKernelGGL((fast2p_kernel<OP, false>), grid, dim3(128 * kPairRows), 0, s, a);
+  else hipLaunchKernelGGL((fast2p_kernel<OP, true>), grid, dim3(128 * kPairRows), 0, s, a);
   return hipGetLastError();
 }
 
