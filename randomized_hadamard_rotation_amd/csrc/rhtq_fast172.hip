@@ -542,6 +542,438 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 
   }
 }
 
+// ---------------------------------------------------------------------------
+// 22016 = 172 x 128 (H172 (x) H128): element j = 128 a + b, b < 128.  H128 = H2 (x) H64 with
+// the top bit c of b = 64 c + d outer, and the factors commute, so a row is its two halves
+// c = 0, 1 (172 x 64 each, element 128 a + 64 c + d), each taken through the same LDS buffer
+// and the same stage 1 (H172 over a) as an 11008 row; one butterfly between the two halves'
+// stage-1 results applies the H2, and each half then runs the 11008 stage 2 (H64 over d) and
+// epilogue on its own output half-row 128 a' + 64 c' + [0, 64).  Groups of 64 lie in a half,
+// groups of 128 .. 512 are 1 .. 4 whole a'-rows (both halves); the per-token maximum spans both.
+// ---------------------------------------------------------------------------
+constexpr int kN2 = 2 * kN;          // 22016
+constexpr int kChunks2 = 2 * kChunks;
+
+template <int OP, int GC, int SD, int NT>
+__device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const float cnorm = (float)(1.0 / __builtin_sqrt((double)kN2));
+  const int64_t rows = a.rows;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+
+  const f16x8 ha[2] = {h32_b_operand<false>(lane, 0), h32_b_operand<false>(lane, 1)};
+
+  float gts = 0.0f, inv6g = 0.0f;
+  if constexpr (OP == OP_NVFP4) {
+    gts = a.tensor_scale[0];
+    inv6g = gts > 0.0f ? 1.0f / (6.0f * gts) : 0.0f;
+  }
+  const int LG = GC == 6 ? __builtin_ctz((unsigned)a.group) : GC;   // log2 of the group
+  float run_max = 0.0f;
+
+  // half h of a row: chunk c < kChunks holds a = c >> 3 and d = 8 (c & 7) .. + 7, the elements
+  // 128 a + 64 h + d
+  uint4 raw[kLoads];
+  auto load = [&](int64_t row, int h) {
+    if (row >= rows) return;
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int c = tid + kT * k;
+      if (c < kChunks) raw[k] = ld_stream(x + row * kN2 + 128 * (c >> 3) + 64 * h + 8 * (c & 7));
+    }
+  };
+  uint8_t* wbase = xs + xrow(8 * (tid & 7)) + 2 * (tid >> 3);
+  const uint8_t* rbase_l[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) rbase_l[mt] = xs + xrow(16 * mt + n) + 16 * g;
+  auto write_lds = [&](int h) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int c = tid + kT * k;
+      if (c < kChunks) {
+        const uint4 m = sgn[kChunks * h + c];
+        const uint32_t w[4] = {raw[k].x ^ m.x, raw[k].y ^ m.y, raw[k].z ^ m.z, raw[k].w ^ m.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint16_t*>(wbase + e * kPitch + (kT / 4) * k) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  };
+  // stage 1 (H172 over a) of the half in LDS; the H172^T operands are loaded (L2 hits) for each
+  // pass rather than held, which leaves the registers to the two halves' results
+  auto stage1 = [&](f32x4 (&acc)[NT][4]) {
+    // an opaque zero keeps the compiler from hoisting these loads out of the row loop
+    int t0 = wave;
+    asm volatile("" : "+v"(t0));
+    bf16x8 hb[NT][6];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand(lane, t0 + kW * j, ks);
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks) {
+      bf16x8 av[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) av[mt] = *reinterpret_cast<const bf16x8*>(rbase_l[mt] + 64 * ks);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], hb[j][ks], ks == 0 ? z : acc[j][mt], 0, 0, 0);
+        }
+    }
+  };
+
+  int64_t row = blockIdx.x;
+  load(row, 0);
+  __syncthreads();   // sign masks and zeroed rows
+  if (row < rows) write_lds(0);
+  load(row, 1);
+  __syncthreads();
+  // per row: stage 1 of half 0 (in LDS); half 1 (in raw[]) goes in after the barrier that ends
+  // those reads, and the next row's half 0 is loaded; stage 1 of half 1; the next row's half 0
+  // goes in and its half 1 is loaded; then the H2 butterfly, stage 2 and the epilogue run from
+  // registers
+  for (; row < rows; row += gridDim.x) {
+    f32x4 acc[2][NT][4];
+    stage1(acc[0]);
+    __syncthreads();   // every wave has read half 0
+    write_lds(1);
+    load(row + gridDim.x, 0);
+    __syncthreads();
+    stage1(acc[1]);
+    __syncthreads();   // every wave has read half 1
+    if (row + gridDim.x < rows) write_lds(0);
+    load(row + gridDim.x, 1);
+
+    // H2 over c: half 0 <- half 0 + half 1, half 1 <- half 0 - half 1
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = acc[0][j][mt][i], q = acc[1][j][mt][i];
+          acc[0][j][mt][i] = p + q;
+          acc[1][j][mt][i] = p - q;
+        }
+
+    // ---------------- stage 2 per half: H2 by butterfly, H32 on the matrix cores ----------------
+    float d2a[2][NT][4][4];   // [half][tile][run r][i]: b'' = 16 r + 4 g + i of the half
+    float invS_t[2][NT];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float u[NT][2][2][4];
+      float S[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        float m = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = acc[c][j][h][i], q = acc[c][j][h + 2][i];
+            u[j][0][h][i] = p + q;
+            u[j][1][h][i] = p - q;
+            m = fmaxf(m, fmaxf(fabsf(p + q), fabsf(p - q)));
+          }
+        S[j] = m;
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) split_scale(__float_as_uint(col_max(S[j])), S[j], invS_t[c][j]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float ys[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ys[e] = u[j][h][e >> 2][e & 3];
+          uint32_t hw[4], lw[4];
+          split8(ys, S[j], hw, lw);
+          f16x8 bh, bl;
+          __builtin_memcpy(&bh, hw, 16);
+          __builtin_memcpy(&bl, lw, 16);
+#pragma unroll
+          for (int mt2 = 0; mt2 < 2; ++mt2) {
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[mt2], bh, z, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[mt2], bl, o, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d2a[c][j][2 * h + mt2][i] = o[i];
+          }
+        }
+    }
+
+    // per-token INT4: one scale per row, from the maximum over both halves of every tile of the
+    // four waves (columns a' >= 172 are zero); all waves pass this barrier, GC being uniform
+    float row_inv = 0.0f;
+    bool row_clamp = false;
+    if constexpr (OP == OP_INT4 && GC == 0) {
+      float m = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float mj = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mj = fmaxf(mj, fabsf(d2a[c][j][r][i]));
+            m = nnmax(m, mj * invS_t[c][j]);
+          }
+      m = group_max(m, 64);
+      if (lane == 0) wmax[wave] = m;
+      __syncthreads();
+      float rm = wmax[0];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) rm = nnmax(rm, wmax[w]);
+      const Int4Scale sc = int4_scale(rm, cnorm, SD);
+      row_inv = sc.inv;
+      row_clamp = sc.clamp;
+      if (tid == 0) {
+        if constexpr (SD == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[row] = sc.s;
+        else static_cast<__half*>(a.scales)[row] = __float2half_rn(fminf(sc.s, 65504.0f));
+      }
+    }
+
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int ap = 16 * (wave + kW * j) + n;
+      const bool valid = ap < 172;
+      // run r of half c: elements rstart(c, r) + 4 g + i
+      auto rstart = [&](int c, int r) -> int64_t { return row * kN2 + 128 * ap + 64 * c + 16 * r; };
+      if constexpr (OP == OP_ROTATE) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float f = invS_t[c][j] * cnorm;
+            const float* d = d2a[c][j][r];
+            if (valid) st_stream(a.y + rstart(c, r) + 4 * g, d[0] * f, d[1] * f, d[2] * f, d[3] * f);
+          }
+        continue;
+      }
+      float mr[2][4];   // run maxima, split units
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float* d = d2a[c][j][r];
+          mr[c][r] = fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3])));
+        }
+      if constexpr (OP == OP_AMAX) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) run_max = nnmax(run_max, mr[c][r] * invS_t[c][j]);
+        continue;
+      }
+
+      // ---------------- group scales, once per group ----------------
+      // sl[c][r]: factor from the split units of half c to code units for run r (0 for an
+      // all-zero group); scale_of returns that factor for unit split scale (true units)
+      float sl[2][4];
+      bool clamp = false;
+      auto scale_of = [&](float bm, int64_t gi, bool writer) -> float {
+        if constexpr (OP == OP_INT4) {
+          const Int4Scale sc = int4_scale(bm, cnorm, SD);
+          clamp |= sc.clamp;
+          if (writer) {
+            if constexpr (SD == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[gi] = sc.s;
+            else static_cast<__half*>(a.scales)[gi] = __float2half_rn(fminf(sc.s, 65504.0f));
+          }
+          return sc.inv;
+        } else if constexpr (OP == OP_NVFP4) {
+          const uint32_t code = e4m3_code((bm * cnorm) * inv6g);
+          const float seff = e4m3_value(code) * gts;
+          if (writer) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)code;
+          return seff > 0.0f ? cnorm * __builtin_amdgcn_rcpf(seff) : 0.0f;
+        } else {
+          const float bt = bm * cnorm;
+          const int ex = mx_exponent(bt);
+          if (writer) static_cast<uint8_t*>(a.scales)[gi] = (uint8_t)(ex + 127);
+          return bt > 0.0f ? __builtin_ldexpf(cnorm, -ex) : 0.0f;
+        }
+      };
+      if constexpr (GC == 0) {   // the row's scale, in each half's split units
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sl[c][r] = row_inv * invS_t[c][j];
+        clamp = row_clamp;
+      } else if constexpr (GC == 4) {   // a run per group; lane group g stores the scale of run g
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sl[c][r] = scale_of(col_max(mr[c][r]) * invS_t[c][j], rstart(c, r) >> 4, valid && g == r) * invS_t[c][j];
+      } else if constexpr (GC == 5) {   // two runs per group; lane groups 0 and 1 store
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float s0 = scale_of(col_max(nnmax(mr[c][0], mr[c][1])) * invS_t[c][j], rstart(c, 0) >> 5, valid && g == 0);
+          const float s1 = scale_of(col_max(nnmax(mr[c][2], mr[c][3])) * invS_t[c][j], rstart(c, 2) >> 5, valid && g == 1);
+          sl[c][0] = sl[c][1] = s0 * invS_t[c][j];
+          sl[c][2] = sl[c][3] = s1 * invS_t[c][j];
+        }
+      } else {   // 64: a half a'-row; 128 .. 512: 1 .. 4 whole a'-rows (lane bits 0-1 for a')
+        float mh[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          mh[c] = col_max(nnmax(nnmax(mr[c][0], mr[c][1]), nnmax(mr[c][2], mr[c][3]))) * invS_t[c][j];
+        if (LG == 6) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float f = scale_of(mh[c], rstart(c, 0) >> 6, valid && g == 0);
+            sl[c][0] = sl[c][1] = sl[c][2] = sl[c][3] = f * invS_t[c][j];
+          }
+        } else {
+          float mm = nnmax(mh[0], mh[1]);
+          if (LG >= 8) mm = dpp_max<0xB1>(mm);   // a' pairs (lane xor 1)
+          if (LG >= 9) mm = dpp_max<0x4E>(mm);   // a' quads (lane xor 2)
+          const float f = scale_of(mm, rstart(0, 0) >> LG, valid && g == 0 && (ap & ((1 << (LG - 7)) - 1)) == 0);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) sl[c][0] = sl[c][1] = sl[c][2] = sl[c][3] = f * invS_t[c][j];
+        }
+      }
+
+      // ---------------- codes per half, stored as the half's 32-byte a'-row ----------------
+      bool any_clamp = false;
+      if constexpr (OP == OP_INT4) any_clamp = __builtin_amdgcn_ballot_w64(clamp) != 0;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const auto& d2 = d2a[c][j];
+        uint32_t p01, p23;
+        if constexpr (OP == OP_INT4) {
+          uint32_t q[4][4];
+          if (!any_clamp) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) q[r][i] = __float_as_uint(__builtin_fmaf(d2[r][i], sl[c][r], 12582912.0f));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                q[r][i] = __float_as_uint(__builtin_amdgcn_fmed3f(d2[r][i] * sl[c][r], -8.0f, 7.0f) + 12582912.0f);
+          }
+          const uint32_t q01[8] = {q[0][0], q[0][1], q[0][2], q[0][3], q[1][0], q[1][1], q[1][2], q[1][3]};
+          const uint32_t q23[8] = {q[2][0], q[2][1], q[2][2], q[2][3], q[3][0], q[3][1], q[3][2], q[3][3]};
+          p01 = pack8_nibbles(q01);
+          p23 = pack8_nibbles(q23);
+        } else {
+          uint32_t w[2] = {0u, 0u};
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+              const int r = 2 * h + rr;
+              const float sv = sl[c][r];
+              uint32_t t = 0;
+              t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, d2[r][0] * sv, d2[r][1] * sv, 1.0f, 0);
+              t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, d2[r][2] * sv, d2[r][3] * sv, 1.0f, 1);
+              w[h] |= (sv > 0.0f ? (t & 0xFFFFu) : 0u) << (16 * rr);   // zero-scale group -> code 0
+            }
+          }
+          p01 = w[0];
+          p23 = w[1];
+        }
+        // lane group g keeps runs g & 1 and 2 + (g & 1), sends the other two to g ^ 1 and
+        // receives the partner's halves of its own runs, then lane groups g and g ^ 2 trade so
+        // that lane group g holds bytes 8 g .. 8 g + 7 of the half's 32-byte a'-row
+        const bool odd = g & 1;
+        const uint32_t send = __builtin_amdgcn_perm(p23, p01, odd ? 0x05040100u : 0x07060302u);
+        const uint32_t keep = __builtin_amdgcn_perm(p23, p01, odd ? 0x07060302u : 0x05040100u);
+        auto pr = __builtin_amdgcn_permlane16_swap(send, send, false, false);
+        const uint32_t recv = odd ? pr[0] : pr[1];
+        const uint32_t lo = odd ? recv : keep, hi = odd ? keep : recv;
+        const uint32_t w0 = __builtin_amdgcn_perm(hi, lo, 0x05040100u), w1 = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+        const bool upper = g & 2;
+        const uint32_t send2 = upper ? w0 : w1;
+        auto pr2 = __builtin_amdgcn_permlane32_swap(send2, send2, false, false);
+        const uint32_t recv2 = upper ? pr2[0] : pr2[1];
+        if (valid) st_stream(a.packed + ((row * kN2 + 128 * ap + 64 * c) >> 1) + 8 * g, upper ? recv2 : w0, upper ? w1 : recv2);
+      }
+    }
+    __syncthreads();   // the next row's half 0 is in LDS
+  }
+
+  if constexpr (OP == OP_AMAX) {
+    run_max = group_max(run_max, 64);
+    if (lane == 0) wmax[wave] = run_max;
+    __syncthreads();
+    if (tid == 0) {
+      float mm = wmax[0];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) mm = nnmax(mm, wmax[w]);
+      atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale), __float_as_uint(nvfp4_tensor_scale(mm * cnorm)));
+    }
+  }
+}
+
+template <int OP, int GC, int SD>
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 : 4))) void fast344_kernel(KernelArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
+  __shared__ uint4 sgn[kChunks2];
+  __shared__ float wmax[kW];
+  const int tid = threadIdx.x;
+  for (int c = tid; c < kChunks2; c += kT) {
+    uint4 m = make_uint4(0, 0, 0, 0);
+    if (a.signs) {
+      // chunk c of half h: elements 128 a + 64 h + d, a = cc >> 3, d = 8 (cc & 7) .. + 7
+      const int h = c / kChunks, cc = c % kChunks;
+      const uint2 sv = *reinterpret_cast<const uint2*>(a.signs + 128 * (cc >> 3) + 64 * h + 8 * (cc & 7));
+      m.x = __builtin_amdgcn_perm(0u, sv.x, 0x010C000Cu) & 0x80008000u;
+      m.y = __builtin_amdgcn_perm(0u, sv.x, 0x030C020Cu) & 0x80008000u;
+      m.z = __builtin_amdgcn_perm(0u, sv.y, 0x010C000Cu) & 0x80008000u;
+      m.w = __builtin_amdgcn_perm(0u, sv.y, 0x030C020Cu) & 0x80008000u;
+    }
+    sgn[c] = m;
+  }
+  for (int c = tid; c < kXBytes / 16; c += kT) reinterpret_cast<uint4*>(xs)[c] = make_uint4(0, 0, 0, 0);   // a >= 172 stays 0
+  if constexpr (kTiles % kW == 0) {
+    rows344<OP, GC, SD, kNT>(a, xs, sgn, wmax);
+  } else {
+    if ((tid >> 6) < kTiles % kW) rows344<OP, GC, SD, kNT>(a, xs, sgn, wmax);
+    else rows344<OP, GC, SD, kNT - 1>(a, xs, sgn, wmax);
+  }
+}
+
+template <int OP, int GC, int SD>
+hipError_t launch344(const KernelArgs& a, hipStream_t s) {
+  auto kern = fast344_kernel<OP, GC, SD>;
+  static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
+  const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int SD>
+hipError_t launch344_int4(const KernelArgs& a, hipStream_t s) {
+  if (a.group == kN2) return launch344<OP_INT4, 0, SD>(a, s);   // one group per row
+  switch (a.group) {
+    case 16: return launch344<OP_INT4, 4, SD>(a, s);
+    case 32: return launch344<OP_INT4, 5, SD>(a, s);
+    case 64: case 128: case 256: case 512: return launch344<OP_INT4, 6, SD>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch344_op(int op, const KernelArgs& a, hipStream_t s) {
+  switch (op) {
+    case OP_ROTATE: return launch344<OP_ROTATE, 6, 0>(a, s);
+    case OP_INT4:
+      return a.scale_dtype == RHTQ_SCALE_F32 ? launch344_int4<RHTQ_SCALE_F32>(a, s)
+                                             : launch344_int4<RHTQ_SCALE_F16>(a, s);
+    case OP_NVFP4: return launch344<OP_NVFP4, 4, 0>(a, s);
+    case OP_MXFP4: return launch344<OP_MXFP4, 5, 0>(a, s);
+    case OP_AMAX: return launch344<OP_AMAX, 6, 0>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
 template <int P, int OP, int GC, int SD>
 hipError_t launch172(const KernelArgs& a, hipStream_t s) {
   auto kern = fast172_kernel<P, OP, GC, SD>;
@@ -584,6 +1016,8 @@ hipError_t launch172_p(int op, const KernelArgs& a, hipStream_t s) {
 hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s) {
   if (reinterpret_cast<uintptr_t>(a.x) & 15) return hipErrorNotSupported;
   if (a.n == kN && a.sign_period == kN) return launch172_p<1>(op, a, s);
+  // 22016 = 172 x 128: the two 64-column halves of each row in turn
+  if (a.n == kN2 && a.sign_period == kN2) return launch344_op(op, a, s);
   // 5504 = 172 x 32 and 2752 = 172 x 16: two and four rows per work row
   if (a.n == kN / 2 && a.sign_period == kN / 2) return launch172_p<2>(op, a, s);
   if (a.n == kN / 4 && a.sign_period == kN / 4) return launch172_p<4>(op, a, s);

@@ -29,6 +29,7 @@ CASES = {
     "mxfp4_4096": 1024,
     "blockh128_4096_int4g128": 1024,
     "downproj7b_11008_int4g128": 512,
+    "wide172_22016_int4g128": 256,
 }
 
 

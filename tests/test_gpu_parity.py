@@ -154,7 +154,7 @@ def test_e3_closed_form(R, n, k):
 
 REDUCED = [("tiny_128_int4", 64), ("llama_4096_int4", 203), ("downproj_12288_int4g128", 37),
            ("kv_128_int4g128", 4099), ("nvfp4_4096", 131), ("mxfp4_4096", 131),
-           ("blockh128_4096_int4g128", 131), ("downproj7b_11008_int4g128", 37)]
+           ("blockh128_4096_int4g128", 131), ("downproj7b_11008_int4g128", 37), ("wide172_22016_int4g128", 37)]
 
 
 @pytest.mark.parametrize("name,tokens", REDUCED)
@@ -168,7 +168,7 @@ def test_workload_reduced(R, name, tokens):
 
 @pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
                                   "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128",
-                                  "downproj7b_11008_int4g128"])
+                                  "downproj7b_11008_int4g128", "wide172_22016_int4g128"])
 def test_workload_full_size_sampled(R, name):
     """Full-size input on the device in the same launch shape as the benchmark;
     the oracle checks sampled rows (first, last, every sink row it can find, random)."""
@@ -205,7 +205,8 @@ def test_workload_full_size_sampled(R, name):
 # (only those rows are copied to the host).
 BEYOND_INT32 = [("llama_4096_int4", 2 ** 19 + 5), ("mxfp4_4096", 2 ** 19 + 3), ("kv_128_int4g128", 2 ** 24 + 3),
                 ("downproj_12288_int4g128", 174763), ("downproj7b_11008_int4g128", 195085),
-                ("downproj_12288_int4g128:n=24576", 87385), ("downproj7b_11008_int4g128:n=5504", 390170)]
+                ("downproj_12288_int4g128:n=24576", 87385), ("downproj7b_11008_int4g128:n=5504", 390170),
+                ("wide172_22016_int4g128", 97548)]
 
 
 @pytest.mark.parametrize("name,tokens", BEYOND_INT32)
@@ -288,7 +289,7 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n", [8192, 16384, 11008, 5504, 2752, 12288, 24576])
+@pytest.mark.parametrize("n", [8192, 16384, 22016, 11008, 5504, 2752, 12288, 24576])
 def test_wide_rows_many_per_workgroup(R, n):
     """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 5504 and 2752 = 172 x 32 and 16 two
     and four rows at a time, 12288 = 12 x 1024, 24576 = 12 x 2048): 2503 rows (the last set of
@@ -327,7 +328,7 @@ def test_wide_rows_many_per_workgroup(R, n):
 
 INT4_GROUPS = ([(n, g) for n in (12288, 24576) for g in (0, 16, 32, 64, 128, 256, 512)]
                + [(11008, g) for g in (0, 16, 32, 64, 128, 256)] + [(5504, g) for g in (0, 16, 32, 64, 128)]
-               + [(2752, g) for g in (0, 16, 32, 64)])
+               + [(2752, g) for g in (0, 16, 32, 64)] + [(22016, g) for g in (0, 16, 32, 64, 128, 256, 512)])
 
 
 @pytest.mark.parametrize("n,group", INT4_GROUPS)
@@ -550,7 +551,8 @@ def test_deterministic(R):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128",
-                                  "nvfp4_4096", "mxfp4_4096", "downproj7b_11008_int4g128"])
+                                  "nvfp4_4096", "mxfp4_4096", "downproj7b_11008_int4g128",
+                                  "wide172_22016_int4g128"])
 def test_inverse_round_trip(R, name):
     import torch
     w = WORKLOADS[name]

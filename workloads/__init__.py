@@ -98,6 +98,10 @@ WORKLOADS = {
     "downproj7b_11008_int4g128": Workload(
         "downproj7b_11008_int4g128", 8192, 11008, "bf16", "llama_like", 8, 0, "int4", 128, "f16",
         description="8192 x 11008 bf16 (H172 x H64), llama-like recipe; INT4 group 128, fp16 scales"),
+    "wide172_22016_int4g128": Workload(
+        "wide172_22016_int4g128", 8192, 22016, "bf16", "llama_like", 9, 0, "int4", 128, "f16",
+        description="8192 x 22016 bf16 (H172 x H128, the next 172 x 2^k width above 11008), llama-like "
+                    "recipe; INT4 group 128, fp16 scales"),
     # MXFP4 on the NVFP4 shape: the thread compares the two FP4 formats on the same model
     "mxfp4_4096": Workload(
         "mxfp4_4096", 16384, 4096, "bf16", "llama_like", 6, 0, "mxfp4", 32, "e8m0",
