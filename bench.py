@@ -16,7 +16,9 @@ Prints ONE JSON line (rank 0).  `value` is tokens/s of the headline workload
 (2048 x 4096 bf16, per-token INT4); the d=12288, KV, NVFP4 (dynamic and with a
 given tensor scale), MXFP4, block-diagonal and d=11008 workloads and the KV
 inverse are reported under "also", and a plain 512 MiB device copy under
-"hbm_copy" as the bandwidth a streaming kernel reaches in practice.  The CPU oracle, timed on a bounded sample on the host,
+"hbm_copy" as the bandwidth a streaming kernel reaches in practice.  For the 4096- and
+12288-wide workloads, "same_grid_stream_floor" times rhtq_stream_floor: the same bytes moved
+with the forward kernel's grid and access pattern and no arithmetic, the floor of that shape.  The CPU oracle, timed on a bounded sample on the host,
 is reported as "cpu_baseline" (a baseline, not a target).
 """
 from __future__ import annotations
@@ -37,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 CACHE_DEFEAT_BYTES = 512 << 20
 HEADLINE = "llama_4096_int4"
 OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128",
-          "downproj7b_11008_int4g128"]
+          "downproj7b_11008_int4g128", "wide172_22016_int4g128"]
 KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast24.hip",
@@ -50,7 +52,9 @@ KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_generic.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_internal.h",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_api.cpp",
-                  "include/rhtq.h"]
+                  "randomized_hadamard_rotation_amd/csrc/rhtq_floor.hip",
+                  "include/rhtq.h",
+                  "include/rhtq_floor.h"]
 
 
 def kernel_source_hash() -> str:
@@ -163,6 +167,33 @@ def time_workload(R, torch, name, steps, warmup, graph=True, given=False, sha=Fa
     }
 
 
+def time_floor(R, torch, name, steps, warmup, graph=True):
+    """The streaming floor of the workload's launch shape (rhtq_stream_floor): the forward
+    kernel's grid, workgroup shape and access pattern moving the same bytes, with no arithmetic
+    beyond XOR folds.  Timed exactly as the workload is (same buffer-set rotation, graph replay)."""
+    from workloads import WORKLOADS, bytes_per_call
+    w = WORKLOADS[name]
+    nbytes = bytes_per_call(w)
+    sets = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / nbytes)))
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    xs = [torch.randn((w.tokens, w.n), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(sets)]
+    ng = 1 if w.group == 0 else w.n // w.group
+    sbytes = ng * {"f32": 4, "f16": 2}[w.scale_dtype]
+    outs = [(torch.empty((w.tokens, w.n // 2), dtype=torch.uint8, device="cuda"),
+             torch.empty((w.tokens, sbytes // 4), dtype=torch.int32, device="cuda")) for _ in range(sets)]
+
+    def step(i):
+        packed, scales = outs[i % sets]
+        R.rhtq_stream_floor(xs[i % sets], packed, scales)
+
+    ms, ms_eager = run_timed(torch, step, steps, warmup, graph)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "rhtq_stream_floor: same grid, workgroup shape and 16-byte non-temporal loads as the "
+                      "forward kernel, same bytes, XOR folds only", "ms_per_step": ms,
+            "bytes_per_call": nbytes, "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
+FLOORED = ["llama_4096_int4", "downproj_12288_int4g128"]   # widths rhtq_stream_floor covers
 INVERSE = ["kv_128_int4g128"]
 GIVEN = ["nvfp4_4096"]   # NVFP4 with the caller's tensor scale: one pass over x
 
@@ -354,11 +385,17 @@ def main():
 
     graph = not args.no_graph
     head = time_workload(R, torch, args.workload, args.steps, args.warmup, graph, given=args.given, sha=True)
+    if args.workload in FLOORED and not args.given:
+        head["same_grid_stream_floor"] = time_floor(R, torch, args.workload, args.steps, args.warmup, graph)
     also = []
     if not args.only:
         for name in OTHERS:
             if name != args.workload:
-                also.append(time_workload(R, torch, name, args.steps, args.warmup, graph))
+                rec = time_workload(R, torch, name, args.steps, args.warmup, graph)
+                if name in FLOORED:
+                    rec["same_grid_stream_floor"] = time_floor(R, torch, name, args.steps, args.warmup, graph)
+                    rec["over_floor"] = rec["ms_per_step"] / rec["same_grid_stream_floor"]["ms_per_step"]
+                also.append(rec)
         for name in GIVEN:
             also.append(time_workload(R, torch, name, args.steps, args.warmup, graph, given=True))
         for name in INVERSE:
@@ -390,6 +427,9 @@ def main():
         "launch": head["launch"],
         "eager_ms_per_step": head["eager_ms_per_step"],
         "roofline": roofline,
+        **({"same_grid_stream_floor": {**head["same_grid_stream_floor"],
+                                       "over_floor": head["ms_per_step"] / head["same_grid_stream_floor"]["ms_per_step"]}}
+           if "same_grid_stream_floor" in head else {}),
         "also": also,
     }
     if not args.only:

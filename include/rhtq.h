@@ -45,8 +45,9 @@
  *    the caller's next synchronisation, as usual for HIP.
  *  - The calls enqueue kernels only (no memset, copy or host synchronisation; the
  *    dynamic NVFP4 path clears its tensor-scale word with a kernel), so they can be
- *    captured into a HIP graph on a capturing stream.  The first call of each
- *    kernel variant queries occupancy on the host: make one call before capturing.
+ *    captured into a HIP graph on a capturing stream, the first call of a kernel
+ *    variant included (its one-time occupancy query is a host call that stream
+ *    capture permits).
  *  - Arguments are checked on the host before any HIP call; on error nothing is
  *    enqueued and the status says why.  tokens == 0 is a valid no-op.
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.

@@ -28,7 +28,7 @@ _DEFAULT_GROUP = {"nvfp4": 16, "mxfp4": 32}
 
 EXPORTED = ["rhtq_abi_version", "rhtq_status_str", "rhtq_supported", "rhtq_rotate",
             "rhtq_forward", "rhtq_inverse", "rhtq_signs_from_seed", "rhtq_rotate_blocked",
-            "rhtq_forward_blocked", "rhtq_inverse_blocked"]
+            "rhtq_forward_blocked", "rhtq_inverse_blocked", "rhtq_stream_floor"]
 
 
 class RhtqError(RuntimeError):
@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.rhtq_forward_blocked.argtypes = [vp, ci, i64, i32, i32, vp, ci, i32, ci, vp, vp, vp, ci, vp]
     lib.rhtq_inverse_blocked.restype = ci
     lib.rhtq_inverse_blocked.argtypes = [vp, vp, vp, i64, i32, i32, vp, ci, i32, ci, vp, vp]
+    lib.rhtq_stream_floor.restype = ci
+    lib.rhtq_stream_floor.argtypes = [vp, i64, i32, vp, vp, i32, vp]
     return lib
 
 
@@ -349,3 +351,26 @@ def rhtq_inverse(packed, scales, n: int, signs=None, fmt: str = "int4", group: i
     _keep_for(st, other, pc if pc is not packed else None, sc if sc is not scales else None,
               tc if (tc is not None and tc is not tensor_scale) else None, s, out if own else None)
     return out
+
+
+def rhtq_stream_floor(x, packed, scales, stream=None):
+    """The streaming floor of the forward call's launch shape (a measurement aid, not part of
+    the method): reads x bf16 [tokens][n] (n = 4096 or 12288) and writes packed uint8
+    [tokens][n/2] and the scale bytes of `scales` ([tokens][k], any dtype, 4 k * itemsize
+    bytes per row a multiple of 4) with the forward kernel's grid and access pattern and no
+    arithmetic beyond XOR folds of the loaded words.  Returns (packed, scales)."""
+    torch = _torch()
+    tokens, n = _rows(x)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    _expect(packed, "packed", torch.uint8, (tokens, n // 2))
+    if scales.dim() != 2 or scales.shape[0] != tokens or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous [tokens][k] tensor")
+    _same_device(x.device, x=x, packed=packed, scales=scales)
+    xc = x.contiguous()
+    st, other = _resolve_stream(stream)
+    row_bytes = scales.shape[1] * scales.element_size()
+    _check(lib.rhtq_stream_floor(_ptr(xc), tokens, n, _ptr(packed), _ptr(scales), row_bytes,
+                                 ctypes.c_void_p(st.cuda_stream)), "rhtq_stream_floor")
+    _keep_for(st, other, xc if xc is not x else None)
+    return packed, scales

@@ -262,6 +262,11 @@ hipError_t launch12(const KernelArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int64_t fast12_grid(int64_t rows) {
+  static const int max_blocks = resident_blocks((const void*)fast12_kernel<OP_INT4>, kT, 0);
+  return rows < max_blocks ? rows : max_blocks;
+}
+
 hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
     case OP_ROTATE: return launch12<OP_ROTATE>(a, s);

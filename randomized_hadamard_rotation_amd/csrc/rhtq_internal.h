@@ -48,6 +48,10 @@ hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
 // Two-wave kernel for 12288-wide rows (called by launch_fast).
 hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s);
 
+// The grid launch_fast12 uses for per-group INT4 on `rows` rows (resident workgroups, at most
+// one per row); the streaming-floor measurement launches the same grid.
+int64_t fast12_grid(int64_t rows);
+
 // Four-wave kernel for 24576-wide rows, H12 (x) H2048 (called by launch_fast).
 hipError_t launch_fast24(int op, const KernelArgs& a, hipStream_t s);
 

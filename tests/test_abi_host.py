@@ -17,13 +17,18 @@ def R():
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "rhtq.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(rhtq_\w+)\s*\(", src, re.M)))
+    inc = os.path.join(ROOT, "include")
+    names = set()
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            src = open(os.path.join(inc, h)).read()
+            names |= set(re.findall(r"^\s*(?:int|const char\*)\s+(rhtq_\w+)\s*\(", src, re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(R):
     decl = declared_functions()
-    assert len(decl) == 10
+    assert len(decl) == 11
     lib = ctypes.CDLL(R.LIB_PATH)
     for name in decl:
         assert hasattr(lib, name), name
@@ -109,6 +114,24 @@ def test_host_validation(R):
     assert I(None, fake, None, 4, 4096, None, 0, 0, 0, fake, s) == R.RHTQ_EINVAL
     assert I(None, None, None, 0, 4096, None, 0, 0, 0, None, s) == R.RHTQ_OK
     assert lib.rhtq_signs_from_seed(1, -1, None) == R.RHTQ_EINVAL
+
+
+def test_stream_floor_host_validation(R):
+    lib = R.lib
+    fake = ctypes.c_void_p(0x100000)          # never dereferenced: every call below fails validation
+    mis = ctypes.c_void_p(0x100002)
+    s = ctypes.c_void_p(0)
+    SF = lambda *a: lib.rhtq_stream_floor(*a)
+    assert SF(fake, 4, 2048, fake, fake, 4, s) == R.RHTQ_EUNSUPPORTED
+    assert SF(fake, 4, 11008, fake, fake, 4, s) == R.RHTQ_EUNSUPPORTED
+    assert SF(fake, -1, 4096, fake, fake, 4, s) == R.RHTQ_EINVAL
+    assert SF(fake, 4, 4096, fake, fake, 6, s) == R.RHTQ_EINVAL      # not a multiple of 4
+    assert SF(fake, 4, 4096, fake, fake, 0, s) == R.RHTQ_EINVAL
+    assert SF(fake, 4, 4096, fake, fake, 516, s) == R.RHTQ_EINVAL
+    assert SF(None, 4, 4096, fake, fake, 4, s) == R.RHTQ_EINVAL
+    assert SF(mis, 4, 4096, fake, fake, 4, s) == R.RHTQ_EINVAL       # x not 16-byte aligned
+    assert SF(fake, 4, 4096, mis, fake, 4, s) == R.RHTQ_EINVAL
+    assert SF(None, 0, 12288, None, None, 192, s) == R.RHTQ_OK       # empty: no-op
 
 
 def test_python_binding_refuses_cpu_tensors(R):

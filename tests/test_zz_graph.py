@@ -25,7 +25,7 @@ def test_graph_replay_matches_eager(name, tokens):
     packed = torch.empty_like(p_e)
     scales = torch.empty_like(sc_e)
     ts = None if ts_e is None else torch.empty_like(ts_e)
-    # warm up on the side (resident-block queries happen on the first call, before capture)
+    # an eager call with the graph's buffers first (the capture-first case has its own test)
     R.rhtq_forward(x, s_dev, fmt=w.fmt, group=w.group, scale_dtype=w.scale_dtype, tensor_scale=ts,
                    packed=packed, scales=scales)
     torch.cuda.synchronize()
@@ -46,3 +46,16 @@ def test_graph_replay_matches_eager(name, tokens):
         assert np.array_equal(scales.cpu().numpy(), ref[1]), f"replay {k}: scales"
         if ts is not None:
             assert np.array_equal(ts.cpu().numpy(), ref[2]), f"replay {k}: tensor scale"
+
+
+def test_first_call_inside_capture_fresh_process():
+    """The first call of each persistent kernel (whose grid comes from an occupancy query made on
+    that call) may be captured directly: no eager warm-up call is needed.  Runs in a fresh process
+    so that no earlier test has made those calls."""
+    import os
+    import subprocess
+    import sys
+    script = os.path.join(os.path.dirname(os.path.abspath(__file__)), "graph_first_call.py")
+    r = subprocess.run([sys.executable, script], capture_output=True, text=True, timeout=300)
+    print(r.stdout[-2000:])
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
