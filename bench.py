@@ -418,6 +418,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_note": "bf16 input; fp32 accumulation; the second matrix-core stage carries each value as two f16 "
+                      "terms under a power-of-two scale (22 significant bits); the worst rotation error against "
+                      "the fp64 oracle over every row of each workload is printed by tests/test_gpu_fullsize.py",
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": head["tokens"], "n": head["n"],
                    "in_dtype": head["in_dtype"], "fmt": head["fmt"], "group": head["group"],

@@ -77,9 +77,7 @@ def test_traffic_is_null_when_sources_changed(tmp_path, monkeypatch):
     assert bench.traffic_for("w_missing") is None
 
 
-@pytest.mark.parametrize("name", ["llama_4096_int4", "downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096",
-                                  "mxfp4_4096", "blockh128_4096_int4g128", "downproj7b_11008_int4g128",
-                                  "nvfp4_4096_given"])
+@pytest.mark.parametrize("name", [bench.HEADLINE] + bench.OTHERS + [g + "_given" for g in bench.GIVEN])
 def test_committed_profiles_cover_every_bench_workload(name):
     with open(os.path.join(ROOT, "profiles", f"{name}_traffic.json")) as f:
         d = json.load(f)
