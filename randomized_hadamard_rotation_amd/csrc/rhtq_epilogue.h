@@ -30,6 +30,28 @@ __device__ __forceinline__ void store_int4_scale(void* scales, int scale_dtype, 
   else static_cast<__half*>(scales)[gi] = __float2half_rn(fminf(s, 65504.0f));
 }
 
+// INT4 codes of R chunks in the layout above: inv[q] takes chunk q from split units to scale
+// units, clamp says this lane's group needs the [-8, 7] clamp (the clamp runs when any lane of
+// the wave needs it); one 4-byte store of eight codes per lane and chunk.
+template <int R, typename ValF, typename BaseF>
+__device__ __forceinline__ void int4_codes(uint8_t* prow, const float (&inv)[R], const bool clamp, const int lc,
+                                           ValF val, BaseF cbase) {
+  const bool any_clamp = __builtin_amdgcn_ballot_w64(clamp) != 0;
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    uint32_t qb[8];
+    if (!any_clamp) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) qb[r] = __float_as_uint(__builtin_fmaf(val(q, r), inv[q], 12582912.0f));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        qb[r] = __float_as_uint(__builtin_amdgcn_fmed3f(val(q, r) * inv[q], -8.0f, 7.0f) + 12582912.0f);
+    }
+    st_stream(prow + (cbase(q) >> 1) + 4 * lc, pack8_nibbles(qb));
+  }
+}
+
 // OP is OP_INT4, OP_NVFP4 or OP_MXFP4.  G = log2 of the group (0: one INT4 group per
 // row; NVFP4: 4; MXFP4: 5).
 // relem0: index of the row's first element in the tensor; N: row width.
@@ -150,20 +172,7 @@ __device__ __forceinline__ void quant_epilogue(const KernelArgs& a, const int64_
   // codes: 8 per lane and chunk -> one dword; a wave store covers 256 contiguous bytes
   uint8_t* prow = a.packed + (relem0 >> 1);
   if constexpr (OP == OP_INT4) {
-    const bool any_clamp = __builtin_amdgcn_ballot_w64(clamp) != 0;
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-      uint32_t qb[8];
-      if (!any_clamp) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) qb[r] = __float_as_uint(__builtin_fmaf(val(q, r), inv[q], 12582912.0f));
-      } else {
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          qb[r] = __float_as_uint(__builtin_amdgcn_fmed3f(val(q, r) * inv[q], -8.0f, 7.0f) + 12582912.0f);
-      }
-      st_stream(prow + (cbase(q) >> 1) + 4 * lc, pack8_nibbles(qb));
-    }
+    int4_codes<R>(prow, inv, clamp, lc, val, cbase);
   } else if constexpr (OP == OP_NVFP4 || OP == OP_MXFP4) {
 #pragma unroll
     for (int q = 0; q < R; ++q) {

@@ -45,11 +45,49 @@ struct Shared12 {
   float xbuf[kW][kX][64];               // exchange buffer, one step of each wave
   float xs[kW];                         // inverse split scale of each wave
   float rmax[kW];                       // per-token row maximum of each wave
+  float gmax[kW][kSub];                 // groups of whole sub-rows: each wave's group maxima
 };
+
+// INT4 groups of PER = 1, 2 or 4 whole sub-rows (1024, 2048 or 4096 elements).  A sub-row spans
+// both waves (wave h holds its half 512 h + [0, 512)), so each wave reduces its share of every
+// group over its lanes and the two shares meet in LDS, behind one barrier, as the per-token
+// maximum does.  Chunk q of this wave is sub-row q; val and cbase as for quant_epilogue.
+template <int PER, int H, typename ValF, typename BaseF>
+__device__ __forceinline__ void fast12_whole_subrow_groups(const KernelArgs& a, Shared12& sh, const int64_t row,
+                                                           const int64_t relem0, const float invS, const float cnorm,
+                                                           const int lane, const int lc, ValF val, BaseF cbase) {
+  constexpr int NGR = kSub / PER;   // groups per row
+  float gm[NGR];
+#pragma unroll
+  for (int k = 0; k < NGR; ++k) {
+    float m = 0.0f;
+#pragma unroll
+    for (int q = PER * k; q < PER * (k + 1); ++q)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(val(q, r)));
+    gm[k] = group_max(m, 64) * invS;   // this wave's half of group k, true units
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < NGR; ++k) sh.gmax[H][k] = gm[k];
+  }
+  __syncthreads();
+  float inv[kSub];
+  bool clamp = false;
+#pragma unroll
+  for (int k = 0; k < NGR; ++k) {
+    const Int4Scale sc = int4_scale(fmaxf(sh.gmax[0][k], sh.gmax[1][k]), cnorm, a.scale_dtype);
+    clamp |= sc.clamp;
+#pragma unroll
+    for (int q = PER * k; q < PER * (k + 1); ++q) inv[q] = sc.inv * invS;
+    if (H == 0 && lane == 0) store_int4_scale(a.scales, a.scale_dtype, row * NGR + k, sc.s);
+  }
+  int4_codes<kSub>(a.packed + (relem0 >> 1), inv, clamp, lc, val, cbase);
+}
 
 // Rows of the workgroup as seen by wave H (a template parameter, so that every register
 // array is indexed by constants).  Both waves pass the same barriers in the same order.
-template <int OP, int H>
+template <int OP, int H, int PER>
 __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, const bf16x8 (&hb)[2],
                                             const f16x8 (&hc)[2], const int lane, const float gts,
                                             const float inv6g, const int G) {
@@ -197,8 +235,13 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
         __syncthreads();
         return fmaxf(sh.rmax[0], sh.rmax[1]);
       };
-      quant_epilogue<OP, kSub>(a, row, relem0, G, invS, cnorm, gts, inv6g, lane, lane == 0 && h == 0, val,
-                               cbase, rowmax);
+      if constexpr (PER > 0) {   // INT4 groups of whole sub-rows
+        (void)rowmax;
+        fast12_whole_subrow_groups<PER, H>(a, sh, row, relem0, invS, cnorm, lane, lc, val, cbase);
+      } else {
+        quant_epilogue<OP, kSub>(a, row, relem0, G, invS, cnorm, gts, inv6g, lane, lane == 0 && h == 0, val,
+                                 cbase, rowmax);
+      }
     }
   }
 
@@ -212,7 +255,9 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
 }
 
 
-template <int OP>
+// PER = 0: groups inside a wave's chunks (or per-token); PER = 1, 2, 4: INT4 groups of PER whole
+// sub-rows (a separate instantiation, so the common kernel carries no code for them).
+template <int OP, int PER>
 __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
   __shared__ Shared12 sh;
   const int lane = threadIdx.x & 63;
@@ -243,27 +288,36 @@ __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
   if constexpr (OP == OP_INT4) G = a.group == kN ? 0 : __builtin_ctz((unsigned)a.group);
   if constexpr (OP == OP_NVFP4) G = 4;
   if constexpr (OP == OP_MXFP4) G = 5;
-  if (h == 0) fast12_rows<OP, 0>(a, sh, hb, hc, lane, gts, inv6g, G);
-  else fast12_rows<OP, 1>(a, sh, hb, hc, lane, gts, inv6g, G);
+  if (h == 0) fast12_rows<OP, 0, PER>(a, sh, hb, hc, lane, gts, inv6g, G);
+  else fast12_rows<OP, 1, PER>(a, sh, hb, hc, lane, gts, inv6g, G);
 }
 
-template <int OP>
-hipError_t launch12(const KernelArgs& a, hipStream_t s) {
-  if (a.sign_period != kN) return hipErrorNotSupported;
-  if constexpr (OP == OP_INT4) {
-    if (!(a.group == kN || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
-  }
-  auto kern = fast12_kernel<OP>;
+template <int OP, int PER>
+hipError_t launch12k(const KernelArgs& a, hipStream_t s) {
+  auto kern = fast12_kernel<OP, PER>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
+template <int OP>
+hipError_t launch12(const KernelArgs& a, hipStream_t s) {
+  if (a.sign_period != kN) return hipErrorNotSupported;
+  if constexpr (OP == OP_INT4) {
+    // per-token, groups of 16 .. 512 inside a wave's chunks, or 1024 .. 4096 (whole sub-rows)
+    if (!(a.group == kN || (a.group >= 16 && a.group <= 4096))) return hipErrorNotSupported;
+    if (a.group == 1024) return launch12k<OP, 1>(a, s);
+    if (a.group == 2048) return launch12k<OP, 2>(a, s);
+    if (a.group == 4096) return launch12k<OP, 4>(a, s);
+  }
+  return launch12k<OP, 0>(a, s);
+}
+
 }  // namespace
 
 int64_t fast12_grid(int64_t rows) {
-  static const int max_blocks = resident_blocks((const void*)fast12_kernel<OP_INT4>, kT, 0);
+  static const int max_blocks = resident_blocks((const void*)fast12_kernel<OP_INT4, 0>, kT, 0);
   return rows < max_blocks ? rows : max_blocks;
 }
 

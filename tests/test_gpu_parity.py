@@ -327,6 +327,7 @@ def test_wide_rows_many_per_workgroup(R, n):
 
 
 INT4_GROUPS = ([(n, g) for n in (12288, 24576) for g in (0, 16, 32, 64, 128, 256, 512)]
+               + [(12288, g) for g in (1024, 2048, 4096)]
                + [(11008, g) for g in (0, 16, 32, 64, 128, 256)] + [(5504, g) for g in (0, 16, 32, 64, 128)]
                + [(2752, g) for g in (0, 16, 32, 64)] + [(22016, g) for g in (0, 16, 32, 64, 128, 256, 512)])
 
@@ -335,7 +336,8 @@ INT4_GROUPS = ([(n, g) for n in (12288, 24576) for g in (0, 16, 32, 64, 128, 256
 def test_wide_every_int4_group(R, n, group):
     """Every INT4 group the wide kernels take, and per-token scales (a row maximum across the
     waves): 12288 = 12 x 1024 (two waves per row) and 24576 = 12 x 2048 (four), groups 16 .. 512
-    from 8 values per lane, lane swaps and 0-4 DPP steps; 11008 = 172 x 64, 5504 = 172 x 32 and
+    from 8 values per lane, lane swaps and 0-4 DPP steps, and at 12288 groups of 1, 2 and 4 whole
+    sub-rows (1024 .. 4096, maxima across both waves); 11008 = 172 x 64, 5504 = 172 x 32 and
     2752 = 172 x 16 (two and four rows per work row), groups of runs, a'-rows and a'-row pairs or
     quads.  Every row against the oracle, both scale types."""
     import dataclasses
@@ -345,6 +347,23 @@ def test_wide_every_int4_group(R, n, group):
     for sd in ("f32", "f16"):
         say(f"{n} int4 group={group} scale={sd}")
         print(check_forward(R, x, s, "int4", group, sd, y_ref=y_ref))
+
+
+def test_12288_whole_subrow_groups_many_rows(R):
+    """INT4 groups of 1024, 2048 and 4096 at width 12288 on more rows than the persistent grid has
+    workgroups (so workgroups take several rows and reuse the LDS group maxima), with rows of
+    magnitude 1e30 among them, whose fp16 scales saturate and whose codes clamp."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(WORKLOADS["downproj_12288_int4g128"], tokens=1100)
+    x, s = generate(w, dev())
+    x[7] = special_rows("huge", 12288, 1, device=dev())[0]
+    x[1093] = special_rows("huge", 12288, 1, seed=8, device=dev())[0]
+    torch.cuda.synchronize()
+    y_ref = O.rotate(x.cpu(), s)
+    for group in (1024, 2048, 4096):
+        say(f"12288 int4 group={group} rows=1100 with saturating rows")
+        print(check_forward(R, x, s, "int4", group, "f16", y_ref=y_ref))
 
 
 @pytest.mark.parametrize("n", [16, 32, 64])
