@@ -20,7 +20,7 @@
 //     512 q + 8 lc + e: the quarter is a register index.
 //  4. Quarter q belongs to wave q.  Every lane keeps its own quarter in registers and writes
 //     the other three to LDS for their waves at its own lane position, so the exchange needs
-//     no lane permutation and stays bank-conflict free.  It takes two rounds (three barriers)
+//     no lane permutation and stays bank-conflict free.  It takes two exchanges (three barriers)
 //     to keep the workgroup within 64 KiB of LDS.
 //  5. Each wave reads the nine sub-rows of its quarter computed by the other waves, applies
 //     the order-12 Williamson factor across the twelve sub-rows, and runs the shared epilogue
@@ -49,8 +49,8 @@ __device__ __forceinline__ int load_off(int h, int jl, int f, int lane) {
 }
 
 // LDS stays within 64 KiB per workgroup: the exchange moves 72 KiB per row, so it takes two
-// rounds.  Round 1 carries the quarters for the waves d = 1 and 2 behind the sender (slot
-// d - 1); round 2 reuses slot 0 for d = 3.
+// exchange rounds.  The first carries the quarters for the waves d = 1 and 2 behind the sender (slot
+// d - 1); the second reuses slot 0 for d = 3.
 struct Shared24 {
   float4 xb[2][kW][kOwn][2][64];   // [slot][receiving wave][jl][half of the run][lane]
   float m1[kW];                    // stage-1 maximum of each wave
@@ -200,7 +200,7 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
             y[2 + t2][t][i] = lo - hi;
           }
       // quarter q goes to wave q, d = (h - q) mod 4 behind this one: d = 1, 2 to LDS now; d = 3
-      // waits in the registers of sub-row jl of wave h + 3, which round 2 fills
+      // waits in the registers of sub-row jl of wave h + 3, which the second exchange fills
 #pragma unroll
       for (int q = 0; q < kW; ++q) {
         const int d = (h - q) & 3;
@@ -225,19 +225,19 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
       w[j1][0][0] = u.x; w[j1][1][0] = u.y; w[j1][0][1] = u.z; w[j1][1][1] = u.w;
       w[j1][0][2] = v.x; w[j1][1][2] = v.y; w[j1][0][3] = v.z; w[j1][1][3] = v.w;
     };
-    __syncthreads();   // round 1 is in LDS
+    __syncthreads();   // the first exchange is in LDS
 #pragma unroll
     for (int d = 1; d <= 2; ++d)
 #pragma unroll
       for (int jl = 0; jl < kOwn; ++jl) take(d - 1, kOwn * ((h + d) & 3) + jl, jl);
-    __syncthreads();   // every wave has read round 1
+    __syncthreads();   // every wave has read the first exchange
 #pragma unroll
     for (int jl = 0; jl < kOwn; ++jl) {
       const int j1 = kOwn * ((h + 3) & 3) + jl;   // holds the quarter for wave h + 1
       sh.xb[0][(h + 1) & 3][jl][0][lane] = make_float4(w[j1][0][0], w[j1][1][0], w[j1][0][1], w[j1][1][1]);
       sh.xb[0][(h + 1) & 3][jl][1][lane] = make_float4(w[j1][0][2], w[j1][1][2], w[j1][0][3], w[j1][1][3]);
     }
-    __syncthreads();   // round 2 is in LDS
+    __syncthreads();   // the second exchange is in LDS
 #pragma unroll
     for (int jl = 0; jl < kOwn; ++jl) take(0, kOwn * ((h + 3) & 3) + jl, jl);
 
