@@ -96,7 +96,9 @@ __host__ __device__ inline int sign_slices(int period) {
   return period / g;            // lcm / UNIT = period / gcd
 }
 
-template <int F, int LOGM, int OP>
+// CG: INT4 groups of two or more whole chunks, short of the row (a separate instantiation, so the
+// common kernels carry no code or registers for them).
+template <int F, int LOGM, int OP, bool CG = false>
 __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   using S = Shape<F, LOGM>;
   extern __shared__ uint32_t smem[];
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     }
 
     // per-token groups wider than a chunk: row maximum now (whole unit is one row)
-    const bool row_group = (OP == OP_INT4) && (a.group > S::CHUNK);
+    const bool row_group = (OP == OP_INT4) && (a.group == S::N) && (S::N > S::CHUNK);
     Int4Scale row_sc{0.0f, 0.0f, false};
     if (row_group) {
       float row_amax = 0.0f;
@@ -282,6 +284,35 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) row_amax = fmaxf(row_amax, fabsf(v[f][t][i]));
       row_sc = int4_scale(group_max(row_amax, 64), cnorm, a.scale_dtype);
+    }
+    // groups of two or more whole chunks, short of the row (a power of two: 2048 at 4096,
+    // 2048 and 4096 at 8192, 1024 at 3072, 1024 and 2048 at 6144): each chunk's maximum over the
+    // wave now, then the maximum over the chunks of its group; chunk c holds fragments
+    // FPC c .. FPC c + FPC - 1, i.e. elements CHUNK c + [0, CHUNK)
+    constexpr bool chunk_groups = CG && (OP == OP_INT4);
+    Int4Scale chunk_sc[S::NCH];
+    if constexpr (chunk_groups) {
+      float cm[S::NCH];
+#pragma unroll
+      for (int c = 0; c < S::NCH; ++c) {
+        float m = 0.0f;
+#pragma unroll
+        for (int fc = 0; fc < S::FPC; ++fc)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(v[S::FPC * c + fc][t][i]));
+        cm[c] = group_max(m, 64);
+      }
+      const int cpg = a.group / S::CHUNK;   // chunks per group
+#pragma unroll
+      for (int c = 0; c < S::NCH; ++c) {
+        float gm = 0.0f;
+#pragma unroll
+        for (int c2 = 0; c2 < S::NCH; ++c2)
+          if (c2 / cpg == c / cpg) gm = fmaxf(gm, cm[c2]);
+        chunk_sc[c] = int4_scale(gm, cnorm, a.scale_dtype);
+      }
     }
 
     // ---------------- epilogue, one chunk at a time ----------------
@@ -327,7 +358,9 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
       } else if constexpr (OP == OP_INT4) {
         Int4Scale sc = row_sc;
         int lanes_per_group = 64;
-        if (!row_group) {
+        if constexpr (chunk_groups) {
+          sc = chunk_sc[c];
+        } else if (!row_group) {
           float m = 0.0f;
 #pragma unroll
           for (int r = 0; r < S::V; ++r) m = fmaxf(m, fabsf(y[r]));
@@ -351,7 +384,9 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
           } else {
             st_stream(a.packed + (g0 >> 1), pack8_nibbles(qb));
           }
-          const bool writer = row_group ? (c == 0 && lane == 0) : ((lane & (lanes_per_group - 1)) == 0);
+          const bool writer = row_group      ? (c == 0 && lane == 0)
+                              : chunk_groups ? (lane == 0 && c % (a.group / S::CHUNK) == 0)
+                                             : ((lane & (lanes_per_group - 1)) == 0);
           if (writer) {
             const int64_t gi = row_group ? u : (g0 >> __builtin_ctz((unsigned)a.group));
             if (a.scale_dtype == RHTQ_SCALE_F32) static_cast<float*>(a.scales)[gi] = sc.s;
@@ -427,13 +462,27 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   }
 }
 
+template <int F, int LOGM, int OP, bool CG>
+hipError_t launch_kern(const KernelArgs& a, hipStream_t s);
+
 template <int F, int LOGM, int OP>
 hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
   using S = Shape<F, LOGM>;
   if constexpr (OP == OP_INT4) {
-    if (!(a.group == S::N || a.group <= S::CHUNK)) return hipErrorNotSupported;
+    // per-token, groups inside a chunk, or groups of whole chunks (the API admits powers of two
+    // that divide the row)
+    if (!(a.group == S::N || a.group <= S::CHUNK || (S::RPU == 1 && a.group < S::N))) return hipErrorNotSupported;
   }
-  auto kern = fast_kernel<F, LOGM, OP>;
+  if constexpr (OP == OP_INT4 && S::RPU == 1 && S::N > S::CHUNK) {
+    if (a.group > S::CHUNK && a.group < S::N) return launch_kern<F, LOGM, OP, true>(a, s);
+  }
+  return launch_kern<F, LOGM, OP, false>(a, s);
+}
+
+template <int F, int LOGM, int OP, bool CG>
+hipError_t launch_kern(const KernelArgs& a, hipStream_t s) {
+  using S = Shape<F, LOGM>;
+  auto kern = fast_kernel<F, LOGM, OP, CG>;
   const int slices = sign_slices<S>(a.sign_period);
   const size_t lds = (size_t)slices * S::NF * 64 * 16 + (size_t)kWaves * S::TBUF * 4;
   if (lds > 65536) return hipErrorNotSupported;

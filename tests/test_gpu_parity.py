@@ -349,6 +349,27 @@ def test_wide_every_int4_group(R, n, group):
         print(check_forward(R, x, s, "int4", group, sd, y_ref=y_ref))
 
 
+WHOLE_CHUNK_GROUPS = [(4096, 2048), (8192, 2048), (8192, 4096), (3072, 1024), (6144, 1024), (6144, 2048)]
+
+
+@pytest.mark.parametrize("n,group", WHOLE_CHUNK_GROUPS)
+def test_int4_groups_of_whole_chunks(R, n, group):
+    """INT4 groups wider than the single-stage kernel's epilogue chunk (512 or 1024 elements) and
+    narrower than the row: each chunk's maximum over the wave, then over the chunks of its group.
+    Every row of 67 against the oracle, with one row of magnitude 1e30 (saturating fp16 scales),
+    both scale types."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(WORKLOADS["downproj_12288_int4g128"], n=n, tokens=67)
+    x, s = generate(w, dev())
+    x[30] = special_rows("huge", n, 1, device=dev())[0]
+    torch.cuda.synchronize()
+    y_ref = O.rotate(x.cpu(), s)
+    for sd in ("f32", "f16"):
+        say(f"{n} int4 group={group} scale={sd}")
+        print(check_forward(R, x, s, "int4", group, sd, y_ref=y_ref))
+
+
 def test_12288_whole_subrow_groups_many_rows(R):
     """INT4 groups of 1024, 2048 and 4096 at width 12288 on more rows than the persistent grid has
     workgroups (so workgroups take several rows and reuse the LDS group maxima), with rows of
