@@ -107,8 +107,9 @@ int rotate_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t 
   a.y = y_out;
   if (rhtq::getenv_test_fail_launch()) return RHTQ_EHIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (in_dtype == RHTQ_IN_BF16) {
-    hipError_t e = rhtq::launch_fast(rhtq::OP_ROTATE, a, s);
+  {
+    const hipError_t e = in_dtype == RHTQ_IN_BF16 ? rhtq::launch_fast(rhtq::OP_ROTATE, a, s)
+                                                  : rhtq::launch_fast_f32(rhtq::OP_ROTATE, a, s);
     if (e != hipErrorNotSupported) return from_hip(e);
   }
   return from_hip(rhtq::launch_generic(rhtq::OP_ROTATE, in_dtype, a, s));
@@ -144,10 +145,8 @@ int forward_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   auto run = [&](int op) -> hipError_t {
-    if (in_dtype == RHTQ_IN_BF16) {
-      hipError_t e = rhtq::launch_fast(op, a, s);
-      if (e != hipErrorNotSupported) return e;
-    }
+    const hipError_t e = in_dtype == RHTQ_IN_BF16 ? rhtq::launch_fast(op, a, s) : rhtq::launch_fast_f32(op, a, s);
+    if (e != hipErrorNotSupported) return e;
     return rhtq::launch_generic(op, in_dtype, a, s);
   };
 

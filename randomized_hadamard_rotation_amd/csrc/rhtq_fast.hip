@@ -88,6 +88,48 @@ __device__ __forceinline__ void load_unit(const uint16_t* x, int64_t u, int64_t 
   }
 }
 
+// fp32 input: the same eight elements per lane and fragment as two 16-byte loads (elements
+// 0-3 and 4-7 of the lane's run).
+template <typename S>
+__device__ __forceinline__ void load_unit_f32(const float* x, int64_t u, int64_t units, int64_t rows, int lane,
+                                              uint4 (*raw)[2]) {
+  const int64_t valid = (rows - u * S::RPU) * S::N;
+#pragma unroll
+  for (int f = 0; f < S::NF; ++f) {
+    const int off = 512 * f + 32 * (lane & 15) + 8 * (lane >> 4);
+    raw[f][0] = make_uint4(0, 0, 0, 0);
+    raw[f][1] = make_uint4(0, 0, 0, 0);
+    if (u < units && (S::RPU == 1 || off < valid)) {
+      const u32x4 t0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + u * S::UNIT + off));
+      const u32x4 t1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + u * S::UNIT + off + 4));
+      raw[f][0] = make_uint4(t0.x, t0.y, t0.z, t0.w);
+      raw[f][1] = make_uint4(t1.x, t1.y, t1.z, t1.w);
+    }
+  }
+}
+
+// fp32 values as the exact sum of three bf16 terms, packed in pairs for the MFMA A operand:
+// hi keeps the top 16 bits of each value (truncation), mid the top 16 bits of what is left,
+// lo the rest, which has at most 8 significant bits and so is a bf16 exactly.  Pair k of
+// the result holds elements 2k (low half) and 2k + 1 (high half).
+__device__ __forceinline__ void split3_bf16(const uint4& r0, const uint4& r1, uint32_t (&hi)[4], uint32_t (&mid)[4],
+                                            uint32_t (&lo)[4]) {
+  const uint32_t e[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  uint32_t r[8], rr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    r[k] = __float_as_uint(__uint_as_float(e[k]) - __uint_as_float(e[k] & 0xFFFF0000u));
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    rr[k] = __float_as_uint(__uint_as_float(r[k]) - __uint_as_float(r[k] & 0xFFFF0000u));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    hi[k] = __builtin_amdgcn_perm(e[2 * k + 1], e[2 * k], 0x07060302u);
+    mid[k] = __builtin_amdgcn_perm(r[2 * k + 1], r[2 * k], 0x07060302u);
+    lo[k] = __builtin_amdgcn_perm(rr[2 * k + 1], rr[2 * k], 0x07060302u);
+  }
+}
+
 // Units of the sign table: lcm(UNIT, sign period) / UNIT (UNIT is a power of two).
 template <typename S>
 __host__ __device__ inline int sign_slices(int period) {
@@ -97,8 +139,10 @@ __host__ __device__ inline int sign_slices(int period) {
 }
 
 // CG: INT4 groups of two or more whole chunks, short of the row (a separate instantiation, so the
-// common kernels carry no code or registers for them).
-template <int F, int LOGM, int OP, bool CG = false>
+// common kernels carry no code or registers for them).  F32: fp32 input, split into three exact
+// bf16 terms for the stage-1 products (three MFMAs accumulating where bf16 input takes one), no
+// prefetch; everything after stage 1 is the bf16 kernel's.
+template <int F, int LOGM, int OP, bool CG = false, bool F32 = false>
 __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   using S = Shape<F, LOGM>;
   extern __shared__ uint32_t smem[];
@@ -113,8 +157,12 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   int64_t u = (int64_t)blockIdx.x * kWaves + wave;
 
   // The first unit's loads go out before the table setup so both latencies overlap.
-  uint4 raw[S::NF];
-  load_unit<S>(x, u, units, a.rows, lane, raw);
+  constexpr bool PREFETCH = S::PREFETCH && !F32;
+  uint4 raw[F32 ? 1 : S::NF];
+  uint4 raw32[F32 ? S::NF : 1][2];
+  const float* xf = static_cast<const float*>(a.x);
+  if constexpr (F32) load_unit_f32<S>(xf, u, units, a.rows, lane, raw32);
+  else load_unit<S>(x, u, units, a.rows, lane, raw);
 
   // bf16 sign-bit masks in load order: entry (slice * NF + f) * 64 + lane holds the four mask
   // dwords (bit 15 / bit 31 of each bf16 pair) of the 8 elements that lane loads for fragment f of
@@ -147,8 +195,12 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   }
 
   for (; u < units; u += ustride) {
-    if constexpr (!S::PREFETCH)
-      if (u != (int64_t)blockIdx.x * kWaves + wave) load_unit<S>(x, u, units, a.rows, lane, raw);
+    if constexpr (!PREFETCH) {
+      if (u != (int64_t)blockIdx.x * kWaves + wave) {
+        if constexpr (F32) load_unit_f32<S>(xf, u, units, a.rows, lane, raw32);
+        else load_unit<S>(x, u, units, a.rows, lane, raw);
+      }
+    }
     const int64_t ubase = u * S::UNIT;                 // element index of the unit start
     const int slice = slices > 1 ? (int)((ubase % ((int64_t)slices * S::UNIT)) / S::UNIT) : 0;
     const int64_t valid = (a.rows - u * S::RPU) * S::N;  // elements of the unit that exist (may exceed UNIT)
@@ -158,19 +210,39 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
 #pragma unroll
     for (int f = 0; f < S::NF; ++f) {
       const uint4 m = sign_tab[(slice * S::NF + f) * 64 + lane];
-      uint4 r = raw[f];
-      r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
-      bf16x8 av;
-      __builtin_memcpy(&av, &r, 16);
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
-      const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+      f32x4 d0, d1;
+      if constexpr (F32) {
+        // the sign flips every term's sign bit: the same bf16-pair masks as for bf16 input
+        uint32_t th[4], tm[4], tl[4];
+        split3_bf16(raw32[f][0], raw32[f][1], th, tm, tl);
+        const uint32_t mk[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { th[k] ^= mk[k]; tm[k] ^= mk[k]; tl[k] ^= mk[k]; }
+        bf16x8 ah, am, al;
+        __builtin_memcpy(&ah, th, 16);
+        __builtin_memcpy(&am, tm, 16);
+        __builtin_memcpy(&al, tl, 16);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hb[0], z, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hb[1], z, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, hb[0], d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, hb[1], d1, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hb[0], d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hb[1], d1, 0, 0, 0);
+      } else {
+        uint4 r = raw[f];
+        r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
+        bf16x8 av;
+        __builtin_memcpy(&av, &r, 16);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[f][0][i] = d0[i]; v[f][1][i] = d1[i]; }
     }
     // raw[] is consumed: its registers now receive the next unit, whose loads run while
     // this unit's butterflies and epilogue execute
-    if constexpr (S::PREFETCH) load_unit<S>(x, u + ustride, units, a.rows, lane, raw);
+    if constexpr (PREFETCH) load_unit<S>(x, u + ustride, units, a.rows, lane, raw);
 
     // ---------------- butterflies on register bits ----------------
     // bits 5, 6: register index i (bit 5 = i & 1, bit 6 = i >> 1), where they lie inside the row
@@ -462,10 +534,10 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   }
 }
 
-template <int F, int LOGM, int OP, bool CG>
+template <int F, int LOGM, int OP, bool CG, bool F32>
 hipError_t launch_kern(const KernelArgs& a, hipStream_t s);
 
-template <int F, int LOGM, int OP>
+template <int F, int LOGM, int OP, bool F32 = false>
 hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
   using S = Shape<F, LOGM>;
   if constexpr (OP == OP_INT4) {
@@ -474,15 +546,15 @@ hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
     if (!(a.group == S::N || a.group <= S::CHUNK || (S::RPU == 1 && a.group < S::N))) return hipErrorNotSupported;
   }
   if constexpr (OP == OP_INT4 && S::RPU == 1 && S::N > S::CHUNK) {
-    if (a.group > S::CHUNK && a.group < S::N) return launch_kern<F, LOGM, OP, true>(a, s);
+    if (a.group > S::CHUNK && a.group < S::N) return launch_kern<F, LOGM, OP, true, F32>(a, s);
   }
-  return launch_kern<F, LOGM, OP, false>(a, s);
+  return launch_kern<F, LOGM, OP, false, F32>(a, s);
 }
 
-template <int F, int LOGM, int OP, bool CG>
+template <int F, int LOGM, int OP, bool CG, bool F32>
 hipError_t launch_kern(const KernelArgs& a, hipStream_t s) {
   using S = Shape<F, LOGM>;
-  auto kern = fast_kernel<F, LOGM, OP, CG>;
+  auto kern = fast_kernel<F, LOGM, OP, CG, F32>;
   const int slices = sign_slices<S>(a.sign_period);
   const size_t lds = (size_t)slices * S::NF * 64 * 16 + (size_t)kWaves * S::TBUF * 4;
   if (lds > 65536) return hipErrorNotSupported;
@@ -494,26 +566,38 @@ hipError_t launch_kern(const KernelArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int OP>
+template <int OP, bool F32 = false>
 hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
   switch (a.n) {
-    case 16: return launch_one<1, 4, OP>(a, s);
-    case 32: return launch_one<1, 5, OP>(a, s);
-    case 64: return launch_one<1, 6, OP>(a, s);
-    case 128: return launch_one<1, 7, OP>(a, s);
-    case 256: return launch_one<1, 8, OP>(a, s);
-    case 512: return launch_one<1, 9, OP>(a, s);
-    case 1024: return launch_one<1, 10, OP>(a, s);
-    case 2048: return launch_one<1, 11, OP>(a, s);
-    case 4096: return launch_one<1, 12, OP>(a, s);
-    case 8192: return launch_one<1, 13, OP>(a, s);
-    case 3072: return launch_one<12, 8, OP>(a, s);
-    case 6144: return launch_one<12, 9, OP>(a, s);
+    case 16: return launch_one<1, 4, OP, F32>(a, s);
+    case 32: return launch_one<1, 5, OP, F32>(a, s);
+    case 64: return launch_one<1, 6, OP, F32>(a, s);
+    case 128: return launch_one<1, 7, OP, F32>(a, s);
+    case 256: return launch_one<1, 8, OP, F32>(a, s);
+    case 512: return launch_one<1, 9, OP, F32>(a, s);
+    case 1024: return launch_one<1, 10, OP, F32>(a, s);
+    case 2048: return launch_one<1, 11, OP, F32>(a, s);
+    case 4096: return launch_one<1, 12, OP, F32>(a, s);
+    case 8192: return launch_one<1, 13, OP, F32>(a, s);
+    case 3072: return launch_one<12, 8, OP, F32>(a, s);
+    case 6144: return launch_one<12, 9, OP, F32>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
 }  // namespace
+
+hipError_t launch_fast_f32(int op, const KernelArgs& a, hipStream_t s) {
+  if (getenv_fast_disabled()) return hipErrorNotSupported;
+  switch (op) {
+    case OP_ROTATE: return dispatch<OP_ROTATE, true>(a, s);
+    case OP_INT4: return dispatch<OP_INT4, true>(a, s);
+    case OP_NVFP4: return dispatch<OP_NVFP4, true>(a, s);
+    case OP_MXFP4: return dispatch<OP_MXFP4, true>(a, s);
+    case OP_AMAX: return dispatch<OP_AMAX, true>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
 
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s) {
   if (getenv_fast_disabled()) return hipErrorNotSupported;

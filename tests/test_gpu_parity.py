@@ -289,6 +289,31 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
+@pytest.mark.parametrize("n,tokens", [(4096, 3000), (128, 40000), (3072, 2500), (8192, 1100)])
+def test_fp32_input_many_rows_per_wave(R, n, tokens):
+    """fp32 input on the single-stage kernel (three exact bf16 terms per value for stage 1, no
+    prefetch): more rows than the persistent grid, so waves take several units; INT4 g128 and
+    per-token, dynamic NVFP4 (its tensor scale over all rows) and MXFP4 on sampled rows, the
+    rotation of the same rows."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(WORKLOADS["llama_4096_int4"], n=n, tokens=tokens)
+    xb, s = generate(w, dev())
+    x = xb.float() * (1.0 + 1e-3 * torch.randn(xb.shape, device=dev()))   # values off the bf16 grid
+    rows = np.unique(np.array([0, 1, 2, tokens // 3, tokens // 2, tokens - 3, tokens - 2, tokens - 1]))
+    y_ref = O.rotate(x[rows].cpu(), s)
+    C.check_rotation(to_np(R.rhtq_rotate(x, s))[rows], y_ref)
+    for group, sd in ((128, "f16"), (0, "f32")):
+        say(f"fp32 int4 n={n} tokens={tokens} group={group}")
+        check_forward(R, x, s, "int4", group, sd, rows=rows, y_ref=y_ref)
+    say(f"fp32 nvfp4 n={n} tokens={tokens}")
+    packed, scales, g = run_forward(R, x, s, "nvfp4", 16, "e4m3")
+    g_ref = np.float32(np.max(np.abs(O.rotate(x.cpu(), s))) / 2688.0)
+    C.check_nvfp4(packed[rows], scales[rows], g, y_ref, g_ref)
+    say(f"fp32 mxfp4 n={n} tokens={tokens}")
+    check_forward(R, x, s, "mxfp4", 32, "e8m0", rows=rows, y_ref=y_ref)
+
+
 @pytest.mark.parametrize("n", [8192, 16384, 22016, 11008, 5504, 2752, 12288, 24576])
 def test_wide_rows_many_per_workgroup(R, n):
     """The multi-wave kernels (8192, 16384, 11008 = 172 x 64, 5504 and 2752 = 172 x 32 and 16 two
