@@ -21,6 +21,33 @@ __device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
 }
+// fp32 input: four values as their bit patterns.
+__device__ __forceinline__ uint4 ld_stream(const float* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+// fp32 values as the exact sum of three bf16 terms, packed in pairs for the MFMA A operand:
+// hi keeps the top 16 bits of each value (truncation), mid the top 16 bits of what is left,
+// lo the rest, which has at most 8 significant bits and so is a bf16 exactly.  Pair k of
+// the result holds elements 2k (low half) and 2k + 1 (high half).
+__device__ __forceinline__ void split3_bf16(const uint4& r0, const uint4& r1, uint32_t (&hi)[4], uint32_t (&mid)[4],
+                                            uint32_t (&lo)[4]) {
+  const uint32_t e[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  uint32_t r[8], rr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    r[k] = __float_as_uint(__uint_as_float(e[k]) - __uint_as_float(e[k] & 0xFFFF0000u));
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    rr[k] = __float_as_uint(__uint_as_float(r[k]) - __uint_as_float(r[k] & 0xFFFF0000u));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    hi[k] = __builtin_amdgcn_perm(e[2 * k + 1], e[2 * k], 0x07060302u);
+    mid[k] = __builtin_amdgcn_perm(r[2 * k + 1], r[2 * k], 0x07060302u);
+    lo[k] = __builtin_amdgcn_perm(rr[2 * k + 1], rr[2 * k], 0x07060302u);
+  }
+}
+
 __device__ __forceinline__ void st_stream(uint8_t* p, uint32_t a, uint32_t b) {
   const u32x2 t = {a, b};
   __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));

@@ -100,33 +100,9 @@ __device__ __forceinline__ void load_unit_f32(const float* x, int64_t u, int64_t
     raw[f][0] = make_uint4(0, 0, 0, 0);
     raw[f][1] = make_uint4(0, 0, 0, 0);
     if (u < units && (S::RPU == 1 || off < valid)) {
-      const u32x4 t0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + u * S::UNIT + off));
-      const u32x4 t1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + u * S::UNIT + off + 4));
-      raw[f][0] = make_uint4(t0.x, t0.y, t0.z, t0.w);
-      raw[f][1] = make_uint4(t1.x, t1.y, t1.z, t1.w);
+      raw[f][0] = ld_stream(x + u * S::UNIT + off);
+      raw[f][1] = ld_stream(x + u * S::UNIT + off + 4);
     }
-  }
-}
-
-// fp32 values as the exact sum of three bf16 terms, packed in pairs for the MFMA A operand:
-// hi keeps the top 16 bits of each value (truncation), mid the top 16 bits of what is left,
-// lo the rest, which has at most 8 significant bits and so is a bf16 exactly.  Pair k of
-// the result holds elements 2k (low half) and 2k + 1 (high half).
-__device__ __forceinline__ void split3_bf16(const uint4& r0, const uint4& r1, uint32_t (&hi)[4], uint32_t (&mid)[4],
-                                            uint32_t (&lo)[4]) {
-  const uint32_t e[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-  uint32_t r[8], rr[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    r[k] = __float_as_uint(__uint_as_float(e[k]) - __uint_as_float(e[k] & 0xFFFF0000u));
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    rr[k] = __float_as_uint(__uint_as_float(r[k]) - __uint_as_float(r[k] & 0xFFFF0000u));
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    hi[k] = __builtin_amdgcn_perm(e[2 * k + 1], e[2 * k], 0x07060302u);
-    mid[k] = __builtin_amdgcn_perm(r[2 * k + 1], r[2 * k], 0x07060302u);
-    lo[k] = __builtin_amdgcn_perm(rr[2 * k + 1], rr[2 * k], 0x07060302u);
   }
 }
 
@@ -589,6 +565,7 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
 
 hipError_t launch_fast_f32(int op, const KernelArgs& a, hipStream_t s) {
   if (getenv_fast_disabled()) return hipErrorNotSupported;
+  if (a.n == 12288) return launch_fast12_f32(op, a, s);
   switch (op) {
     case OP_ROTATE: return dispatch<OP_ROTATE, true>(a, s);
     case OP_INT4: return dispatch<OP_INT4, true>(a, s);

@@ -87,7 +87,7 @@ __device__ __forceinline__ void fast12_whole_subrow_groups(const KernelArgs& a, 
 
 // Rows of the workgroup as seen by wave H (a template parameter, so that every register
 // array is indexed by constants).  Both waves pass the same barriers in the same order.
-template <int OP, int H, int PER>
+template <int OP, int H, int PER, bool F32>
 __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, const bf16x8 (&hb)[2],
                                             const f16x8 (&hc)[2], const int lane, const float gts,
                                             const float inv6g, const int G) {
@@ -98,38 +98,70 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
   const int lc = (lane >> 4) | ((lane & 15) << 2);
 
   // loads of one row (12 x 16 bytes per lane); the next row's go out as soon as stage 1
-  // has consumed these registers, so they run during this row's work
-  uint4 raw[kOwn][2] = {};
+  // has consumed these registers, so they run during this row's work.  fp32 input (F32):
+  // 12 x 2 x 16 bytes per lane, loaded at the top of each row (no registers for a prefetch).
+  uint4 raw[F32 ? 1 : kOwn][2] = {};
+  uint4 raw32[F32 ? kOwn : 1][2][2] = {};
+  const float* xf = static_cast<const float*>(a.x);
   auto load = [&](int64_t r) {
     if (r < a.rows) {
 #pragma unroll
       for (int jl = 0; jl < kOwn; ++jl)
 #pragma unroll
-        for (int f = 0; f < 2; ++f) raw[jl][f] = ld_stream(x + r * kN + load_off(h, jl, f, lane));
+        for (int f = 0; f < 2; ++f) {
+          if constexpr (F32) {
+            const float* p = xf + r * kN + load_off(h, jl, f, lane);
+            raw32[jl][f][0] = ld_stream(p);
+            raw32[jl][f][1] = ld_stream(p + 4);
+          } else {
+            raw[jl][f] = ld_stream(x + r * kN + load_off(h, jl, f, lane));
+          }
+        }
     }
   };
-  load(blockIdx.x);
+  if constexpr (!F32) load(blockIdx.x);
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const int64_t relem0 = row * kN;
+    if constexpr (F32) load(row);
     // ---------------- H1024 of the own sub-rows ----------------
     float d1[kOwn][2][2][4];   // [jl][f][t][i]
 #pragma unroll
     for (int jl = 0; jl < kOwn; ++jl)
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        uint4 r = raw[jl][f];
         const uint4 mk = sh.sign_tab[((h * kOwn + jl) * 2 + f) * 64 + lane];
-        r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
-        bf16x8 av;
-        __builtin_memcpy(&av, &r, 16);
         const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
-        const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+        f32x4 p0, p1;
+        if constexpr (F32) {
+          // three exact bf16 terms per value; the signs flip each term
+          uint32_t th[4], tm[4], tl[4];
+          split3_bf16(raw32[jl][f][0], raw32[jl][f][1], th, tm, tl);
+          const uint32_t m4[4] = {mk.x, mk.y, mk.z, mk.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) { th[k] ^= m4[k]; tm[k] ^= m4[k]; tl[k] ^= m4[k]; }
+          bf16x8 ah, am, al;
+          __builtin_memcpy(&ah, th, 16);
+          __builtin_memcpy(&am, tm, 16);
+          __builtin_memcpy(&al, tl, 16);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hb[0], z, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hb[1], z, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, hb[0], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, hb[1], p1, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hb[0], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hb[1], p1, 0, 0, 0);
+        } else {
+          uint4 r = raw[jl][f];
+          r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
+          bf16x8 av;
+          __builtin_memcpy(&av, &r, 16);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) { d1[jl][f][0][i] = p0[i]; d1[jl][f][1][i] = p1[i]; }
       }
-    load(row + gridDim.x);
+    if constexpr (!F32) load(row + gridDim.x);
     float m1 = 0.0f;
 #pragma unroll
     for (int jl = 0; jl < kOwn; ++jl)
@@ -257,7 +289,7 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
 
 // PER = 0: groups inside a wave's chunks (or per-token); PER = 1, 2, 4: INT4 groups of PER whole
 // sub-rows (a separate instantiation, so the common kernel carries no code for them).
-template <int OP, int PER>
+template <int OP, int PER, bool F32 = false>
 __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
   __shared__ Shared12 sh;
   const int lane = threadIdx.x & 63;
@@ -288,36 +320,36 @@ __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
   if constexpr (OP == OP_INT4) G = a.group == kN ? 0 : __builtin_ctz((unsigned)a.group);
   if constexpr (OP == OP_NVFP4) G = 4;
   if constexpr (OP == OP_MXFP4) G = 5;
-  if (h == 0) fast12_rows<OP, 0, PER>(a, sh, hb, hc, lane, gts, inv6g, G);
-  else fast12_rows<OP, 1, PER>(a, sh, hb, hc, lane, gts, inv6g, G);
+  if (h == 0) fast12_rows<OP, 0, PER, F32>(a, sh, hb, hc, lane, gts, inv6g, G);
+  else fast12_rows<OP, 1, PER, F32>(a, sh, hb, hc, lane, gts, inv6g, G);
 }
 
-template <int OP, int PER>
+template <int OP, int PER, bool F32>
 hipError_t launch12k(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast12_kernel<OP, PER>;
+  auto kern = fast12_kernel<OP, PER, F32>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int OP>
+template <int OP, bool F32 = false>
 hipError_t launch12(const KernelArgs& a, hipStream_t s) {
   if (a.sign_period != kN) return hipErrorNotSupported;
   if constexpr (OP == OP_INT4) {
     // per-token, groups of 16 .. 512 inside a wave's chunks, or 1024 .. 4096 (whole sub-rows)
     if (!(a.group == kN || (a.group >= 16 && a.group <= 4096))) return hipErrorNotSupported;
-    if (a.group == 1024) return launch12k<OP, 1>(a, s);
-    if (a.group == 2048) return launch12k<OP, 2>(a, s);
-    if (a.group == 4096) return launch12k<OP, 4>(a, s);
+    if (a.group == 1024) return launch12k<OP, 1, F32>(a, s);
+    if (a.group == 2048) return launch12k<OP, 2, F32>(a, s);
+    if (a.group == 4096) return launch12k<OP, 4, F32>(a, s);
   }
-  return launch12k<OP, 0>(a, s);
+  return launch12k<OP, 0, F32>(a, s);
 }
 
 }  // namespace
 
 int64_t fast12_grid(int64_t rows) {
-  static const int max_blocks = resident_blocks((const void*)fast12_kernel<OP_INT4, 0>, kT, 0);
+  static const int max_blocks = resident_blocks((const void*)fast12_kernel<OP_INT4, 0, false>, kT, 0);
   return rows < max_blocks ? rows : max_blocks;
 }
 
@@ -328,6 +360,17 @@ hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s) {
     case OP_NVFP4: return launch12<OP_NVFP4>(a, s);
     case OP_MXFP4: return launch12<OP_MXFP4>(a, s);
     case OP_AMAX: return launch12<OP_AMAX>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_fast12_f32(int op, const KernelArgs& a, hipStream_t s) {
+  switch (op) {
+    case OP_ROTATE: return launch12<OP_ROTATE, true>(a, s);
+    case OP_INT4: return launch12<OP_INT4, true>(a, s);
+    case OP_NVFP4: return launch12<OP_NVFP4, true>(a, s);
+    case OP_MXFP4: return launch12<OP_MXFP4, true>(a, s);
+    case OP_AMAX: return launch12<OP_AMAX, true>(a, s);
     default: return hipErrorNotSupported;
   }
 }

@@ -45,13 +45,15 @@ hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t
 // (op, n, group) combination has no fast kernel; the caller then uses the generic one.
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
 
-// fp32 input on the single-stage register-resident kernels (widths 16 .. 8192, 3072, 6144):
-// each value is split into three exact bf16 terms for the stage-1 products.  Returns
+// fp32 input on the single-stage register-resident kernels (widths 16 .. 8192, 3072, 6144) and
+// the 12288 kernel: each value is split into three exact bf16 terms for the stage-1 products.  Returns
 // hipErrorNotSupported where that kernel has no variant; the caller then uses the generic one.
 hipError_t launch_fast_f32(int op, const KernelArgs& a, hipStream_t s);
 
-// Two-wave kernel for 12288-wide rows (called by launch_fast).
+// Two-wave kernel for 12288-wide rows (called by launch_fast), and its fp32-input form
+// (called by launch_fast_f32).
 hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s);
+hipError_t launch_fast12_f32(int op, const KernelArgs& a, hipStream_t s);
 
 // The grid launch_fast12 uses for per-group INT4 on `rows` rows (resident workgroups, at most
 // one per row); the streaming-floor measurement launches the same grid.

@@ -289,9 +289,9 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n,tokens", [(4096, 3000), (128, 40000), (3072, 2500), (8192, 1100)])
+@pytest.mark.parametrize("n,tokens", [(4096, 3000), (128, 40000), (3072, 2500), (8192, 1100), (12288, 1100)])
 def test_fp32_input_many_rows_per_wave(R, n, tokens):
-    """fp32 input on the single-stage kernel (three exact bf16 terms per value for stage 1, no
+    """fp32 input on the single-stage and 12288 kernels (three exact bf16 terms per value for stage 1, no
     prefetch): more rows than the persistent grid, so waves take several units; INT4 g128 and
     per-token, dynamic NVFP4 (its tensor scale over all rows) and MXFP4 on sampled rows, the
     rotation of the same rows."""
