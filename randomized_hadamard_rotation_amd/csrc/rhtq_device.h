@@ -26,26 +26,43 @@ __device__ __forceinline__ uint4 ld_stream(const float* p) {
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
 }
-// fp32 values as the exact sum of three bf16 terms, packed in pairs for the MFMA A operand:
-// hi keeps the top 16 bits of each value (truncation), mid the top 16 bits of what is left,
-// lo the rest, which has at most 8 significant bits and so is a bf16 exactly.  Pair k of
-// the result holds elements 2k (low half) and 2k + 1 (high half).
-__device__ __forceinline__ void split3_bf16(const uint4& r0, const uint4& r1, uint32_t (&hi)[4], uint32_t (&mid)[4],
-                                            uint32_t (&lo)[4]) {
+// fp32 values as three bf16 terms, packed in pairs for the MFMA A operand: hi keeps the top 16
+// bits of each value (truncation); mid8 is the top 16 bits of what is left, times 2^8; lo16 the
+// rest times 2^16, which has at most 8 significant bits and so is a bf16 exactly.  Every step is
+// exact, so x = hi + 2^-8 mid8 + 2^-16 lo16.  The factors keep the lower terms about as large as
+// the value itself: unscaled, they would be bf16 denormals for values below about 2^-110, and
+// the matrix cores flush denormal operands (rows near 1e-37 lost 2^-8 of their precision).  Pair
+// k holds elements 2k (low half) and 2k + 1 (high half).
+__device__ __forceinline__ void split3_bf16(const uint4& r0, const uint4& r1, uint32_t (&hi)[4], uint32_t (&mid8)[4],
+                                            uint32_t (&lo16)[4]) {
   const uint32_t e[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-  uint32_t r[8], rr[8];
+  uint32_t m[8], l[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    r[k] = __float_as_uint(__uint_as_float(e[k]) - __uint_as_float(e[k] & 0xFFFF0000u));
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    rr[k] = __float_as_uint(__uint_as_float(r[k]) - __uint_as_float(r[k] & 0xFFFF0000u));
+  for (int k = 0; k < 8; ++k) {
+    const float r8 = (__uint_as_float(e[k]) - __uint_as_float(e[k] & 0xFFFF0000u)) * 256.0f;
+    m[k] = __float_as_uint(r8);
+    l[k] = __float_as_uint((r8 - __uint_as_float(m[k] & 0xFFFF0000u)) * 256.0f);
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     hi[k] = __builtin_amdgcn_perm(e[2 * k + 1], e[2 * k], 0x07060302u);
-    mid[k] = __builtin_amdgcn_perm(r[2 * k + 1], r[2 * k], 0x07060302u);
-    lo[k] = __builtin_amdgcn_perm(rr[2 * k + 1], rr[2 * k], 0x07060302u);
+    mid8[k] = __builtin_amdgcn_perm(m[2 * k + 1], m[2 * k], 0x07060302u);
+    lo16[k] = __builtin_amdgcn_perm(l[2 * k + 1], l[2 * k], 0x07060302u);
   }
+}
+
+// Stage-1 products of fp32 input: the three terms through the same +-1 operand, each into its
+// own accumulator (the scaled terms must not meet the hi products unscaled), then
+// d = dh + 2^-8 dm + 2^-16 dl.
+__device__ __forceinline__ f32x4 stage1_f32(const bf16x8& ah, const bf16x8& am, const bf16x8& al, const bf16x8& b) {
+  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x4 dh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, z, 0, 0, 0);
+  const f32x4 dm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b, z, 0, 0, 0);
+  const f32x4 dl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, z, 0, 0, 0);
+  f32x4 d;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = __builtin_fmaf(dl[i], 1.0f / 65536.0f, __builtin_fmaf(dm[i], 1.0f / 256.0f, dh[i]));
+  return d;
 }
 
 __device__ __forceinline__ void st_stream(uint8_t* p, uint32_t a, uint32_t b) {

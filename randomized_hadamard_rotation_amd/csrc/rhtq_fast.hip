@@ -199,12 +199,8 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
         __builtin_memcpy(&ah, th, 16);
         __builtin_memcpy(&am, tm, 16);
         __builtin_memcpy(&al, tl, 16);
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hb[0], z, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hb[1], z, 0, 0, 0);
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, hb[0], d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, hb[1], d1, 0, 0, 0);
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hb[0], d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hb[1], d1, 0, 0, 0);
+        d0 = stage1_f32(ah, am, al, hb[0]);
+        d1 = stage1_f32(ah, am, al, hb[1]);
       } else {
         uint4 r = raw[f];
         r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;

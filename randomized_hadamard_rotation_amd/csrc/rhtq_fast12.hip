@@ -134,7 +134,7 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
         const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
         f32x4 p0, p1;
         if constexpr (F32) {
-          // three exact bf16 terms per value; the signs flip each term
+          // three bf16 terms per value (split3_bf16); the signs flip each term
           uint32_t th[4], tm[4], tl[4];
           split3_bf16(raw32[jl][f][0], raw32[jl][f][1], th, tm, tl);
           const uint32_t m4[4] = {mk.x, mk.y, mk.z, mk.w};
@@ -144,12 +144,8 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
           __builtin_memcpy(&ah, th, 16);
           __builtin_memcpy(&am, tm, 16);
           __builtin_memcpy(&al, tl, 16);
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hb[0], z, 0, 0, 0);
-          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hb[1], z, 0, 0, 0);
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, hb[0], p0, 0, 0, 0);
-          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, hb[1], p1, 0, 0, 0);
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hb[0], p0, 0, 0, 0);
-          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hb[1], p1, 0, 0, 0);
+          p0 = stage1_f32(ah, am, al, hb[0]);
+          p1 = stage1_f32(ah, am, al, hb[1]);
         } else {
           uint4 r = raw[jl][f];
           r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;

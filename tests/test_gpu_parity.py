@@ -570,6 +570,23 @@ def test_special_inputs(R, kind):
         check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
+@pytest.mark.parametrize("n", [128, 4096, 12288])
+def test_fp32_rows_near_the_normal_floor(R, n):
+    """fp32 rows of magnitude 1e-35 .. 3e-38 (just above the fp32 denormal range) through the fp32
+    fast paths: the three bf16 terms of each value must stay normal numbers (the matrix cores flush
+    denormal operands), so the rotation meets R1 at every magnitude; INT4 g128 at 1e-35."""
+    import torch
+    s = splitmix64_signs(3, n)
+    for scale in (1e-35, 1e-37, 3e-38):
+        say(f"fp32 n={n} rows of magnitude {scale:g}")
+        g = torch.Generator().manual_seed(n)
+        x = (torch.randn(5, n, generator=g, dtype=torch.float64) * scale).to(torch.float32)
+        y_ref = O.rotate(x, s)
+        C.check_rotation(to_np(R.rhtq_rotate(x.to(dev()), s)), y_ref)
+        if scale == 1e-35:
+            check_forward(R, x.to(dev()), s, "int4", 128, "f32", y_ref=y_ref)
+
+
 def test_zero_tokens_is_noop(R):
     import torch
     say("tokens = 0")
