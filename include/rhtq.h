@@ -50,7 +50,9 @@
  *    capture permits).
  *  - Arguments are checked on the host before any HIP call; on error nothing is
  *    enqueued and the status says why.  tokens == 0 is a valid no-op.
- *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.  Denormal input
+ *    values (below 1.2e-38 in magnitude) may be read as zero by the matrix-core kernels,
+ *    so a row made only of denormals does not get fp32 accuracy.
  *  - Alignment: x, y_out, packed_out, x_out and signs must be 16-byte aligned;
  *    scale buffers aligned to their element size.
  *  - Supported widths: n = 2^k with 16 <= n <= 16384, n = 12 * 2^k with
