@@ -50,9 +50,10 @@
  *    capture permits).
  *  - Arguments are checked on the host before any HIP call; on error nothing is
  *    enqueued and the status says why.  tokens == 0 is a valid no-op.
- *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.  Denormal input
- *    values (below 1.2e-38 in magnitude) may be read as zero by the matrix-core kernels,
- *    so a row made only of denormals does not get fp32 accuracy.
+ *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.  Denormal bf16 or
+ *    fp32 input values (below 1.2e-38 in magnitude) may be read as zero by the matrix-core
+ *    kernels, so a row made only of them does not get fp32 accuracy.  fp16 input is read
+ *    exactly, its subnormals (below 6.1e-5) included.
  *  - Alignment: x, y_out, packed_out, x_out and signs must be 16-byte aligned;
  *    scale buffers aligned to their element size.
  *  - Supported widths: n = 2^k with 16 <= n <= 16384, n = 12 * 2^k with
@@ -70,7 +71,7 @@
 extern "C" {
 #endif
 
-#define RHTQ_ABI_VERSION 3   /* 2: MXFP4 format and E8M0 scales; 3: block-diagonal calls */
+#define RHTQ_ABI_VERSION 4   /* 2: MXFP4 format and E8M0 scales; 3: block-diagonal calls; 4: fp16 input */
 
 /* Status codes. */
 #define RHTQ_OK           0   /* enqueued (or nothing to do)                       */
@@ -84,6 +85,7 @@ extern "C" {
 /* Input element types. */
 #define RHTQ_IN_BF16 0
 #define RHTQ_IN_F32  1
+#define RHTQ_IN_F16  2   /* IEEE binary16: the FP16 baseline models of the QuaRot reviews page, review 4 Weaknesses */
 
 /* 4-bit formats. */
 #define RHTQ_FMT_INT4  0      /* symmetric absmax INT4, two's complement nibbles     */
@@ -114,7 +116,7 @@ int rhtq_supported(int32_t n, int fmt, int32_t group);
 
 /*
  * Rotation only:  y_out[t][i] = (H_n diag(s) x[t])[i] / sqrt(n), fp32.
- *   x       [tokens][n] bf16 (RHTQ_IN_BF16) or fp32 (RHTQ_IN_F32)
+ *   x       [tokens][n] bf16 (RHTQ_IN_BF16), fp16 (RHTQ_IN_F16) or fp32 (RHTQ_IN_F32)
  *   signs   [n] int8 or NULL
  *   y_out   [tokens][n] fp32
  * Cite: QuaRot reviews, review 1 Summary (Walsh-Hadamard algorithm) and review 2

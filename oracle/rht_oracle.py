@@ -218,8 +218,8 @@ def fwht(v: np.ndarray) -> np.ndarray:
 
 
 def _as_f64(x) -> np.ndarray:
-    """Read bf16 / fp32 / fp64 input exactly into fp64 (bf16 arrives as a torch
-    tensor or as uint16 bit patterns)."""
+    """Read bf16 / fp16 / fp32 / fp64 input exactly into fp64 (bf16 and fp16 arrive as
+    torch tensors; bf16 also as uint16 bit patterns)."""
     try:
         import torch
         if isinstance(x, torch.Tensor):

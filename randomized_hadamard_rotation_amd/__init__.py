@@ -16,7 +16,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librhtq.so")
 
 RHTQ_OK, RHTQ_EINVAL, RHTQ_EUNSUPPORTED, RHTQ_EHIP = 0, 1, 2, 3
-RHTQ_IN_BF16, RHTQ_IN_F32 = 0, 1
+RHTQ_IN_BF16, RHTQ_IN_F32, RHTQ_IN_F16 = 0, 1, 2
 RHTQ_FMT_INT4, RHTQ_FMT_NVFP4, RHTQ_FMT_MXFP4 = 0, 1, 2
 RHTQ_SCALE_F32, RHTQ_SCALE_F16, RHTQ_SCALE_E4M3, RHTQ_SCALE_E8M0 = 0, 1, 2, 3
 RHTQ_TENSOR_SCALE_DYNAMIC, RHTQ_TENSOR_SCALE_GIVEN = 0, 1
@@ -154,9 +154,11 @@ def _in_dtype(x):
     torch = _torch()
     if x.dtype == torch.bfloat16:
         return RHTQ_IN_BF16
+    if x.dtype == torch.float16:
+        return RHTQ_IN_F16
     if x.dtype == torch.float32:
         return RHTQ_IN_F32
-    raise ValueError("x must be bfloat16 or float32")
+    raise ValueError("x must be bfloat16, float16 or float32")
 
 
 def _rows(x):

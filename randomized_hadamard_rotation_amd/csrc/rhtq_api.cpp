@@ -38,6 +38,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int from_hip(hipError_t e) { return e == hipSuccess ? RHTQ_OK : RHTQ_EHIP; }
 
+// The matrix-core kernels for an input type; hipErrorNotSupported sends the call to the generic one.
+hipError_t fast_for(int in_dtype, int op, const rhtq::KernelArgs& a, hipStream_t s) {
+  if (in_dtype == RHTQ_IN_BF16) return rhtq::launch_fast(op, a, s);
+  if (in_dtype == RHTQ_IN_F16) return rhtq::launch_fast(op, a, s, /*f16=*/true);
+  return rhtq::launch_fast_f32(op, a, s);
+}
+
 // Shared checks of rhtq_forward / rhtq_inverse.  Returns RHTQ_OK or the status.
 int check_quant_args(int64_t tokens, int32_t n, int fmt, int32_t group, int scale_dtype) {
   if (tokens < 0) return RHTQ_EINVAL;
@@ -94,7 +101,7 @@ int check_quant_block(int32_t n, int32_t block, int fmt, int32_t group, int scal
 
 int rotate_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t block, const int8_t* signs,
                 float* y_out, rhtq_stream_t stream) {
-  if (in_dtype != RHTQ_IN_BF16 && in_dtype != RHTQ_IN_F32) return RHTQ_EINVAL;
+  if (in_dtype != RHTQ_IN_BF16 && in_dtype != RHTQ_IN_F16 && in_dtype != RHTQ_IN_F32) return RHTQ_EINVAL;
   rhtq::KernelArgs a{};
   const int st = shape_args(tokens, n, block, a);
   if (st != RHTQ_OK) return st;
@@ -108,8 +115,7 @@ int rotate_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t 
   if (rhtq::getenv_test_fail_launch()) return RHTQ_EHIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   {
-    const hipError_t e = in_dtype == RHTQ_IN_BF16 ? rhtq::launch_fast(rhtq::OP_ROTATE, a, s)
-                                                  : rhtq::launch_fast_f32(rhtq::OP_ROTATE, a, s);
+    const hipError_t e = fast_for(in_dtype, rhtq::OP_ROTATE, a, s);
     if (e != hipErrorNotSupported) return from_hip(e);
   }
   return from_hip(rhtq::launch_generic(rhtq::OP_ROTATE, in_dtype, a, s));
@@ -118,7 +124,7 @@ int rotate_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t 
 int forward_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t block, const int8_t* signs,
                  int fmt, int32_t group, int scale_dtype, uint8_t* packed_out, void* scales_out,
                  float* tensor_scale, int tensor_scale_mode, rhtq_stream_t stream) {
-  if (in_dtype != RHTQ_IN_BF16 && in_dtype != RHTQ_IN_F32) return RHTQ_EINVAL;
+  if (in_dtype != RHTQ_IN_BF16 && in_dtype != RHTQ_IN_F16 && in_dtype != RHTQ_IN_F32) return RHTQ_EINVAL;
   rhtq::KernelArgs a{};
   int st = shape_args(tokens, n, block, a);
   if (st == RHTQ_OK) st = check_quant_block(n, block, fmt, group, scale_dtype);
@@ -145,7 +151,7 @@ int forward_impl(const void* x, int in_dtype, int64_t tokens, int32_t n, int32_t
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   auto run = [&](int op) -> hipError_t {
-    const hipError_t e = in_dtype == RHTQ_IN_BF16 ? rhtq::launch_fast(op, a, s) : rhtq::launch_fast_f32(op, a, s);
+    const hipError_t e = fast_for(in_dtype, op, a, s);
     if (e != hipErrorNotSupported) return e;
     return rhtq::launch_generic(op, in_dtype, a, s);
   };

@@ -125,20 +125,53 @@ struct alignas(16) H32Operands {
         }
   }
 };
+// b1 and b16 as f16 (+-1 and 0 are exact in both): the B operands of v_mfma_f32_16x16x32_f16
+// when the input itself is fp16.
+struct alignas(16) H32OperandsF16 {
+  uint16_t b1h[2][64][8];
+  uint16_t b16h[2][64][8];
+  constexpr H32OperandsF16() : b1h(), b16h() {
+    const H32Operands h;
+    for (int t = 0; t < 2; ++t)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          b1h[t][lane][e] = (uint16_t)((h.b1[t][lane][e] & 0x8000) | 0x3C00);
+          b16h[t][lane][e] = h.b16[t][lane][e] ? (uint16_t)((h.b16[t][lane][e] & 0x8000) | 0x3C00) : (uint16_t)0;
+        }
+  }
+};
 namespace {
 __constant__ H32Operands kH32Ops;
+__constant__ H32OperandsF16 kH32OpsF16;
 }
 
+// The stage-1 operands as raw 16-bit patterns: bf16 +-1, or f16 +-1 for fp16 input (H16).
+template <bool H16 = false>
 __device__ __forceinline__ bf16x8 h32_operand(int lane, int t) {
   bf16x8 r;
-  __builtin_memcpy(&r, &kH32Ops.b1[t][lane][0], 16);
+  if constexpr (H16) __builtin_memcpy(&r, &kH32OpsF16.b1h[t][lane][0], 16);
+  else __builtin_memcpy(&r, &kH32Ops.b1[t][lane][0], 16);
   return r;
 }
 
+template <bool H16 = false>
 __device__ __forceinline__ bf16x8 h16_operand(int lane, int t) {
   bf16x8 r;
-  __builtin_memcpy(&r, &kH32Ops.b16[t][lane][0], 16);
+  if constexpr (H16) __builtin_memcpy(&r, &kH32OpsF16.b16h[t][lane][0], 16);
+  else __builtin_memcpy(&r, &kH32Ops.b16[t][lane][0], 16);
   return r;
+}
+
+// One stage-1 product, c + A B with A eight input values per lane (sign bits already flipped)
+// and B a +-1 operand from h32_operand / h16_operand of the same type: bf16 input on the bf16
+// instruction, fp16 input (H16) on the f16 one.  Both read their operands exactly.
+template <bool H16>
+__device__ __forceinline__ f32x4 stage1_mma(bf16x8 av, bf16x8 hb, f32x4 c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, hb), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb, c, 0, 0, 0);
 }
 
 

@@ -117,8 +117,9 @@ __host__ __device__ inline int sign_slices(int period) {
 // CG: INT4 groups of two or more whole chunks, short of the row (a separate instantiation, so the
 // common kernels carry no code or registers for them).  F32: fp32 input, split into three exact
 // bf16 terms for the stage-1 products (three MFMAs accumulating where bf16 input takes one), no
-// prefetch; everything after stage 1 is the bf16 kernel's.
-template <int F, int LOGM, int OP, bool CG = false, bool F32 = false>
+// prefetch; everything after stage 1 is the bf16 kernel's.  H16: fp16 input, the same loads and
+// sign masks with stage 1 on the f16 matrix-core instruction.
+template <int F, int LOGM, int OP, bool CG = false, bool F32 = false, bool H16 = false>
 __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   using S = Shape<F, LOGM>;
   extern __shared__ uint32_t smem[];
@@ -160,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
     sign_tab[k] = m;
   }
   // stage-1 operand: H32 over element bits 0-4, or I2 (x) H16 for 16-wide rows (bit 4 = row)
-  const bf16x8 hb[2] = {LOGM == 4 ? h16_operand(lane, 0) : h32_operand(lane, 0),
-                        LOGM == 4 ? h16_operand(lane, 1) : h32_operand(lane, 1)};
+  const bf16x8 hb[2] = {LOGM == 4 ? h16_operand<H16>(lane, 0) : h32_operand<H16>(lane, 0),
+                        LOGM == 4 ? h16_operand<H16>(lane, 1) : h32_operand<H16>(lane, 1)};
   __syncthreads();
   float run_max = 0.0f;
   float gts = 0.0f, inv6g = 0.0f;
@@ -206,8 +207,8 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
         r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
         bf16x8 av;
         __builtin_memcpy(&av, &r, 16);
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+        d0 = stage1_mma<H16>(av, hb[0], z);
+        d1 = stage1_mma<H16>(av, hb[1], z);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[f][0][i] = d0[i]; v[f][1][i] = d1[i]; }
@@ -506,10 +507,10 @@ __global__ __launch_bounds__(kThreads) void fast_kernel(KernelArgs a) {
   }
 }
 
-template <int F, int LOGM, int OP, bool CG, bool F32>
+template <int F, int LOGM, int OP, bool CG, int IN>
 hipError_t launch_kern(const KernelArgs& a, hipStream_t s);
 
-template <int F, int LOGM, int OP, bool F32 = false>
+template <int F, int LOGM, int OP, int IN>
 hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
   using S = Shape<F, LOGM>;
   if constexpr (OP == OP_INT4) {
@@ -518,15 +519,15 @@ hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
     if (!(a.group == S::N || a.group <= S::CHUNK || (S::RPU == 1 && a.group < S::N))) return hipErrorNotSupported;
   }
   if constexpr (OP == OP_INT4 && S::RPU == 1 && S::N > S::CHUNK) {
-    if (a.group > S::CHUNK && a.group < S::N) return launch_kern<F, LOGM, OP, true, F32>(a, s);
+    if (a.group > S::CHUNK && a.group < S::N) return launch_kern<F, LOGM, OP, true, IN>(a, s);
   }
-  return launch_kern<F, LOGM, OP, false, F32>(a, s);
+  return launch_kern<F, LOGM, OP, false, IN>(a, s);
 }
 
-template <int F, int LOGM, int OP, bool CG, bool F32>
+template <int F, int LOGM, int OP, bool CG, int IN>
 hipError_t launch_kern(const KernelArgs& a, hipStream_t s) {
   using S = Shape<F, LOGM>;
-  auto kern = fast_kernel<F, LOGM, OP, CG, F32>;
+  auto kern = fast_kernel<F, LOGM, OP, CG, IN == RHTQ_IN_F32, IN == RHTQ_IN_F16>;
   const int slices = sign_slices<S>(a.sign_period);
   const size_t lds = (size_t)slices * S::NF * 64 * 16 + (size_t)kWaves * S::TBUF * 4;
   if (lds > 65536) return hipErrorNotSupported;
@@ -538,21 +539,33 @@ hipError_t launch_kern(const KernelArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int OP, bool F32 = false>
+template <int OP, int IN>
 hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
   switch (a.n) {
-    case 16: return launch_one<1, 4, OP, F32>(a, s);
-    case 32: return launch_one<1, 5, OP, F32>(a, s);
-    case 64: return launch_one<1, 6, OP, F32>(a, s);
-    case 128: return launch_one<1, 7, OP, F32>(a, s);
-    case 256: return launch_one<1, 8, OP, F32>(a, s);
-    case 512: return launch_one<1, 9, OP, F32>(a, s);
-    case 1024: return launch_one<1, 10, OP, F32>(a, s);
-    case 2048: return launch_one<1, 11, OP, F32>(a, s);
-    case 4096: return launch_one<1, 12, OP, F32>(a, s);
-    case 8192: return launch_one<1, 13, OP, F32>(a, s);
-    case 3072: return launch_one<12, 8, OP, F32>(a, s);
-    case 6144: return launch_one<12, 9, OP, F32>(a, s);
+    case 16: return launch_one<1, 4, OP, IN>(a, s);
+    case 32: return launch_one<1, 5, OP, IN>(a, s);
+    case 64: return launch_one<1, 6, OP, IN>(a, s);
+    case 128: return launch_one<1, 7, OP, IN>(a, s);
+    case 256: return launch_one<1, 8, OP, IN>(a, s);
+    case 512: return launch_one<1, 9, OP, IN>(a, s);
+    case 1024: return launch_one<1, 10, OP, IN>(a, s);
+    case 2048: return launch_one<1, 11, OP, IN>(a, s);
+    case 4096: return launch_one<1, 12, OP, IN>(a, s);
+    case 8192: return launch_one<1, 13, OP, IN>(a, s);
+    case 3072: return launch_one<12, 8, OP, IN>(a, s);
+    case 6144: return launch_one<12, 9, OP, IN>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <int IN>
+hipError_t dispatch_op(int op, const KernelArgs& a, hipStream_t s) {
+  switch (op) {
+    case OP_ROTATE: return dispatch<OP_ROTATE, IN>(a, s);
+    case OP_INT4: return dispatch<OP_INT4, IN>(a, s);
+    case OP_NVFP4: return dispatch<OP_NVFP4, IN>(a, s);
+    case OP_MXFP4: return dispatch<OP_MXFP4, IN>(a, s);
+    case OP_AMAX: return dispatch<OP_AMAX, IN>(a, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -562,37 +575,23 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
 hipError_t launch_fast_f32(int op, const KernelArgs& a, hipStream_t s) {
   if (getenv_fast_disabled()) return hipErrorNotSupported;
   if (a.n == 12288) return launch_fast12_f32(op, a, s);
-  switch (op) {
-    case OP_ROTATE: return dispatch<OP_ROTATE, true>(a, s);
-    case OP_INT4: return dispatch<OP_INT4, true>(a, s);
-    case OP_NVFP4: return dispatch<OP_NVFP4, true>(a, s);
-    case OP_MXFP4: return dispatch<OP_MXFP4, true>(a, s);
-    case OP_AMAX: return dispatch<OP_AMAX, true>(a, s);
-    default: return hipErrorNotSupported;
-  }
+  return dispatch_op<RHTQ_IN_F32>(op, a, s);
 }
 
-hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s) {
+hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
   if (getenv_fast_disabled()) return hipErrorNotSupported;
-  if (a.n == 12288) return launch_fast12(op, a, s);
-  if (a.n == 24576) return launch_fast24(op, a, s);
-  if (a.n == 22016 || a.n == 11008 || a.n == 5504 || a.n == 2752) return launch_fast172(op, a, s);
+  if (a.n == 12288) return launch_fast12(op, a, s, f16in);
+  if (a.n == 24576) return launch_fast24(op, a, s, f16in);
+  if (a.n == 22016 || a.n == 11008 || a.n == 5504 || a.n == 2752) return launch_fast172(op, a, s, f16in);
   if (a.n == 8192 || a.n == 16384) {
-    const hipError_t e = launch_fastw(op, a, s);
+    const hipError_t e = launch_fastw(op, a, s, f16in);
     if (e != hipErrorNotSupported) return e;
   }
   if (!getenv_fast2_disabled()) {
-    const hipError_t e = launch_fast2(op, a, s);
+    const hipError_t e = launch_fast2(op, a, s, f16in);
     if (e != hipErrorNotSupported) return e;
   }
-  switch (op) {
-    case OP_ROTATE: return dispatch<OP_ROTATE>(a, s);
-    case OP_INT4: return dispatch<OP_INT4>(a, s);
-    case OP_NVFP4: return dispatch<OP_NVFP4>(a, s);
-    case OP_MXFP4: return dispatch<OP_MXFP4>(a, s);
-    case OP_AMAX: return dispatch<OP_AMAX>(a, s);
-    default: return hipErrorNotSupported;
-  }
+  return f16in ? dispatch_op<RHTQ_IN_F16>(op, a, s) : dispatch_op<RHTQ_IN_BF16>(op, a, s);
 }
 
 }  // namespace rhtq

@@ -87,7 +87,7 @@ __device__ __forceinline__ void fast12_whole_subrow_groups(const KernelArgs& a, 
 
 // Rows of the workgroup as seen by wave H (a template parameter, so that every register
 // array is indexed by constants).  Both waves pass the same barriers in the same order.
-template <int OP, int H, int PER, bool F32>
+template <int OP, int H, int PER, bool F32, bool H16>
 __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, const bf16x8 (&hb)[2],
                                             const f16x8 (&hc)[2], const int lane, const float gts,
                                             const float inv6g, const int G) {
@@ -151,8 +151,8 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
           r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
           bf16x8 av;
           __builtin_memcpy(&av, &r, 16);
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
-          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+          p0 = stage1_mma<H16>(av, hb[0], z);
+          p1 = stage1_mma<H16>(av, hb[1], z);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) { d1[jl][f][0][i] = p0[i]; d1[jl][f][1][i] = p1[i]; }
@@ -284,8 +284,9 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
 
 
 // PER = 0: groups inside a wave's chunks (or per-token); PER = 1, 2, 4: INT4 groups of PER whole
-// sub-rows (a separate instantiation, so the common kernel carries no code for them).
-template <int OP, int PER, bool F32 = false>
+// sub-rows (a separate instantiation, so the common kernel carries no code for them).  F32: fp32
+// input (three bf16 terms per value); H16: fp16 input (stage 1 on the f16 matrix-core instruction).
+template <int OP, int PER, bool F32 = false, bool H16 = false>
 __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
   __shared__ Shared12 sh;
   const int lane = threadIdx.x & 63;
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
     }
     sh.sign_tab[k] = m;
   }
-  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  const bf16x8 hb[2] = {h32_operand<H16>(lane, 0), h32_operand<H16>(lane, 1)};
   const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
   __syncthreads();
 
@@ -316,30 +317,30 @@ __global__ __launch_bounds__(kT) void fast12_kernel(KernelArgs a) {
   if constexpr (OP == OP_INT4) G = a.group == kN ? 0 : __builtin_ctz((unsigned)a.group);
   if constexpr (OP == OP_NVFP4) G = 4;
   if constexpr (OP == OP_MXFP4) G = 5;
-  if (h == 0) fast12_rows<OP, 0, PER, F32>(a, sh, hb, hc, lane, gts, inv6g, G);
-  else fast12_rows<OP, 1, PER, F32>(a, sh, hb, hc, lane, gts, inv6g, G);
+  if (h == 0) fast12_rows<OP, 0, PER, F32, H16>(a, sh, hb, hc, lane, gts, inv6g, G);
+  else fast12_rows<OP, 1, PER, F32, H16>(a, sh, hb, hc, lane, gts, inv6g, G);
 }
 
-template <int OP, int PER, bool F32>
+template <int OP, int PER, int IN>
 hipError_t launch12k(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast12_kernel<OP, PER, F32>;
+  auto kern = fast12_kernel<OP, PER, IN == RHTQ_IN_F32, IN == RHTQ_IN_F16>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int OP, bool F32 = false>
+template <int OP, int IN>
 hipError_t launch12(const KernelArgs& a, hipStream_t s) {
   if (a.sign_period != kN) return hipErrorNotSupported;
   if constexpr (OP == OP_INT4) {
     // per-token, groups of 16 .. 512 inside a wave's chunks, or 1024 .. 4096 (whole sub-rows)
     if (!(a.group == kN || (a.group >= 16 && a.group <= 4096))) return hipErrorNotSupported;
-    if (a.group == 1024) return launch12k<OP, 1, F32>(a, s);
-    if (a.group == 2048) return launch12k<OP, 2, F32>(a, s);
-    if (a.group == 4096) return launch12k<OP, 4, F32>(a, s);
+    if (a.group == 1024) return launch12k<OP, 1, IN>(a, s);
+    if (a.group == 2048) return launch12k<OP, 2, IN>(a, s);
+    if (a.group == 4096) return launch12k<OP, 4, IN>(a, s);
   }
-  return launch12k<OP, 0, F32>(a, s);
+  return launch12k<OP, 0, IN>(a, s);
 }
 
 }  // namespace
@@ -349,26 +350,26 @@ int64_t fast12_grid(int64_t rows) {
   return rows < max_blocks ? rows : max_blocks;
 }
 
-hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s) {
+namespace {
+template <int IN>
+hipError_t launch12_op(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return launch12<OP_ROTATE>(a, s);
-    case OP_INT4: return launch12<OP_INT4>(a, s);
-    case OP_NVFP4: return launch12<OP_NVFP4>(a, s);
-    case OP_MXFP4: return launch12<OP_MXFP4>(a, s);
-    case OP_AMAX: return launch12<OP_AMAX>(a, s);
+    case OP_ROTATE: return launch12<OP_ROTATE, IN>(a, s);
+    case OP_INT4: return launch12<OP_INT4, IN>(a, s);
+    case OP_NVFP4: return launch12<OP_NVFP4, IN>(a, s);
+    case OP_MXFP4: return launch12<OP_MXFP4, IN>(a, s);
+    case OP_AMAX: return launch12<OP_AMAX, IN>(a, s);
     default: return hipErrorNotSupported;
   }
 }
+}  // namespace
+
+hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
+  return f16in ? launch12_op<RHTQ_IN_F16>(op, a, s) : launch12_op<RHTQ_IN_BF16>(op, a, s);
+}
 
 hipError_t launch_fast12_f32(int op, const KernelArgs& a, hipStream_t s) {
-  switch (op) {
-    case OP_ROTATE: return launch12<OP_ROTATE, true>(a, s);
-    case OP_INT4: return launch12<OP_INT4, true>(a, s);
-    case OP_NVFP4: return launch12<OP_NVFP4, true>(a, s);
-    case OP_MXFP4: return launch12<OP_MXFP4, true>(a, s);
-    case OP_AMAX: return launch12<OP_AMAX, true>(a, s);
-    default: return hipErrorNotSupported;
-  }
+  return launch12_op<RHTQ_IN_F32>(op, a, s);
 }
 
 }  // namespace rhtq

@@ -76,11 +76,28 @@ struct H172TOperands {
           }
   }
 };
+// The same operands as f16 (+-1 and 0 are exact in both) for fp16 input.
+struct H172TOperandsF16 {
+  uint16_t v[kTiles][6][64][8];
+  constexpr H172TOperandsF16() : v() {
+    const H172TOperands h;
+    for (int t = 0; t < kTiles; ++t)
+      for (int ks = 0; ks < 6; ++ks)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t b = h.v[t][ks][lane][e];
+            v[t][ks][lane][e] = b ? (uint16_t)((b & 0x8000) | 0x3C00) : (uint16_t)0;
+          }
+  }
+};
 __constant__ H172TOperands kH172TOps;
+__constant__ H172TOperandsF16 kH172TOpsF16;
 
+template <bool H16>
 __device__ __forceinline__ bf16x8 h172t_operand(int lane, int t, int ks) {
   bf16x8 r;
-  __builtin_memcpy(&r, &kH172TOps.v[t][ks][lane][0], 16);
+  if constexpr (H16) __builtin_memcpy(&r, &kH172TOpsF16.v[t][ks][lane][0], 16);
+  else __builtin_memcpy(&r, &kH172TOps.v[t][ks][lane][0], 16);
   return r;
 }
 
@@ -121,8 +138,9 @@ __device__ __forceinline__ float nnmax(float a, float b) { return __uint_as_floa
 // r / (4 / P) of the set.
 // GC: group class, 0 (one INT4 group per row: the row maximum across the four waves through
 // LDS), 4 (16-element groups: one run), 5 (32: two runs), 6 (64..256: whole
-// a'-rows); SD: INT4 scale storage (RHTQ_SCALE_F32 / F16).
-template <int P, int OP, int GC, int SD, int NT>
+// a'-rows); SD: INT4 scale storage (RHTQ_SCALE_F32 / F16).  H16: fp16 input (stage 1 on the f16
+// matrix-core instruction against f16 operands; everything else is the same).
+template <int P, int OP, int GC, int SD, int NT, bool H16>
 __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
   static_assert(P == 1 || P == 2 || P == 4, "one, two or four rows per work row");
   constexpr int kPn = kN / P;     // elements per row
@@ -141,7 +159,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand(lane, wave + kW * j, ks);
+    for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand<H16>(lane, wave + kW * j, ks);
   const f16x8 ha[2] = {h32_b_operand<P == 4>(lane, 0), h32_b_operand<P == 4>(lane, 1)};
 
   float gts = 0.0f, inv6g = 0.0f;
@@ -214,7 +232,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], hb[j][ks], ks == 0 ? z : acc[j][mt], 0, 0, 0);
+          acc[j][mt] = stage1_mma<H16>(av[mt], hb[j][ks], ks == 0 ? z : acc[j][mt]);
         }
     }
     __syncthreads();   // every wave has read this row
@@ -512,7 +530,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   }
 }
 
-template <int P, int OP, int GC, int SD>
+template <int P, int OP, int GC, int SD, bool H16 = false>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 : 4))) void fast172_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
   __shared__ uint4 sgn[kChunks];
@@ -535,10 +553,10 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 
   for (int c = tid; c < kXBytes / 16; c += kT) reinterpret_cast<uint4*>(xs)[c] = make_uint4(0, 0, 0, 0);   // a >= 172 stays 0
   // waves with a tile fewer than the busiest (kTiles not a multiple of kW) take the smaller copy
   if constexpr (kTiles % kW == 0) {
-    rows172<P, OP, GC, SD, kNT>(a, xs, sgn, wmax);
+    rows172<P, OP, GC, SD, kNT, H16>(a, xs, sgn, wmax);
   } else {
-    if ((tid >> 6) < kTiles % kW) rows172<P, OP, GC, SD, kNT>(a, xs, sgn, wmax);
-    else rows172<P, OP, GC, SD, kNT - 1>(a, xs, sgn, wmax);
+    if ((tid >> 6) < kTiles % kW) rows172<P, OP, GC, SD, kNT, H16>(a, xs, sgn, wmax);
+    else rows172<P, OP, GC, SD, kNT - 1, H16>(a, xs, sgn, wmax);
   }
 }
 
@@ -554,7 +572,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 
 constexpr int kN2 = 2 * kN;          // 22016
 constexpr int kChunks2 = 2 * kChunks;
 
-template <int OP, int GC, int SD, int NT>
+template <int OP, int GC, int SD, int NT, bool H16>
 __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
@@ -610,7 +628,7 @@ __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand(lane, t0 + kW * j, ks);
+      for (int ks = 0; ks < 6; ++ks) hb[j][ks] = h172t_operand<H16>(lane, t0 + kW * j, ks);
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) {
       bf16x8 av[4];
@@ -621,7 +639,7 @@ __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], hb[j][ks], ks == 0 ? z : acc[j][mt], 0, 0, 0);
+          acc[j][mt] = stage1_mma<H16>(av[mt], hb[j][ks], ks == 0 ? z : acc[j][mt]);
         }
     }
   };
@@ -913,7 +931,7 @@ __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const 
   }
 }
 
-template <int OP, int GC, int SD>
+template <int OP, int GC, int SD, bool H16 = false>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 : 4))) void fast344_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
   __shared__ uint4 sgn[kChunks2];
@@ -934,49 +952,50 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 
   }
   for (int c = tid; c < kXBytes / 16; c += kT) reinterpret_cast<uint4*>(xs)[c] = make_uint4(0, 0, 0, 0);   // a >= 172 stays 0
   if constexpr (kTiles % kW == 0) {
-    rows344<OP, GC, SD, kNT>(a, xs, sgn, wmax);
+    rows344<OP, GC, SD, kNT, H16>(a, xs, sgn, wmax);
   } else {
-    if ((tid >> 6) < kTiles % kW) rows344<OP, GC, SD, kNT>(a, xs, sgn, wmax);
-    else rows344<OP, GC, SD, kNT - 1>(a, xs, sgn, wmax);
+    if ((tid >> 6) < kTiles % kW) rows344<OP, GC, SD, kNT, H16>(a, xs, sgn, wmax);
+    else rows344<OP, GC, SD, kNT - 1, H16>(a, xs, sgn, wmax);
   }
 }
 
-template <int OP, int GC, int SD>
+template <int OP, int GC, int SD, bool H16>
 hipError_t launch344(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast344_kernel<OP, GC, SD>;
+  auto kern = fast344_kernel<OP, GC, SD, H16>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int SD>
+template <int SD, bool H16>
 hipError_t launch344_int4(const KernelArgs& a, hipStream_t s) {
-  if (a.group == kN2) return launch344<OP_INT4, 0, SD>(a, s);   // one group per row
+  if (a.group == kN2) return launch344<OP_INT4, 0, SD, H16>(a, s);   // one group per row
   switch (a.group) {
-    case 16: return launch344<OP_INT4, 4, SD>(a, s);
-    case 32: return launch344<OP_INT4, 5, SD>(a, s);
-    case 64: case 128: case 256: case 512: return launch344<OP_INT4, 6, SD>(a, s);
+    case 16: return launch344<OP_INT4, 4, SD, H16>(a, s);
+    case 32: return launch344<OP_INT4, 5, SD, H16>(a, s);
+    case 64: case 128: case 256: case 512: return launch344<OP_INT4, 6, SD, H16>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
+template <bool H16>
 hipError_t launch344_op(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return launch344<OP_ROTATE, 6, 0>(a, s);
+    case OP_ROTATE: return launch344<OP_ROTATE, 6, 0, H16>(a, s);
     case OP_INT4:
-      return a.scale_dtype == RHTQ_SCALE_F32 ? launch344_int4<RHTQ_SCALE_F32>(a, s)
-                                             : launch344_int4<RHTQ_SCALE_F16>(a, s);
-    case OP_NVFP4: return launch344<OP_NVFP4, 4, 0>(a, s);
-    case OP_MXFP4: return launch344<OP_MXFP4, 5, 0>(a, s);
-    case OP_AMAX: return launch344<OP_AMAX, 6, 0>(a, s);
+      return a.scale_dtype == RHTQ_SCALE_F32 ? launch344_int4<RHTQ_SCALE_F32, H16>(a, s)
+                                             : launch344_int4<RHTQ_SCALE_F16, H16>(a, s);
+    case OP_NVFP4: return launch344<OP_NVFP4, 4, 0, H16>(a, s);
+    case OP_MXFP4: return launch344<OP_MXFP4, 5, 0, H16>(a, s);
+    case OP_AMAX: return launch344<OP_AMAX, 6, 0, H16>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
-template <int P, int OP, int GC, int SD>
+template <int P, int OP, int GC, int SD, bool H16>
 hipError_t launch172(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast172_kernel<P, OP, GC, SD>;
+  auto kern = fast172_kernel<P, OP, GC, SD, H16>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int64_t vrows = (a.rows + P - 1) / P;
   const int grid = (int)(vrows < max_blocks ? vrows : max_blocks);
@@ -984,44 +1003,51 @@ hipError_t launch172(const KernelArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int P, int SD>
+template <int P, int SD, bool H16>
 hipError_t launch172_int4(const KernelArgs& a, hipStream_t s) {
-  if (a.group == kN / P) return launch172<P, OP_INT4, 0, SD>(a, s);   // one group per row
+  if (a.group == kN / P) return launch172<P, OP_INT4, 0, SD, H16>(a, s);   // one group per row
   switch (a.group) {
-    case 16: return launch172<P, OP_INT4, 4, SD>(a, s);
-    case 32: return launch172<P, OP_INT4, 5, SD>(a, s);
-    case 64: return launch172<P, OP_INT4, 6, SD>(a, s);
-    case 128: return P <= 2 ? launch172<P, OP_INT4, 6, SD>(a, s) : hipErrorNotSupported;
-    case 256: return P == 1 ? launch172<P, OP_INT4, 6, SD>(a, s) : hipErrorNotSupported;
+    case 16: return launch172<P, OP_INT4, 4, SD, H16>(a, s);
+    case 32: return launch172<P, OP_INT4, 5, SD, H16>(a, s);
+    case 64: return launch172<P, OP_INT4, 6, SD, H16>(a, s);
+    case 128: return P <= 2 ? launch172<P, OP_INT4, 6, SD, H16>(a, s) : hipErrorNotSupported;
+    case 256: return P == 1 ? launch172<P, OP_INT4, 6, SD, H16>(a, s) : hipErrorNotSupported;
     default: return hipErrorNotSupported;
   }
 }
 
-template <int P>
+template <int P, bool H16>
 hipError_t launch172_p(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return launch172<P, OP_ROTATE, 6, 0>(a, s);
+    case OP_ROTATE: return launch172<P, OP_ROTATE, 6, 0, H16>(a, s);
     case OP_INT4:
-      return a.scale_dtype == RHTQ_SCALE_F32 ? launch172_int4<P, RHTQ_SCALE_F32>(a, s)
-                                             : launch172_int4<P, RHTQ_SCALE_F16>(a, s);
-    case OP_NVFP4: return launch172<P, OP_NVFP4, 4, 0>(a, s);
-    case OP_MXFP4: return launch172<P, OP_MXFP4, 5, 0>(a, s);
-    case OP_AMAX: return launch172<P, OP_AMAX, 6, 0>(a, s);
+      return a.scale_dtype == RHTQ_SCALE_F32 ? launch172_int4<P, RHTQ_SCALE_F32, H16>(a, s)
+                                             : launch172_int4<P, RHTQ_SCALE_F16, H16>(a, s);
+    case OP_NVFP4: return launch172<P, OP_NVFP4, 4, 0, H16>(a, s);
+    case OP_MXFP4: return launch172<P, OP_MXFP4, 5, 0, H16>(a, s);
+    case OP_AMAX: return launch172<P, OP_AMAX, 6, 0, H16>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s) {
+namespace {
+template <bool H16>
+hipError_t launch172_any(int op, const KernelArgs& a, hipStream_t s) {
   if (reinterpret_cast<uintptr_t>(a.x) & 15) return hipErrorNotSupported;
-  if (a.n == kN && a.sign_period == kN) return launch172_p<1>(op, a, s);
+  if (a.n == kN && a.sign_period == kN) return launch172_p<1, H16>(op, a, s);
   // 22016 = 172 x 128: the two 64-column halves of each row in turn
-  if (a.n == kN2 && a.sign_period == kN2) return launch344_op(op, a, s);
+  if (a.n == kN2 && a.sign_period == kN2) return launch344_op<H16>(op, a, s);
   // 5504 = 172 x 32 and 2752 = 172 x 16: two and four rows per work row
-  if (a.n == kN / 2 && a.sign_period == kN / 2) return launch172_p<2>(op, a, s);
-  if (a.n == kN / 4 && a.sign_period == kN / 4) return launch172_p<4>(op, a, s);
+  if (a.n == kN / 2 && a.sign_period == kN / 2) return launch172_p<2, H16>(op, a, s);
+  if (a.n == kN / 4 && a.sign_period == kN / 4) return launch172_p<4, H16>(op, a, s);
   return hipErrorNotSupported;
+}
+}  // namespace
+
+hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
+  return f16in ? launch172_any<true>(op, a, s) : launch172_any<false>(op, a, s);
 }
 
 }  // namespace rhtq

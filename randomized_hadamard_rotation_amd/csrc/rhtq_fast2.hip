@@ -73,7 +73,8 @@ struct Tune2 {
   static constexpr int WAVES = LOGM == 10 ? 4 : 3;
 };
 
-template <int LOGM, int OP, int DEPTH, int WAVES>
+// H16: fp16 input (stage 1 on the f16 matrix-core instruction; everything else is the same).
+template <int LOGM, int OP, int DEPTH, int WAVES, bool H16 = false>
 __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void fast2_kernel(KernelArgs a) {
   using S2 = Shape2<LOGM>;
@@ -110,7 +111,7 @@ void fast2_kernel(KernelArgs a) {
     }
     sign_tab[k] = m;
   }
-  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  const bf16x8 hb[2] = {h32_operand<H16>(lane, 0), h32_operand<H16>(lane, 1)};
   const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
   __syncthreads();
 
@@ -140,8 +141,8 @@ void fast2_kernel(KernelArgs a) {
       bf16x8 av;
       __builtin_memcpy(&av, &r, 16);
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
-      const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+      const f32x4 p0 = stage1_mma<H16>(av, hb[0], z);
+      const f32x4 p1 = stage1_mma<H16>(av, hb[1], z);
 #pragma unroll
       for (int i = 0; i < 4; ++i) { d1[f][0][i] = p0[i]; d1[f][1][i] = p1[i]; }
     }
@@ -297,8 +298,8 @@ struct PairShared {
 };
 
 // Wave H's half of one row (H a template parameter so every register array is indexed by
-// constants).
-template <int OP, int H, bool SLICED>
+// constants).  H16: fp16 input.
+template <int OP, int H, bool SLICED, bool H16>
 __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, int64_t row) {
   constexpr int N = 4096;
   const int lane = threadIdx.x & 63;
@@ -308,7 +309,7 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
 
   // constant operands and signs first (L2 hits), then the row's fragments; the scheduling
   // barriers keep that order, so each fragment's wait covers only the loads ahead of it
-  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  const bf16x8 hb[2] = {h32_operand<H16>(lane, 0), h32_operand<H16>(lane, 1)};
   const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
   const f16x8 hn[2] = {h32_stage2_operand_neg(lane, 0), h32_stage2_operand_neg(lane, 1)};
   // SLICED: the rows are blocks of longer rows, and the block's slice of the sign vector
@@ -344,8 +345,8 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
     bf16x8 av;
     __builtin_memcpy(&av, &r, 16);
     const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
-    const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+    const f32x4 p0 = stage1_mma<H16>(av, hb[0], z);
+    const f32x4 p1 = stage1_mma<H16>(av, hb[1], z);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { d1[fl][0][i] = p0[i]; d1[fl][1][i] = p1[i]; }
     // the previous fragment's maximum while this one's products run
@@ -485,35 +486,35 @@ __device__ __forceinline__ void pair_row(const KernelArgs& a, PairShared& sh, in
   }
 }
 
-template <int OP, bool SLICED>
+template <int OP, bool SLICED, bool H16 = false>
 __global__ __launch_bounds__(128 * kPairRows) __attribute__((amdgpu_waves_per_eu(RHTQ_PAIR_WAVES))) void fast2p_kernel(KernelArgs a) {
   __shared__ PairShared sh[kPairRows];
   const int wave = threadIdx.x >> 6, pair = wave >> 1;
   int64_t row = kPairRows * (int64_t)blockIdx.x + pair;
   if (row >= a.rows) row = a.rows - 1;   // past the end: repeat the last row (same bytes, same barriers)
-  if (wave & 1) pair_row<OP, 1, SLICED>(a, sh[pair], row);
-  else pair_row<OP, 0, SLICED>(a, sh[pair], row);
+  if (wave & 1) pair_row<OP, 1, SLICED, H16>(a, sh[pair], row);
+  else pair_row<OP, 0, SLICED, H16>(a, sh[pair], row);
 }
 
-template <int OP>
+template <int OP, bool H16>
 hipError_t launch2p(const KernelArgs& a, hipStream_t s) {
   if constexpr (OP == OP_INT4) {
     if (!(a.group == 4096 || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
   if (a.rows > 0xFFFFFFFE) return hipErrorNotSupported;
   const dim3 grid((unsigned)((a.rows + kPairRows - 1) / kPairRows));
-  if (a.sign_period == 4096) hipLaunchKernelGGL((fast2p_kernel<OP, false>), grid, dim3(128 * kPairRows), 0, s, a);
-  else hipLaunchKernelGGL((fast2p_kernel<OP, true>), grid, dim3(128 * kPairRows), 0, s, a);
+  if (a.sign_period == 4096) hipLaunchKernelGGL((fast2p_kernel<OP, false, H16>), grid, dim3(128 * kPairRows), 0, s, a);
+  else hipLaunchKernelGGL((fast2p_kernel<OP, true, H16>), grid, dim3(128 * kPairRows), 0, s, a);
   return hipGetLastError();
 }
 
-template <int LOGM, int OP>
+template <int LOGM, int OP, bool H16>
 hipError_t launch2(const KernelArgs& a, hipStream_t s) {
   using S2 = Shape2<LOGM>;
   if constexpr (OP == OP_INT4) {
     if (!(a.group == S2::N || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-  auto kern = fast2_kernel<LOGM, OP, Tune2<LOGM>::DEPTH, Tune2<LOGM>::WAVES>;
+  auto kern = fast2_kernel<LOGM, OP, Tune2<LOGM>::DEPTH, Tune2<LOGM>::WAVES, H16>;
   static const int max_blocks = resident_blocks((const void*)kern, kThreads2, S2::NF * 64 * 16);
   const int64_t want = (a.rows + kWaves2 - 1) / kWaves2;
   const int grid = (int)(want < max_blocks ? want : max_blocks);
@@ -532,32 +533,39 @@ inline int64_t pair_rows_limit() {
   return v;
 }
 
-template <int OP>
+template <int OP, bool H16>
 hipError_t dispatch2(const KernelArgs& a, hipStream_t s) {
   switch (a.n) {
-    case 1024: return launch2<10, OP>(a, s);
-    case 2048: return launch2<11, OP>(a, s);
+    case 1024: return launch2<10, OP, H16>(a, s);
+    case 2048: return launch2<11, OP, H16>(a, s);
     case 4096:
       if (a.rows <= pair_rows_limit()) {
-        const hipError_t e = launch2p<OP>(a, s);
+        const hipError_t e = launch2p<OP, H16>(a, s);
         if (e != hipErrorNotSupported) return e;
       }
-      return launch2<12, OP>(a, s);
+      return launch2<12, OP, H16>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s) {
+namespace {
+template <bool H16>
+hipError_t dispatch2_op(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return dispatch2<OP_ROTATE>(a, s);
-    case OP_INT4: return dispatch2<OP_INT4>(a, s);
-    case OP_NVFP4: return dispatch2<OP_NVFP4>(a, s);
-    case OP_MXFP4: return dispatch2<OP_MXFP4>(a, s);
-    case OP_AMAX: return dispatch2<OP_AMAX>(a, s);
+    case OP_ROTATE: return dispatch2<OP_ROTATE, H16>(a, s);
+    case OP_INT4: return dispatch2<OP_INT4, H16>(a, s);
+    case OP_NVFP4: return dispatch2<OP_NVFP4, H16>(a, s);
+    case OP_MXFP4: return dispatch2<OP_MXFP4, H16>(a, s);
+    case OP_AMAX: return dispatch2<OP_AMAX, H16>(a, s);
     default: return hipErrorNotSupported;
   }
+}
+}  // namespace
+
+hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
+  return f16in ? dispatch2_op<true>(op, a, s) : dispatch2_op<false>(op, a, s);
 }
 
 }  // namespace rhtq

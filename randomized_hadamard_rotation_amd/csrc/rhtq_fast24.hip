@@ -86,17 +86,19 @@ __device__ __forceinline__ uint4 sign_masks(uint32_t b, int f) {
   return m;
 }
 
-// Bits 0-4 of 8 signed bf16 inputs against the H32 operand of one output half (exact).
+// Bits 0-4 of 8 signed inputs (bf16, or fp16 when H16) against the H32 operand of one output
+// half (exact).
+template <bool H16>
 __device__ __forceinline__ f32x4 stage1(const uint4& r, const bf16x8& hbt) {
   bf16x8 av;
   __builtin_memcpy(&av, &r, 16);
   const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hbt, z, 0, 0, 0);
+  return stage1_mma<H16>(av, hbt, z);
 }
 
 // Rows of the workgroup as seen by wave H (a template parameter, so that every register
 // array is indexed by constants).  All four waves pass the same barriers in the same order.
-template <int OP, int H>
+template <int OP, int H, bool H16>
 __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, const bf16x8 (&hb)[2],
                                             const f16x8 (&hc)[2], const uint32_t (&sb)[kOwn], const int lane,
                                             const float gts, const float inv6g, const int G) {
@@ -138,8 +140,8 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
         uint4& r = raw[jl][f];
         const uint4 mk = sign_masks(sb[jl], f);
         r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
-        const f32x4 p0 = stage1(r, hb[0]);
-        const f32x4 p1 = stage1(r, hb[1]);
+        const f32x4 p0 = stage1<H16>(r, hb[0]);
+        const f32x4 p1 = stage1<H16>(r, hb[1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fmaxf(fabsf(p0[i]), fabsf(p1[i])));
       }
@@ -157,8 +159,8 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
       float d1[kNF][2][4];   // [f][t][i]: stage 1 of this sub-row again
 #pragma unroll
       for (int f = 0; f < kNF; ++f) {
-        const f32x4 p0 = stage1(raw[jl][f], hb[0]);
-        const f32x4 p1 = stage1(raw[jl][f], hb[1]);
+        const f32x4 p0 = stage1<H16>(raw[jl][f], hb[0]);
+        const f32x4 p1 = stage1<H16>(raw[jl][f], hb[1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) { d1[f][0][i] = p0[i]; d1[f][1][i] = p1[i]; }
       }
@@ -299,7 +301,8 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
   }
 }
 
-template <int OP>
+// H16: fp16 input (stage 1 on the f16 matrix-core instruction).
+template <int OP, bool H16 = false>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fast24_kernel(KernelArgs a) {
   __shared__ Shared24 sh;
   const int lane = threadIdx.x & 63;
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fa
   uint32_t sb[kOwn];
 #pragma unroll
   for (int jl = 0; jl < kOwn; ++jl) sb[jl] = pack_signs(a.signs, h, jl, lane);
-  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  const bf16x8 hb[2] = {h32_operand<H16>(lane, 0), h32_operand<H16>(lane, 1)};
   const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
 
   float gts = 0.0f, inv6g = 0.0f;
@@ -321,37 +324,42 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fa
   if constexpr (OP == OP_NVFP4) G = 4;
   if constexpr (OP == OP_MXFP4) G = 5;
   switch (h) {
-    case 0: fast24_rows<OP, 0>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    case 1: fast24_rows<OP, 1>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    case 2: fast24_rows<OP, 2>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    default: fast24_rows<OP, 3>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 0: fast24_rows<OP, 0, H16>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 1: fast24_rows<OP, 1, H16>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 2: fast24_rows<OP, 2, H16>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    default: fast24_rows<OP, 3, H16>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
   }
 }
 
-template <int OP>
+template <int OP, bool H16>
 hipError_t launch24(const KernelArgs& a, hipStream_t s) {
   if (a.sign_period != kN) return hipErrorNotSupported;
   if constexpr (OP == OP_INT4) {
     if (!(a.group == kN || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-  auto kern = fast24_kernel<OP>;
+  auto kern = fast24_kernel<OP, H16>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_fast24(int op, const KernelArgs& a, hipStream_t s) {
+template <bool H16>
+hipError_t launch24_op(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return launch24<OP_ROTATE>(a, s);
-    case OP_INT4: return launch24<OP_INT4>(a, s);
-    case OP_NVFP4: return launch24<OP_NVFP4>(a, s);
-    case OP_MXFP4: return launch24<OP_MXFP4>(a, s);
-    case OP_AMAX: return launch24<OP_AMAX>(a, s);
+    case OP_ROTATE: return launch24<OP_ROTATE, H16>(a, s);
+    case OP_INT4: return launch24<OP_INT4, H16>(a, s);
+    case OP_NVFP4: return launch24<OP_NVFP4, H16>(a, s);
+    case OP_MXFP4: return launch24<OP_MXFP4, H16>(a, s);
+    case OP_AMAX: return launch24<OP_AMAX, H16>(a, s);
     default: return hipErrorNotSupported;
   }
+}
+
+}  // namespace
+
+hipError_t launch_fast24(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
+  return f16in ? launch24_op<true>(op, a, s) : launch24_op<false>(op, a, s);
 }
 
 }  // namespace rhtq

@@ -122,7 +122,8 @@ __device__ __forceinline__ void exchange_round(Slots& v, float& S, float& invS, 
 
 // Rows of the workgroup as seen by wave K (a template parameter, so that every register array
 // is indexed by constants).  All waves of the workgroup take the same rows and barriers.
-template <int B, int OP, int K>
+// H16: fp16 input (stage 1 on the f16 matrix-core instruction).
+template <int B, int OP, int K, bool H16>
 __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B>& sh) {
   constexpr int W = 1 << B, N = kSub << B;
   const int lane = threadIdx.x & 63;
@@ -130,7 +131,7 @@ __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const int lcol = 32 * (lane & 15) + 8 * (lane >> 4);   // this lane's 8 elements within a fragment
   const int lc = (lane >> 4) | ((lane & 15) << 2);       // element bits 3-4 = lane >> 4, 5-8 = lane & 15
-  const bf16x8 hb[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+  const bf16x8 hb[2] = {h32_operand<H16>(lane, 0), h32_operand<H16>(lane, 1)};
   const f16x8 hc[2] = {h32_stage2_operand(lane, 0), h32_stage2_operand(lane, 1)};
   // bf16 sign-bit masks of the 8 elements this lane loads in each fragment of its sub-row, held
   // in registers for the whole kernel (every row has the same signs)
@@ -175,8 +176,8 @@ __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B
       bf16x8 av;
       __builtin_memcpy(&av, &r, 16);
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[0], z, 0, 0, 0);
-      const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb[1], z, 0, 0, 0);
+      const f32x4 p0 = stage1_mma<H16>(av, hb[0], z);
+      const f32x4 p1 = stage1_mma<H16>(av, hb[1], z);
 #pragma unroll
       for (int i = 0; i < 4; ++i) { d1[f][0][i] = p0[i]; d1[f][1][i] = p1[i]; }
     }
@@ -284,24 +285,24 @@ __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B
   }
 }
 
-template <int B, int OP>
+template <int B, int OP, bool H16 = false>
 __global__ __launch_bounds__(64 << B) void fastw_kernel(KernelArgs a) {
   __shared__ WideShared<1 << B> sh;
   const int wave = threadIdx.x >> 6;
   if constexpr (B == 1) {
-    if (wave == 0) wide_rows<B, OP, 0>(a, sh);
-    else wide_rows<B, OP, 1>(a, sh);
+    if (wave == 0) wide_rows<B, OP, 0, H16>(a, sh);
+    else wide_rows<B, OP, 1, H16>(a, sh);
   } else {
     switch (wave) {
-      case 0: wide_rows<B, OP, 0>(a, sh); break;
-      case 1: wide_rows<B, OP, 1>(a, sh); break;
-      case 2: wide_rows<B, OP, 2>(a, sh); break;
-      default: wide_rows<B, OP, 3>(a, sh); break;
+      case 0: wide_rows<B, OP, 0, H16>(a, sh); break;
+      case 1: wide_rows<B, OP, 1, H16>(a, sh); break;
+      case 2: wide_rows<B, OP, 2, H16>(a, sh); break;
+      default: wide_rows<B, OP, 3, H16>(a, sh); break;
     }
   }
 }
 
-template <int B, int OP>
+template <int B, int OP, bool H16>
 hipError_t launchw(const KernelArgs& a, hipStream_t s) {
   constexpr int N = kSub << B;
   if (a.sign_period != N) return hipErrorNotSupported;   // block-diagonal calls: the other kernels
@@ -309,33 +310,38 @@ hipError_t launchw(const KernelArgs& a, hipStream_t s) {
   if constexpr (OP == OP_INT4) {
     if (!(a.group == N || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-  auto kern = fastw_kernel<B, OP>;
+  auto kern = fastw_kernel<B, OP, H16>;
   static const int max_blocks = resident_blocks((const void*)kern, 64 << B, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 << B), 0, s, a);
   return hipGetLastError();
 }
 
-template <int OP>
+template <int OP, bool H16>
 hipError_t dispatchw(const KernelArgs& a, hipStream_t s) {
   switch (a.n) {
-    case 8192: return launchw<1, OP>(a, s);
-    case 16384: return launchw<2, OP>(a, s);
+    case 8192: return launchw<1, OP, H16>(a, s);
+    case 16384: return launchw<2, OP, H16>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <bool H16>
+hipError_t dispatchw_op(int op, const KernelArgs& a, hipStream_t s) {
+  switch (op) {
+    case OP_ROTATE: return dispatchw<OP_ROTATE, H16>(a, s);
+    case OP_INT4: return dispatchw<OP_INT4, H16>(a, s);
+    case OP_NVFP4: return dispatchw<OP_NVFP4, H16>(a, s);
+    case OP_MXFP4: return dispatchw<OP_MXFP4, H16>(a, s);
+    case OP_AMAX: return dispatchw<OP_AMAX, H16>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fastw(int op, const KernelArgs& a, hipStream_t s) {
-  switch (op) {
-    case OP_ROTATE: return dispatchw<OP_ROTATE>(a, s);
-    case OP_INT4: return dispatchw<OP_INT4>(a, s);
-    case OP_NVFP4: return dispatchw<OP_NVFP4>(a, s);
-    case OP_MXFP4: return dispatchw<OP_MXFP4>(a, s);
-    case OP_AMAX: return dispatchw<OP_AMAX>(a, s);
-    default: return hipErrorNotSupported;
-  }
+hipError_t launch_fastw(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
+  return f16in ? dispatchw_op<true>(op, a, s) : dispatchw_op<false>(op, a, s);
 }
 
 }  // namespace rhtq

@@ -123,6 +123,14 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(KernelArgs a) {
             v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
             v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z);
             v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
+          } else if constexpr (IN == RHTQ_IN_F16) {
+            const uint4 raw = *(const uint4*)((const uint16_t*)a.x + gbase + e0);
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {   // f16 -> f32 is exact
+              v[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xFFFFu));
+              v[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
+            }
           } else {
             const float4* p = (const float4*)((const float*)a.x + gbase + e0);
             const float4 p0 = p[0], p1 = p[1];
@@ -406,6 +414,15 @@ hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t
       case OP_MXFP4: return dispatch_width<RHTQ_IN_BF16, OP_MXFP4>(a, s);
       case OP_AMAX: return dispatch_width<RHTQ_IN_BF16, OP_AMAX>(a, s);
       case OP_INVERSE: return dispatch_width<RHTQ_IN_BF16, OP_INVERSE>(a, s);
+    }
+  } else if (in_dtype == RHTQ_IN_F16) {
+    switch (op) {
+      case OP_ROTATE: return dispatch_width<RHTQ_IN_F16, OP_ROTATE>(a, s);
+      case OP_INT4: return dispatch_width<RHTQ_IN_F16, OP_INT4>(a, s);
+      case OP_NVFP4: return dispatch_width<RHTQ_IN_F16, OP_NVFP4>(a, s);
+      case OP_MXFP4: return dispatch_width<RHTQ_IN_F16, OP_MXFP4>(a, s);
+      case OP_AMAX: return dispatch_width<RHTQ_IN_F16, OP_AMAX>(a, s);
+      case OP_INVERSE: return hipErrorInvalidValue;  // inverse input is packed codes
     }
   } else {
     switch (op) {

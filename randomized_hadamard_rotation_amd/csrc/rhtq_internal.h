@@ -41,9 +41,10 @@ struct KernelArgs {
 // Returns hipSuccess or the launch error.
 hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t s);
 
-// Register-resident fast path (bf16 input).  Returns hipErrorNotSupported when the
-// (op, n, group) combination has no fast kernel; the caller then uses the generic one.
-hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s);
+// Register-resident fast path for 16-bit input: bf16, or fp16 when f16in (the same kernels with
+// stage 1 on the f16 matrix-core instruction).  Returns hipErrorNotSupported when the
+// (op, n, group, input type) combination has no fast kernel; the caller then uses the generic one.
+hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
 
 // fp32 input on the single-stage register-resident kernels (widths 16 .. 8192, 3072, 6144) and
 // the 12288 kernel: each value is split into three exact bf16 terms for the stage-1 products.  Returns
@@ -52,7 +53,7 @@ hipError_t launch_fast_f32(int op, const KernelArgs& a, hipStream_t s);
 
 // Two-wave kernel for 12288-wide rows (called by launch_fast), and its fp32-input form
 // (called by launch_fast_f32).
-hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s);
+hipError_t launch_fast12(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
 hipError_t launch_fast12_f32(int op, const KernelArgs& a, hipStream_t s);
 
 // The grid launch_fast12 uses for per-group INT4 on `rows` rows (resident workgroups, at most
@@ -60,17 +61,17 @@ hipError_t launch_fast12_f32(int op, const KernelArgs& a, hipStream_t s);
 int64_t fast12_grid(int64_t rows);
 
 // Four-wave kernel for 24576-wide rows, H12 (x) H2048 (called by launch_fast).
-hipError_t launch_fast24(int op, const KernelArgs& a, hipStream_t s);
+hipError_t launch_fast24(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
 
 // Matrix-core kernel for 11008-wide rows, H172 (x) H64 (called by launch_fast).
-hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s);
+hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
 
 // Two-stage matrix-core kernel for 1024-, 2048- and 4096-wide rows (called by launch_fast).
-hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s);
+hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
 
 // 8192- and 16384-wide rows, 2 or 4 waves per row with the top index bits exchanged through LDS
 // (called by launch_fast).
-hipError_t launch_fastw(int op, const KernelArgs& a, hipStream_t s);
+hipError_t launch_fastw(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
 
 // Integer matrix-core inverse for KV-cache rows (64, 128, 256) with one INT4 scale per row.
 // Returns hipErrorNotSupported for other cases (the generic kernel then runs).

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(R):
 
 
 def test_abi_version_and_status_strings(R):
-    assert R.rhtq_abi_version() == 3
+    assert R.rhtq_abi_version() == 4
     assert R.rhtq_status_str(0) == "ok"
     assert "invalid" in R.rhtq_status_str(1)
     assert "unsupported" in R.rhtq_status_str(2)
@@ -81,6 +81,9 @@ def test_host_validation(R):
     # rotate
     assert lib.rhtq_rotate(fake, 0, -1, 4096, None, fake, s) == R.RHTQ_EINVAL
     assert lib.rhtq_rotate(fake, 7, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
+    assert lib.rhtq_rotate(fake, 3, 4, 4096, None, fake, s) == R.RHTQ_EINVAL     # no input type 3
+    assert lib.rhtq_rotate(mis, R.RHTQ_IN_F16, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
+    assert lib.rhtq_rotate(None, R.RHTQ_IN_F16, 0, 4096, None, None, s) == R.RHTQ_OK
     assert lib.rhtq_rotate(fake, 0, 4, 100, None, fake, s) == R.RHTQ_EUNSUPPORTED
     assert lib.rhtq_rotate(None, 0, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
     assert lib.rhtq_rotate(mis, 0, 4, 4096, None, fake, s) == R.RHTQ_EINVAL
@@ -106,6 +109,9 @@ def test_host_validation(R):
     assert F(fake, 0, 4, 4096, None, 0, 0, 0, fake, ctypes.c_void_p(0x100002), None, 0, s) == R.RHTQ_EINVAL
     assert F(fake, 0, 4, 4096, mis, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EINVAL
     assert F(None, 0, 0, 4096, None, 0, 0, 0, None, None, None, 0, s) == R.RHTQ_OK
+    assert F(fake, 3, 4, 4096, None, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EINVAL
+    assert F(mis, R.RHTQ_IN_F16, 4, 4096, None, 0, 0, 0, fake, fake, None, 0, s) == R.RHTQ_EINVAL
+    assert F(None, R.RHTQ_IN_F16, 0, 4096, None, 0, 0, 0, None, None, None, 0, s) == R.RHTQ_OK
     # inverse
     I = lambda *a: lib.rhtq_inverse(*a)
     assert I(fake, fake, None, -1, 4096, None, 0, 0, 0, fake, s) == R.RHTQ_EINVAL

@@ -262,7 +262,7 @@ def test_rotate_every_width(R, n):
             g = torch.Generator().manual_seed(n + tokens)
             xc = torch.randn(tokens, n, generator=g) * torch.exp(torch.randn(n, generator=g))
             s = None if seed is None else splitmix64_signs(seed, n)
-            for dt in (torch.bfloat16, torch.float32):
+            for dt in (torch.bfloat16, torch.float16, torch.float32):
                 x = xc.to(dt).to(dev())
                 y = to_np(R.rhtq_rotate(x, s))
                 C.check_rotation(y, O.rotate(x.cpu(), s))
@@ -274,7 +274,7 @@ def test_quantise_every_width(R, n):
     g = torch.Generator().manual_seed(3 * n)
     xc = torch.randn(35, n, generator=g) * torch.exp(torch.randn(n, generator=g))
     s = splitmix64_signs(2, n)
-    for dt in (torch.bfloat16, torch.float32):
+    for dt in (torch.bfloat16, torch.float16, torch.float32):
         x = xc.to(dt).to(dev())
         y_ref = O.rotate(x.cpu(), s)
         groups = [0, 16, 128] if n % 128 == 0 else [0, 16]
@@ -587,6 +587,56 @@ def test_fp32_rows_near_the_normal_floor(R, n):
             check_forward(R, x.to(dev()), s, "int4", 128, "f32", y_ref=y_ref)
 
 
+@pytest.mark.parametrize("n", [128, 4096, 12288, 24576, 16384])
+def test_fp16_rows_near_and_below_the_normal_floor(R, n):
+    """fp16 rows whose values sit around the fp16 normal floor (6.1e-5) and in its subnormal range:
+    an fp16 input value is an exact operand of the f16 matrix-core instruction, so the rotation
+    must meet R1 on rows made mostly or only of fp16 subnormals, and INT4 g128 / MXFP4 on them."""
+    import torch
+    s = splitmix64_signs(5, n)
+    for scale in (1e-3, 6e-5, 1e-6):
+        say(f"fp16 n={n} rows of magnitude {scale:g}")
+        g = torch.Generator().manual_seed(n + 1)
+        x = (torch.randn(5, n, generator=g, dtype=torch.float64) * scale).to(torch.float16)
+        if scale == 1e-6:
+            assert float(x.abs().max()) < 6.1e-5          # every value an fp16 subnormal
+        y_ref = O.rotate(x, s)
+        C.check_rotation(to_np(R.rhtq_rotate(x.to(dev()), s)), y_ref)
+        check_forward(R, x.to(dev()), s, "int4", 128, "f32", y_ref=y_ref)
+        check_forward(R, x.to(dev()), s, "mxfp4", 32, "e8m0", y_ref=y_ref)
+
+
+@pytest.mark.parametrize("n,tokens", [(4096, 3000), (4096, 64), (1024, 5000), (128, 40000), (8192, 1100),
+                                      (16384, 600), (12288, 1100), (24576, 300), (11008, 700), (22016, 300),
+                                      (2752, 3000), (3072, 2500)])
+def test_fp16_input_many_rows(R, n, tokens):
+    """fp16 input on every kernel family (the paired and one-wave 4096 kernels, the two-stage,
+    wide, 12288, 24576, 172 x 2^k and single-stage kernels): more rows than the persistent grids,
+    INT4 per-token and g128, dynamic NVFP4 (tensor scale over all rows) and MXFP4 on sampled rows,
+    and the rotation of the same rows."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(WORKLOADS["llama_4096_int4"], n=n, tokens=tokens)
+    xb, s = x_to(w)
+    # a quarter of the recipe: its sink-row outlier columns reach ~5e4, near fp16's largest value
+    x = (xb.to(torch.float32) * 0.25).to(torch.float16)
+    assert bool(torch.isfinite(x).all())
+    rows = np.unique(np.array([0, 1, tokens // 3, tokens // 2, tokens - 2, tokens - 1]))
+    amax = None
+    g2 = 128 if n % 128 == 0 else 64
+    for fmt, grp, sd in [("int4", 0, "f32"), ("int4", g2, "f16"), ("nvfp4", 16, "e4m3"), ("mxfp4", 32, "e8m0")]:
+        say(f"fp16 n={n} rows={tokens} {fmt} g{grp}")
+        g_ref = None
+        if fmt == "nvfp4":
+            if amax is None:
+                step = max(1, (1 << 22) // n)
+                amax = max(float(np.max(np.abs(O.rotate(x[r0:r0 + step].cpu(), s)))) for r0 in range(0, tokens, step))
+            g_ref = np.float32(amax / 2688.0)
+        check_forward(R, x, s, fmt, grp, sd, rows=rows, g_ref=g_ref)
+    y = to_np(R.rhtq_rotate(x, s))
+    C.check_rotation(y[rows], O.rotate(x[rows].cpu(), s))
+
+
 def test_zero_tokens_is_noop(R):
     import torch
     say("tokens = 0")
@@ -718,7 +768,7 @@ def test_blocked_rotation_and_quantisation(R, n, block):
     g = torch.Generator().manual_seed(n + block)
     xc = torch.randn(21, n, generator=g) * torch.exp(torch.randn(n, generator=g))
     s = splitmix64_signs(8, n)
-    for dt in (torch.bfloat16, torch.float32):
+    for dt in (torch.bfloat16, torch.float16, torch.float32):
         x = xc.to(dt).to(dev())
         y_ref = O.rotate_blocked(x.cpu(), s, block)
         say(f"blocked rotate n={n} b={block} dtype={dt}")

@@ -1,6 +1,7 @@
 """GPU: a seeded sweep over the call space.  Each case draws a supported width (powers of two
 16 .. 16384, 12 x 2^k, 172 x 2^k), an input type, a format with a valid group and scale type, a
-row count, signs or none, and sometimes a block-diagonal block; the device's rotation and
+row count, signs or none, and sometimes a block-diagonal block (a further set of cases takes fp16
+input); the device's rotation and
 quantisation of every row are checked against the oracle by the same rules as the other parity
 tests.  The draws are fixed by the seed, so a failure names a reproducible case."""
 import numpy as np
@@ -17,11 +18,14 @@ TWELVE = [12 * (1 << k) for k in range(8, 12)]
 W172 = [172 * (1 << k) for k in range(4, 8)]
 WIDTHS = POW2 + TWELVE + W172
 N_CASES = 160
+N_F16_CASES = 48
 
 
-def draw_case(rng):
+def draw_case(rng, f16=False):
     n = int(rng.choice(WIDTHS))
     dtype = "fp32" if rng.random() < 0.35 else "bf16"
+    if f16:
+        dtype = "fp16"
     # block-diagonal on a quarter of the power-of-two-divisible widths
     block = None
     pow2_part = n & -n
@@ -47,7 +51,8 @@ def draw_case(rng):
                 tokens=tokens, signed=signed, seed=seed)
 
 
-CASES = [draw_case(np.random.default_rng(1000 + i)) for i in range(N_CASES)]
+CASES = [draw_case(np.random.default_rng(1000 + i)) for i in range(N_CASES)] + \
+        [draw_case(np.random.default_rng(5000 + i), f16=True) for i in range(N_F16_CASES)]
 
 
 @pytest.fixture(scope="module")
@@ -66,7 +71,7 @@ def test_sweep_case(R, case):
     print(f"[case] {c}", flush=True)
     g = torch.Generator().manual_seed(c["seed"])
     xc = torch.randn(c["tokens"], c["n"], generator=g) * torch.exp(torch.randn(c["n"], generator=g))
-    x = xc.to(torch.float32 if c["dtype"] == "fp32" else torch.bfloat16)
+    x = xc.to({"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[c["dtype"]])
     s = splitmix64_signs(c["seed"] & 0xFFFF, c["n"]) if c["signed"] else None
     blk = c["block"]
     y_ref = O.rotate(x, s) if not blk else O.rotate_blocked(x, s, blk)

@@ -52,7 +52,7 @@ class Workload:
     name: str
     tokens: int            # rows handed to the library
     n: int                 # row width
-    in_dtype: str          # "f32" or "bf16"
+    in_dtype: str          # "f32", "bf16" or "f16"
     recipe: str            # "gauss_outlier_cols", "llama_like", "kv_spikes"
     seed: int              # value seed
     sign_seed: int         # splitmix64 seed of the sign vector
@@ -76,6 +76,11 @@ WORKLOADS = {
         "llama_4096_int4", 2048, 4096, "bf16", "llama_like", 2, 0, "int4", 0, "f32",
         description="2048 x 4096 bf16, log-normal channel scales, 8 outlier channels x50, "
                     "0.5% sink rows x40; per-token INT4, fp32 scale"),
+    # the headline shape with fp16 input (QuaRot's baselines are FP16 models: reviews page, review 4
+    # Weaknesses); the recipe is scaled by 1/4 so its largest values (~5e4) stay inside fp16's range
+    "llama_4096_int4_f16": Workload(
+        "llama_4096_int4_f16", 2048, 4096, "f16", "llama_like", 2, 0, "int4", 0, "f32",
+        description="2048 x 4096 fp16, the llama-like recipe x 1/4; per-token INT4, fp32 scale"),
     "downproj_12288_int4g128": Workload(
         "downproj_12288_int4g128", 8192, 12288, "bf16", "llama_like", 3, 0, "int4", 128, "f16",
         description="8192 x 12288 bf16 (H12 x H1024), same value recipe; INT4 group 128, fp16 scales"),
@@ -120,7 +125,8 @@ def generate(w: Workload, device="cpu"):
 
     x is a torch tensor [tokens, n] in w.in_dtype on `device`, drawn with
     torch.Generator(device).manual_seed(w.seed); values are produced in fp32
-    and cast to bf16 with round-to-nearest-even when the dtype is bf16.
+    and cast to bf16 with round-to-nearest-even when the dtype is bf16, or scaled
+    by 1/4 (exact) and cast to fp16 the same way when it is f16.
     signs is an int8 numpy vector of length n.
     """
     torch = _torch()
@@ -145,7 +151,12 @@ def generate(w: Workload, device="cpu"):
         z = torch.where(spikes, z * 10.0, z)
     else:
         raise ValueError(f"unknown recipe {w.recipe}")
-    x = z if w.in_dtype == "f32" else z.to(torch.bfloat16)
+    if w.in_dtype == "f32":
+        x = z
+    elif w.in_dtype == "f16":
+        x = (z * 0.25).to(torch.float16)
+    else:
+        x = z.to(torch.bfloat16)
     return x.contiguous(), splitmix64_signs(w.sign_seed, n)
 
 
