@@ -6,8 +6,8 @@ inherits the parent's GPU context).  Each chunk returns counts; the parent sums 
 applies R3's fraction limit to the whole tensor, so "at most 1e-4 of codes" is evaluated
 over the entire configuration rather than per chunk.
 
-Workers receive the bf16 input as its 16-bit patterns and the device's outputs as numpy
-arrays; none of them touches a GPU.
+Workers receive the bf16 or fp16 input as its 16-bit patterns and the device's outputs as
+numpy arrays; none of them touches a GPU.
 """
 from __future__ import annotations
 
@@ -26,7 +26,10 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 def check_chunk(job: dict) -> dict:
     """One row chunk: the oracle's rotation of x, then every rule against the device's
     rotation (R1), scales and codes (R2-R4).  Returns counts for the parent to sum."""
-    x = bf16_bits_to_f64(job["bits"])
+    if job.get("in_dtype") == "f16":
+        x = np.asarray(job["bits"]).astype(np.int16).view(np.float16).astype(np.float64)   # exact
+    else:
+        x = bf16_bits_to_f64(job["bits"])
     s, block = job["signs"], job["block"]
     y_ref = O.rotate(x, s) if not block else O.rotate_blocked(x, s, block)
     rep = {"rows": int(x.shape[0]), "codes": int(x.size), "amax": float(np.max(np.abs(y_ref)))}

@@ -30,6 +30,7 @@ CASES = {
     "blockh128_4096_int4g128": 1024,
     "downproj7b_11008_int4g128": 512,
     "wide172_22016_int4g128": 256,
+    "llama_4096_int4_f16": 512,
 }
 
 
@@ -97,7 +98,8 @@ def test_workload_every_row(R, pool, name):
     jobs = []
     for r0 in range(0, w.tokens, step):
         r1 = min(w.tokens, r0 + step)
-        jobs.append({"bits": bits[r0:r1], "signs": s, "block": w.block, "fmt": w.fmt, "group": w.group,
+        jobs.append({"bits": bits[r0:r1], "in_dtype": w.in_dtype, "signs": s, "block": w.block, "fmt": w.fmt,
+                     "group": w.group,
                      "scale_dtype": w.scale_dtype, "y": y_h[r0:r1],
                      "outs": {k: (p[r0:r1], sc[r0:r1], gg) for k, (p, sc, gg) in outs.items()}})
     say(f"{name}: {len(jobs)} chunks of {step} rows")
