@@ -54,7 +54,8 @@ KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_api.cpp",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_floor.hip",
                   "include/rhtq.h",
-                  "include/rhtq_floor.h"]
+                  "include/rhtq_floor.h",
+                  "randomized_hadamard_rotation_amd/build.py"]   # compiler flags shape the kernels too
 
 
 def kernel_source_hash() -> str:

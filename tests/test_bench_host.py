@@ -55,6 +55,7 @@ def test_kernel_hash_covers_every_source():
     csrc = os.path.join(ROOT, "randomized_hadamard_rotation_amd", "csrc")
     built = {os.path.join("randomized_hadamard_rotation_amd", "csrc", f) for f in os.listdir(csrc)}
     built.add(os.path.join("include", "rhtq.h"))
+    built.add(os.path.join("randomized_hadamard_rotation_amd", "build.py"))   # the flags
     assert built <= set(bench.KERNEL_SOURCES)
 
 
