@@ -201,7 +201,8 @@ def _same_device(dev, **ts):
 
 
 def rhtq_rotate(x, signs=None, out=None, stream=None, block=None):
-    """y = H_n diag(signs) x / sqrt(n) per row, fp32 [tokens][n].  With block = b < n the
+    """y = H_n diag(signs) x / sqrt(n) per row, fp32 [tokens][n]; x is a bfloat16, float16 or
+    float32 device tensor [tokens][n].  With block = b < n the
     rotation is block-diagonal: (I (x) H_b) diag(signs) x / sqrt(b).  An `out` passed in must
     be contiguous fp32 [tokens][n] on x's device."""
     torch = _torch()
@@ -238,7 +239,8 @@ def scale_shape(tokens: int, n: int, fmt: str, group: int):
 def rhtq_forward(x, signs=None, fmt: str = "int4", group: int = 0, scale_dtype: str | None = None,
                  tensor_scale=None, tensor_scale_mode: str = "dynamic", packed=None, scales=None,
                  stream=None, block=None):
-    """Rotate, quantise, pack.  Returns (packed uint8 [tokens][n/2], scales, tensor_scale).
+    """Rotate, quantise, pack x (bfloat16, float16 or float32 [tokens][n] on the device).
+    Returns (packed uint8 [tokens][n/2], scales, tensor_scale).
 
     INT4: scales fp32/fp16 [tokens][n/group] (group 0 = one per row).
     NVFP4: scales uint8 E4M3 [tokens][n/16]; tensor_scale a device float32 [1]
