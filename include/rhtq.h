@@ -52,8 +52,9 @@
  *    enqueued and the status says why.  tokens == 0 is a valid no-op.
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.  Denormal bf16 or
  *    fp32 input values (below 1.2e-38 in magnitude) may be read as zero by the matrix-core
- *    kernels, so a row made only of them does not get fp32 accuracy.  fp16 input is read
- *    exactly, its subnormals (below 6.1e-5) included.
+ *    kernels, so a row made only of them does not get fp32 accuracy; for fp32 input at the
+ *    172 x 2^k widths the same holds for rows whose values all lie below about 1e-33 (2^-110).
+ *    fp16 input is read exactly, its subnormals (below 6.1e-5) included.
  *  - Alignment: x, y_out, packed_out, x_out and signs must be 16-byte aligned;
  *    scale buffers aligned to their element size.
  *  - Supported widths: n = 2^k with 16 <= n <= 16384, n = 12 * 2^k with

@@ -51,6 +51,21 @@ __device__ __forceinline__ void split3_bf16(const uint4& r0, const uint4& r1, ui
   }
 }
 
+// Term t (0, 1, 2) of the exact split of an fp32 value (bit pattern v) into three bf16 values
+// v = hi + mid + lo, each returned as an fp32 bit pattern whose low 16 bits are zero: hi keeps the
+// top 16 bits of v, mid the top 16 bits of v - hi, and lo = v - hi - mid has at most 8
+// significant bits.  Unlike split3_bf16 the terms are not rescaled, so they can share one
+// accumulator: below about 2^-110 the lower terms are bf16 denormals, which the matrix cores
+// read as zero.
+__device__ __forceinline__ uint32_t f32_term(uint32_t v, int t) {
+  const uint32_t hi = v & 0xFFFF0000u;
+  if (t == 0) return hi;
+  const float r = __uint_as_float(v) - __uint_as_float(hi);
+  const uint32_t mid = __float_as_uint(r) & 0xFFFF0000u;
+  if (t == 1) return mid;
+  return __float_as_uint(r - __uint_as_float(mid));
+}
+
 // Stage-1 products of fp32 input: the three terms through the same +-1 operand, each into its
 // own accumulator (the scaled terms must not meet the hi products unscaled), then
 // d = dh + 2^-8 dm + 2^-16 dl.

@@ -139,8 +139,11 @@ __device__ __forceinline__ float nnmax(float a, float b) { return __uint_as_floa
 // GC: group class, 0 (one INT4 group per row: the row maximum across the four waves through
 // LDS), 4 (16-element groups: one run), 5 (32: two runs), 6 (64..256: whole
 // a'-rows); SD: INT4 scale storage (RHTQ_SCALE_F32 / F16).  H16: fp16 input (stage 1 on the f16
-// matrix-core instruction against f16 operands; everything else is the same).
-template <int P, int OP, int GC, int SD, int NT, bool H16>
+// matrix-core instruction against f16 operands; everything else is the same).  F32: fp32 input,
+// taken through the LDS tile in three passes (f32_term: the exact bf16 terms hi, mid, lo of each
+// value) that stage 1 accumulates into the same products; the next row's loads are issued
+// before the last pass instead of a row ahead (P = 1), or each pass loads its data (P > 1).
+template <int P, int OP, int GC, int SD, int NT, bool H16, bool F32>
 __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
   static_assert(P == 1 || P == 2 || P == 4, "one, two or four rows per work row");
   constexpr int kPn = kN / P;     // elements per row
@@ -154,6 +157,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)kPn));
   const int64_t vrows = (a.rows + P - 1) / P;   // work rows
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const float* xf = static_cast<const float*>(a.x);
 
   bf16x8 hb[NT][6];
 #pragma unroll
@@ -170,14 +174,25 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   const int LG = GC == 6 ? __builtin_ctz((unsigned)a.group) : GC;   // log2 of the group
   float run_max = 0.0f;
 
-  uint4 raw[kLoads];
+  uint4 raw[F32 ? 1 : kLoads];
+  uint4 raw32[F32 ? kLoads : 1][2];   // fp32 input: the chunk's 8 values as two 16-byte loads
   auto load = [&](int64_t row) {
     if (row >= vrows) return;
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = tid + kT * k;
       if (c < kChunks) {
-        if constexpr (P == 1) {
+        if constexpr (F32) {
+          // as below, with two 16-byte loads of fp32 values per chunk
+          const int b0 = 8 * (c & 7);
+          const int64_t prow = P == 1 ? row : row * P + b0 / kM;
+          const int64_t off = P == 1 ? row * kN + 8 * c : prow * kPn + kM * (c >> 3) + b0 % kM;
+          raw32[k][0] = raw32[k][1] = make_uint4(0, 0, 0, 0);
+          if (P == 1 || prow < a.rows) {
+            raw32[k][0] = ld_stream(xf + off);
+            raw32[k][1] = ld_stream(xf + off + 4);
+          }
+        } else if constexpr (P == 1) {
           raw[k] = ld_stream(x + row * kN + 8 * c);
         } else {
           // chunk c: a = c >> 3, b = 8 (c & 7) .. + 7 of the work row, i.e. row P row + b / kM
@@ -198,30 +213,34 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   const uint8_t* rbase_l[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) rbase_l[mt] = xs + xrow(16 * mt + n) + 16 * g;
-  // x of the row in raw[] -> LDS, signs applied
-  auto write_lds = [&]() {
+  // x of the row in raw[] -> LDS, signs applied; fp32 input: bf16 term `term` of each value
+  auto write_lds = [&](int term) {
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = tid + kT * k;
       if (c < kChunks) {
         const uint4 m = sgn[c];
-        const uint32_t w[4] = {raw[k].x ^ m.x, raw[k].y ^ m.y, raw[k].z ^ m.z, raw[k].w ^ m.w};
+        if constexpr (F32) {
+          const uint32_t mk[4] = {m.x, m.y, m.z, m.w};
+          const uint4 r0 = raw32[k][0], r1 = raw32[k][1];
+          const uint32_t v[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(wbase + e * kPitch + (kT / 4) * k) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          for (int e = 0; e < 8; ++e) {
+            // the sign flips the whole fp32 value (bit 15 / bit 31 of the bf16-pair mask)
+            const uint32_t sb = (e & 1) ? (mk[e >> 1] & 0x80000000u) : (mk[e >> 1] << 16);
+            *reinterpret_cast<uint16_t*>(wbase + e * kPitch + (kT / 4) * k) = (uint16_t)(f32_term(v[e] ^ sb, term) >> 16);
+          }
+        } else {
+          const uint32_t w[4] = {raw[k].x ^ m.x, raw[k].y ^ m.y, raw[k].z ^ m.z, raw[k].w ^ m.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<uint16_t*>(wbase + e * kPitch + (kT / 4) * k) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
       }
     }
   };
-  __syncthreads();   // sign masks and zeroed rows
-  if (row < vrows) write_lds();
-  load(row + gridDim.x);
-  __syncthreads();
-  // per row: stage 1 reads the row from LDS; after the barrier that ends those reads the next
-  // row goes into LDS (its loads were issued one row earlier) and the loads of the row after
-  // it are issued, then stage 2 and the epilogue of this row run from registers
-  for (; row < vrows; row += gridDim.x) {
-    // ---------------- stage 1: H172 over a ----------------
-    f32x4 acc[NT][4];
+  // stage 1 (H172 over a) of the tile in LDS, into acc (first: start from zero)
+  auto stage1 = [&](f32x4 (&acc)[NT][4], bool first) {
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) {
       bf16x8 av[4];
@@ -232,12 +251,53 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-          acc[j][mt] = stage1_mma<H16>(av[mt], hb[j][ks], ks == 0 ? z : acc[j][mt]);
+          acc[j][mt] = stage1_mma<H16>(av[mt], hb[j][ks], (first && ks == 0) ? z : acc[j][mt]);
         }
     }
+  };
+  __syncthreads();   // sign masks and zeroed rows
+  if (row < vrows) write_lds(0);
+  if constexpr (!F32) load(row + gridDim.x);
+  __syncthreads();
+  // per row: stage 1 reads the row from LDS; after the barrier that ends those reads the next
+  // row goes into LDS (its loads were issued one row earlier) and the loads of the row after
+  // it are issued, then stage 2 and the epilogue of this row run from registers.  fp32 input:
+  // three passes (hi, mid, lo) through the tile, the next row's loads issued before the third
+  for (; row < vrows; row += gridDim.x) {
+    // ---------------- stage 1: H172 over a ----------------
+    f32x4 acc[NT][4];
+    stage1(acc, true);
     __syncthreads();   // every wave has read this row
-    if (row + gridDim.x < vrows) write_lds();
-    load(row + 2 * (int64_t)gridDim.x);
+    if constexpr (F32 && P == 1) {
+      write_lds(1);
+      __syncthreads();
+      stage1(acc, false);
+      __syncthreads();
+      write_lds(2);
+      load(row + gridDim.x);
+      __syncthreads();
+      stage1(acc, false);
+      __syncthreads();
+      if (row + gridDim.x < vrows) write_lds(0);
+    } else if constexpr (F32) {
+      // two and four rows per work row leave no registers to hold the fp32 data across a
+      // pass: it is loaded again right before each term is written
+#pragma unroll 1
+      for (int term = 1; term < 3; ++term) {
+        load(row);
+        write_lds(term);
+        __syncthreads();
+        stage1(acc, false);
+        __syncthreads();
+      }
+      if (row + gridDim.x < vrows) {
+        load(row + gridDim.x);
+        write_lds(0);
+      }
+    } else {
+      if (row + gridDim.x < vrows) write_lds(0);
+      load(row + 2 * (int64_t)gridDim.x);
+    }
 
     // ---------------- stage 2: H2 by butterfly (P = 1), H32 on the matrix cores ----------------
     // (each step runs over all of this wave's tiles before the next, so that the tiles'
@@ -530,7 +590,7 @@ __device__ __forceinline__ void rows172(const KernelArgs& a, uint8_t* xs, const 
   }
 }
 
-template <int P, int OP, int GC, int SD, bool H16 = false>
+template <int P, int OP, int GC, int SD, bool H16 = false, bool F32 = false>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 : 4))) void fast172_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
   __shared__ uint4 sgn[kChunks];
@@ -553,10 +613,10 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 
   for (int c = tid; c < kXBytes / 16; c += kT) reinterpret_cast<uint4*>(xs)[c] = make_uint4(0, 0, 0, 0);   // a >= 172 stays 0
   // waves with a tile fewer than the busiest (kTiles not a multiple of kW) take the smaller copy
   if constexpr (kTiles % kW == 0) {
-    rows172<P, OP, GC, SD, kNT, H16>(a, xs, sgn, wmax);
+    rows172<P, OP, GC, SD, kNT, H16, F32>(a, xs, sgn, wmax);
   } else {
-    if ((tid >> 6) < kTiles % kW) rows172<P, OP, GC, SD, kNT, H16>(a, xs, sgn, wmax);
-    else rows172<P, OP, GC, SD, kNT - 1, H16>(a, xs, sgn, wmax);
+    if ((tid >> 6) < kTiles % kW) rows172<P, OP, GC, SD, kNT, H16, F32>(a, xs, sgn, wmax);
+    else rows172<P, OP, GC, SD, kNT - 1, H16, F32>(a, xs, sgn, wmax);
   }
 }
 
@@ -572,13 +632,17 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 
 constexpr int kN2 = 2 * kN;          // 22016
 constexpr int kChunks2 = 2 * kChunks;
 
-template <int OP, int GC, int SD, int NT, bool H16>
+// F32: fp32 input; each half goes through the LDS tile in three passes (the bf16 terms of
+// f32_term, accumulated into the same products), and each pass loads its half again right
+// before writing it, so no fp32 data is held across a pass.
+template <int OP, int GC, int SD, int NT, bool H16, bool F32>
 __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const uint4* sgn, float* wmax) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)kN2));
   const int64_t rows = a.rows;
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const float* xf = static_cast<const float*>(a.x);
 
   const f16x8 ha[2] = {h32_b_operand<false>(lane, 0), h32_b_operand<false>(lane, 1)};
 
@@ -592,35 +656,55 @@ __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const 
 
   // half h of a row: chunk c < kChunks holds a = c >> 3 and d = 8 (c & 7) .. + 7, the elements
   // 128 a + 64 h + d
-  uint4 raw[kLoads];
+  uint4 raw[F32 ? 1 : kLoads];
+  uint4 raw32[F32 ? kLoads : 1][2];
   auto load = [&](int64_t row, int h) {
     if (row >= rows) return;
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = tid + kT * k;
-      if (c < kChunks) raw[k] = ld_stream(x + row * kN2 + 128 * (c >> 3) + 64 * h + 8 * (c & 7));
+      if constexpr (F32) {
+        if (c < kChunks) {
+          const float* p = xf + row * kN2 + 128 * (c >> 3) + 64 * h + 8 * (c & 7);
+          raw32[k][0] = ld_stream(p);
+          raw32[k][1] = ld_stream(p + 4);
+        }
+      } else {
+        if (c < kChunks) raw[k] = ld_stream(x + row * kN2 + 128 * (c >> 3) + 64 * h + 8 * (c & 7));
+      }
     }
   };
   uint8_t* wbase = xs + xrow(8 * (tid & 7)) + 2 * (tid >> 3);
   const uint8_t* rbase_l[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) rbase_l[mt] = xs + xrow(16 * mt + n) + 16 * g;
-  auto write_lds = [&](int h) {
+  auto write_lds = [&](int h, int term) {
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = tid + kT * k;
       if (c < kChunks) {
         const uint4 m = sgn[kChunks * h + c];
-        const uint32_t w[4] = {raw[k].x ^ m.x, raw[k].y ^ m.y, raw[k].z ^ m.z, raw[k].w ^ m.w};
+        if constexpr (F32) {
+          const uint32_t mk[4] = {m.x, m.y, m.z, m.w};
+          const uint4 r0 = raw32[k][0], r1 = raw32[k][1];
+          const uint32_t v[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(wbase + e * kPitch + (kT / 4) * k) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t sb = (e & 1) ? (mk[e >> 1] & 0x80000000u) : (mk[e >> 1] << 16);
+            *reinterpret_cast<uint16_t*>(wbase + e * kPitch + (kT / 4) * k) = (uint16_t)(f32_term(v[e] ^ sb, term) >> 16);
+          }
+        } else {
+          const uint32_t w[4] = {raw[k].x ^ m.x, raw[k].y ^ m.y, raw[k].z ^ m.z, raw[k].w ^ m.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<uint16_t*>(wbase + e * kPitch + (kT / 4) * k) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
       }
     }
   };
   // stage 1 (H172 over a) of the half in LDS; the H172^T operands are loaded (L2 hits) for each
   // pass rather than held, which leaves the registers to the two halves' results
-  auto stage1 = [&](f32x4 (&acc)[NT][4]) {
+  auto stage1 = [&](f32x4 (&acc)[NT][4], bool first) {
     // an opaque zero keeps the compiler from hoisting these loads out of the row loop
     int t0 = wave;
     asm volatile("" : "+v"(t0));
@@ -639,16 +723,34 @@ __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const 
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-          acc[j][mt] = stage1_mma<H16>(av[mt], hb[j][ks], ks == 0 ? z : acc[j][mt]);
+          acc[j][mt] = stage1_mma<H16>(av[mt], hb[j][ks], (first && ks == 0) ? z : acc[j][mt]);
         }
+    }
+  };
+  // fp32 input: half h of the row through the tile, term by term, into acc (the tile is free)
+  auto half_f32 = [&](int64_t row, int h, f32x4 (&acc)[NT][4]) {
+    load(row, h);
+    write_lds(h, 0);
+    __syncthreads();
+    stage1(acc, true);
+    __syncthreads();   // every wave has read the tile
+#pragma unroll 1
+    for (int term = 1; term < 3; ++term) {
+      load(row, h);
+      write_lds(h, term);
+      __syncthreads();
+      stage1(acc, false);
+      __syncthreads();
     }
   };
 
   int64_t row = blockIdx.x;
-  load(row, 0);
-  __syncthreads();   // sign masks and zeroed rows
-  if (row < rows) write_lds(0);
-  load(row, 1);
+  if constexpr (!F32) {
+    load(row, 0);
+    __syncthreads();   // sign masks and zeroed rows
+    if (row < rows) write_lds(0, 0);
+    load(row, 1);
+  }
   __syncthreads();
   // per row: stage 1 of half 0 (in LDS); half 1 (in raw[]) goes in after the barrier that ends
   // those reads, and the next row's half 0 is loaded; stage 1 of half 1; the next row's half 0
@@ -656,15 +758,20 @@ __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const 
   // registers
   for (; row < rows; row += gridDim.x) {
     f32x4 acc[2][NT][4];
-    stage1(acc[0]);
-    __syncthreads();   // every wave has read half 0
-    write_lds(1);
-    load(row + gridDim.x, 0);
-    __syncthreads();
-    stage1(acc[1]);
-    __syncthreads();   // every wave has read half 1
-    if (row + gridDim.x < rows) write_lds(0);
-    load(row + gridDim.x, 1);
+    if constexpr (F32) {
+      half_f32(row, 0, acc[0]);
+      half_f32(row, 1, acc[1]);
+    } else {
+      stage1(acc[0], true);
+      __syncthreads();   // every wave has read half 0
+      write_lds(1, 0);
+      load(row + gridDim.x, 0);
+      __syncthreads();
+      stage1(acc[1], true);
+      __syncthreads();   // every wave has read half 1
+      if (row + gridDim.x < rows) write_lds(0, 0);
+      load(row + gridDim.x, 1);
+    }
 
     // H2 over c: half 0 <- half 0 + half 1, half 1 <- half 0 - half 1
 #pragma unroll
@@ -931,7 +1038,7 @@ __device__ __forceinline__ void rows344(const KernelArgs& a, uint8_t* xs, const 
   }
 }
 
-template <int OP, int GC, int SD, bool H16 = false>
+template <int OP, int GC, int SD, bool H16 = false, bool F32 = false>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 : 4))) void fast344_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
   __shared__ uint4 sgn[kChunks2];
@@ -952,50 +1059,50 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kW == 4 ? 2 
   }
   for (int c = tid; c < kXBytes / 16; c += kT) reinterpret_cast<uint4*>(xs)[c] = make_uint4(0, 0, 0, 0);   // a >= 172 stays 0
   if constexpr (kTiles % kW == 0) {
-    rows344<OP, GC, SD, kNT, H16>(a, xs, sgn, wmax);
+    rows344<OP, GC, SD, kNT, H16, F32>(a, xs, sgn, wmax);
   } else {
-    if ((tid >> 6) < kTiles % kW) rows344<OP, GC, SD, kNT, H16>(a, xs, sgn, wmax);
-    else rows344<OP, GC, SD, kNT - 1, H16>(a, xs, sgn, wmax);
+    if ((tid >> 6) < kTiles % kW) rows344<OP, GC, SD, kNT, H16, F32>(a, xs, sgn, wmax);
+    else rows344<OP, GC, SD, kNT - 1, H16, F32>(a, xs, sgn, wmax);
   }
 }
 
-template <int OP, int GC, int SD, bool H16>
+template <int OP, int GC, int SD, int IN>
 hipError_t launch344(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast344_kernel<OP, GC, SD, H16>;
+  auto kern = fast344_kernel<OP, GC, SD, IN == RHTQ_IN_F16, IN == RHTQ_IN_F32>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int SD, bool H16>
+template <int SD, int IN>
 hipError_t launch344_int4(const KernelArgs& a, hipStream_t s) {
-  if (a.group == kN2) return launch344<OP_INT4, 0, SD, H16>(a, s);   // one group per row
+  if (a.group == kN2) return launch344<OP_INT4, 0, SD, IN>(a, s);   // one group per row
   switch (a.group) {
-    case 16: return launch344<OP_INT4, 4, SD, H16>(a, s);
-    case 32: return launch344<OP_INT4, 5, SD, H16>(a, s);
-    case 64: case 128: case 256: case 512: return launch344<OP_INT4, 6, SD, H16>(a, s);
+    case 16: return launch344<OP_INT4, 4, SD, IN>(a, s);
+    case 32: return launch344<OP_INT4, 5, SD, IN>(a, s);
+    case 64: case 128: case 256: case 512: return launch344<OP_INT4, 6, SD, IN>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
-template <bool H16>
+template <int IN>
 hipError_t launch344_op(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return launch344<OP_ROTATE, 6, 0, H16>(a, s);
+    case OP_ROTATE: return launch344<OP_ROTATE, 6, 0, IN>(a, s);
     case OP_INT4:
-      return a.scale_dtype == RHTQ_SCALE_F32 ? launch344_int4<RHTQ_SCALE_F32, H16>(a, s)
-                                             : launch344_int4<RHTQ_SCALE_F16, H16>(a, s);
-    case OP_NVFP4: return launch344<OP_NVFP4, 4, 0, H16>(a, s);
-    case OP_MXFP4: return launch344<OP_MXFP4, 5, 0, H16>(a, s);
-    case OP_AMAX: return launch344<OP_AMAX, 6, 0, H16>(a, s);
+      return a.scale_dtype == RHTQ_SCALE_F32 ? launch344_int4<RHTQ_SCALE_F32, IN>(a, s)
+                                             : launch344_int4<RHTQ_SCALE_F16, IN>(a, s);
+    case OP_NVFP4: return launch344<OP_NVFP4, 4, 0, IN>(a, s);
+    case OP_MXFP4: return launch344<OP_MXFP4, 5, 0, IN>(a, s);
+    case OP_AMAX: return launch344<OP_AMAX, 6, 0, IN>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
-template <int P, int OP, int GC, int SD, bool H16>
+template <int P, int OP, int GC, int SD, int IN>
 hipError_t launch172(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast172_kernel<P, OP, GC, SD, H16>;
+  auto kern = fast172_kernel<P, OP, GC, SD, IN == RHTQ_IN_F16, IN == RHTQ_IN_F32>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int64_t vrows = (a.rows + P - 1) / P;
   const int grid = (int)(vrows < max_blocks ? vrows : max_blocks);
@@ -1003,29 +1110,29 @@ hipError_t launch172(const KernelArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int P, int SD, bool H16>
+template <int P, int SD, int IN>
 hipError_t launch172_int4(const KernelArgs& a, hipStream_t s) {
-  if (a.group == kN / P) return launch172<P, OP_INT4, 0, SD, H16>(a, s);   // one group per row
+  if (a.group == kN / P) return launch172<P, OP_INT4, 0, SD, IN>(a, s);   // one group per row
   switch (a.group) {
-    case 16: return launch172<P, OP_INT4, 4, SD, H16>(a, s);
-    case 32: return launch172<P, OP_INT4, 5, SD, H16>(a, s);
-    case 64: return launch172<P, OP_INT4, 6, SD, H16>(a, s);
-    case 128: return P <= 2 ? launch172<P, OP_INT4, 6, SD, H16>(a, s) : hipErrorNotSupported;
-    case 256: return P == 1 ? launch172<P, OP_INT4, 6, SD, H16>(a, s) : hipErrorNotSupported;
+    case 16: return launch172<P, OP_INT4, 4, SD, IN>(a, s);
+    case 32: return launch172<P, OP_INT4, 5, SD, IN>(a, s);
+    case 64: return launch172<P, OP_INT4, 6, SD, IN>(a, s);
+    case 128: return P <= 2 ? launch172<P, OP_INT4, 6, SD, IN>(a, s) : hipErrorNotSupported;
+    case 256: return P == 1 ? launch172<P, OP_INT4, 6, SD, IN>(a, s) : hipErrorNotSupported;
     default: return hipErrorNotSupported;
   }
 }
 
-template <int P, bool H16>
+template <int P, int IN>
 hipError_t launch172_p(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return launch172<P, OP_ROTATE, 6, 0, H16>(a, s);
+    case OP_ROTATE: return launch172<P, OP_ROTATE, 6, 0, IN>(a, s);
     case OP_INT4:
-      return a.scale_dtype == RHTQ_SCALE_F32 ? launch172_int4<P, RHTQ_SCALE_F32, H16>(a, s)
-                                             : launch172_int4<P, RHTQ_SCALE_F16, H16>(a, s);
-    case OP_NVFP4: return launch172<P, OP_NVFP4, 4, 0, H16>(a, s);
-    case OP_MXFP4: return launch172<P, OP_MXFP4, 5, 0, H16>(a, s);
-    case OP_AMAX: return launch172<P, OP_AMAX, 6, 0, H16>(a, s);
+      return a.scale_dtype == RHTQ_SCALE_F32 ? launch172_int4<P, RHTQ_SCALE_F32, IN>(a, s)
+                                             : launch172_int4<P, RHTQ_SCALE_F16, IN>(a, s);
+    case OP_NVFP4: return launch172<P, OP_NVFP4, 4, 0, IN>(a, s);
+    case OP_MXFP4: return launch172<P, OP_MXFP4, 5, 0, IN>(a, s);
+    case OP_AMAX: return launch172<P, OP_AMAX, 6, 0, IN>(a, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -1033,21 +1140,25 @@ hipError_t launch172_p(int op, const KernelArgs& a, hipStream_t s) {
 }  // namespace
 
 namespace {
-template <bool H16>
+template <int IN>
 hipError_t launch172_any(int op, const KernelArgs& a, hipStream_t s) {
   if (reinterpret_cast<uintptr_t>(a.x) & 15) return hipErrorNotSupported;
-  if (a.n == kN && a.sign_period == kN) return launch172_p<1, H16>(op, a, s);
+  if (a.n == kN && a.sign_period == kN) return launch172_p<1, IN>(op, a, s);
   // 22016 = 172 x 128: the two 64-column halves of each row in turn
-  if (a.n == kN2 && a.sign_period == kN2) return launch344_op<H16>(op, a, s);
+  if (a.n == kN2 && a.sign_period == kN2) return launch344_op<IN>(op, a, s);
   // 5504 = 172 x 32 and 2752 = 172 x 16: two and four rows per work row
-  if (a.n == kN / 2 && a.sign_period == kN / 2) return launch172_p<2, H16>(op, a, s);
-  if (a.n == kN / 4 && a.sign_period == kN / 4) return launch172_p<4, H16>(op, a, s);
+  if (a.n == kN / 2 && a.sign_period == kN / 2) return launch172_p<2, IN>(op, a, s);
+  if (a.n == kN / 4 && a.sign_period == kN / 4) return launch172_p<4, IN>(op, a, s);
   return hipErrorNotSupported;
 }
 }  // namespace
 
 hipError_t launch_fast172(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
-  return f16in ? launch172_any<true>(op, a, s) : launch172_any<false>(op, a, s);
+  return f16in ? launch172_any<RHTQ_IN_F16>(op, a, s) : launch172_any<RHTQ_IN_BF16>(op, a, s);
+}
+
+hipError_t launch_fast172_f32(int op, const KernelArgs& a, hipStream_t s) {
+  return launch172_any<RHTQ_IN_F32>(op, a, s);
 }
 
 }  // namespace rhtq

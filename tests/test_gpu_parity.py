@@ -637,6 +637,34 @@ def test_fp16_input_many_rows(R, n, tokens):
     C.check_rotation(y[rows], O.rotate(x[rows].cpu(), s))
 
 
+@pytest.mark.parametrize("n,tokens", [(11008, 700), (22016, 300), (5504, 1101), (2752, 2101)])
+def test_fp32_input_172_widths_many_rows(R, n, tokens):
+    """fp32 input on the 172 x 2^k kernels (three passes of exact bf16 terms through the LDS
+    tile): more rows than the persistent grid, odd row counts for the two- and four-row work
+    rows, INT4 per-token and g64, dynamic NVFP4 and MXFP4 on sampled rows, and the rotation."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(WORKLOADS["llama_4096_int4"], n=n, tokens=tokens)
+    xb, s = x_to(w)
+    x = xb.to(torch.float32) * (1.0 + 2.0 ** -12)   # values with more than 8 significant bits
+    rows = np.unique(np.array([0, 1, tokens // 3, tokens // 2, tokens - 2, tokens - 1]))
+    amax = None
+    for fmt, grp, sd in [("int4", 0, "f32"), ("int4", 64, "f16"), ("nvfp4", 16, "e4m3"), ("mxfp4", 32, "e8m0")]:
+        say(f"fp32 n={n} rows={tokens} {fmt} g{grp}")
+        g_ref = None
+        if fmt == "nvfp4":
+            if amax is None:
+                step = max(1, (1 << 22) // n)
+                amax = max(float(np.max(np.abs(O.rotate(x[r0:r0 + step].cpu(), s)))) for r0 in range(0, tokens, step))
+            g_ref = np.float32(amax / 2688.0)
+        check_forward(R, x, s, fmt, grp, sd, rows=rows, g_ref=g_ref)
+    y = to_np(R.rhtq_rotate(x, s))
+    C.check_rotation(y[rows], O.rotate(x[rows].cpu(), s))
+    # rows of magnitude 1e-30, above the 2^-110 floor of the unscaled lower terms
+    xt = (torch.randn(3, n, generator=torch.Generator().manual_seed(n), dtype=torch.float64) * 1e-30).to(torch.float32)
+    C.check_rotation(to_np(R.rhtq_rotate(xt.to(dev()), s)), O.rotate(xt, s))
+
+
 def test_zero_tokens_is_noop(R):
     import torch
     say("tokens = 0")
