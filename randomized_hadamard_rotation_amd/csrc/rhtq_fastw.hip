@@ -122,13 +122,15 @@ __device__ __forceinline__ void exchange_round(Slots& v, float& S, float& invS, 
 
 // Rows of the workgroup as seen by wave K (a template parameter, so that every register array
 // is indexed by constants).  All waves of the workgroup take the same rows and barriers.
-// H16: fp16 input (stage 1 on the f16 matrix-core instruction).
-template <int B, int OP, int K, bool H16>
+// H16: fp16 input (stage 1 on the f16 matrix-core instruction).  F32: fp32 input, each value split
+// into three exact bf16 terms for stage 1 (split3_bf16, stage1_f32).
+template <int B, int OP, int K, bool H16, bool F32>
 __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B>& sh) {
   constexpr int W = 1 << B, N = kSub << B;
   const int lane = threadIdx.x & 63;
   const float cnorm = (float)(1.0 / __builtin_sqrt((double)N));
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const float* xf = static_cast<const float*>(a.x);
   const int lcol = 32 * (lane & 15) + 8 * (lane >> 4);   // this lane's 8 elements within a fragment
   const int lc = (lane >> 4) | ((lane & 15) << 2);       // element bits 3-4 = lane >> 4, 5-8 = lane & 15
   const bf16x8 hb[2] = {h32_operand<H16>(lane, 0), h32_operand<H16>(lane, 1)};
@@ -162,22 +164,47 @@ __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B
   float run_max = 0.0f;
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-    uint4 raw[kNF];
+    uint4 raw[F32 ? 1 : kNF];
+    uint4 raw32[F32 ? kNF : 1][2];
 #pragma unroll
-    for (int f = 0; f < kNF; ++f) raw[f] = ld_stream(x + row * N + kSub * K + 512 * f + lcol);
+    for (int f = 0; f < kNF; ++f) {
+      if constexpr (F32) {
+        const float* p = xf + row * N + kSub * K + 512 * f + lcol;
+        raw32[f][0] = ld_stream(p);
+        raw32[f][1] = ld_stream(p + 4);
+      } else {
+        raw[f] = ld_stream(x + row * N + kSub * K + 512 * f + lcol);
+      }
+    }
 
     // ---------------- stage 1: bits 0-4 ----------------
     float d1[kNF][2][4];
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
       const uint4 m = smask[f];
-      uint4 r = raw[f];
-      r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
-      bf16x8 av;
-      __builtin_memcpy(&av, &r, 16);
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 p0 = stage1_mma<H16>(av, hb[0], z);
-      const f32x4 p1 = stage1_mma<H16>(av, hb[1], z);
+      f32x4 p0, p1;
+      if constexpr (F32) {
+        // the signs flip every term: the same bf16-pair masks
+        uint32_t th[4], tm[4], tl[4];
+        split3_bf16(raw32[f][0], raw32[f][1], th, tm, tl);
+        const uint32_t mk[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { th[k] ^= mk[k]; tm[k] ^= mk[k]; tl[k] ^= mk[k]; }
+        bf16x8 ah, am, al;
+        __builtin_memcpy(&ah, th, 16);
+        __builtin_memcpy(&am, tm, 16);
+        __builtin_memcpy(&al, tl, 16);
+        p0 = stage1_f32(ah, am, al, hb[0]);
+        p1 = stage1_f32(ah, am, al, hb[1]);
+      } else {
+        uint4 r = raw[f];
+        r.x ^= m.x; r.y ^= m.y; r.z ^= m.z; r.w ^= m.w;
+        bf16x8 av;
+        __builtin_memcpy(&av, &r, 16);
+        p0 = stage1_mma<H16>(av, hb[0], z);
+        p1 = stage1_mma<H16>(av, hb[1], z);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) { d1[f][0][i] = p0[i]; d1[f][1][i] = p1[i]; }
     }
@@ -285,24 +312,24 @@ __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B
   }
 }
 
-template <int B, int OP, bool H16 = false>
+template <int B, int OP, bool H16 = false, bool F32 = false>
 __global__ __launch_bounds__(64 << B) void fastw_kernel(KernelArgs a) {
   __shared__ WideShared<1 << B> sh;
   const int wave = threadIdx.x >> 6;
   if constexpr (B == 1) {
-    if (wave == 0) wide_rows<B, OP, 0, H16>(a, sh);
-    else wide_rows<B, OP, 1, H16>(a, sh);
+    if (wave == 0) wide_rows<B, OP, 0, H16, F32>(a, sh);
+    else wide_rows<B, OP, 1, H16, F32>(a, sh);
   } else {
     switch (wave) {
-      case 0: wide_rows<B, OP, 0, H16>(a, sh); break;
-      case 1: wide_rows<B, OP, 1, H16>(a, sh); break;
-      case 2: wide_rows<B, OP, 2, H16>(a, sh); break;
-      default: wide_rows<B, OP, 3, H16>(a, sh); break;
+      case 0: wide_rows<B, OP, 0, H16, F32>(a, sh); break;
+      case 1: wide_rows<B, OP, 1, H16, F32>(a, sh); break;
+      case 2: wide_rows<B, OP, 2, H16, F32>(a, sh); break;
+      default: wide_rows<B, OP, 3, H16, F32>(a, sh); break;
     }
   }
 }
 
-template <int B, int OP, bool H16>
+template <int B, int OP, int IN>
 hipError_t launchw(const KernelArgs& a, hipStream_t s) {
   constexpr int N = kSub << B;
   if (a.sign_period != N) return hipErrorNotSupported;   // block-diagonal calls: the other kernels
@@ -310,30 +337,30 @@ hipError_t launchw(const KernelArgs& a, hipStream_t s) {
   if constexpr (OP == OP_INT4) {
     if (!(a.group == N || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-  auto kern = fastw_kernel<B, OP, H16>;
+  auto kern = fastw_kernel<B, OP, IN == RHTQ_IN_F16, IN == RHTQ_IN_F32>;
   static const int max_blocks = resident_blocks((const void*)kern, 64 << B, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 << B), 0, s, a);
   return hipGetLastError();
 }
 
-template <int OP, bool H16>
+template <int OP, int IN>
 hipError_t dispatchw(const KernelArgs& a, hipStream_t s) {
   switch (a.n) {
-    case 8192: return launchw<1, OP, H16>(a, s);
-    case 16384: return launchw<2, OP, H16>(a, s);
+    case 8192: return launchw<1, OP, IN>(a, s);
+    case 16384: return launchw<2, OP, IN>(a, s);
     default: return hipErrorNotSupported;
   }
 }
 
-template <bool H16>
+template <int IN>
 hipError_t dispatchw_op(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return dispatchw<OP_ROTATE, H16>(a, s);
-    case OP_INT4: return dispatchw<OP_INT4, H16>(a, s);
-    case OP_NVFP4: return dispatchw<OP_NVFP4, H16>(a, s);
-    case OP_MXFP4: return dispatchw<OP_MXFP4, H16>(a, s);
-    case OP_AMAX: return dispatchw<OP_AMAX, H16>(a, s);
+    case OP_ROTATE: return dispatchw<OP_ROTATE, IN>(a, s);
+    case OP_INT4: return dispatchw<OP_INT4, IN>(a, s);
+    case OP_NVFP4: return dispatchw<OP_NVFP4, IN>(a, s);
+    case OP_MXFP4: return dispatchw<OP_MXFP4, IN>(a, s);
+    case OP_AMAX: return dispatchw<OP_AMAX, IN>(a, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -341,7 +368,11 @@ hipError_t dispatchw_op(int op, const KernelArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fastw(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
-  return f16in ? dispatchw_op<true>(op, a, s) : dispatchw_op<false>(op, a, s);
+  return f16in ? dispatchw_op<RHTQ_IN_F16>(op, a, s) : dispatchw_op<RHTQ_IN_BF16>(op, a, s);
+}
+
+hipError_t launch_fastw_f32(int op, const KernelArgs& a, hipStream_t s) {
+  return a.n == 16384 ? dispatchw_op<RHTQ_IN_F32>(op, a, s) : hipErrorNotSupported;
 }
 
 }  // namespace rhtq

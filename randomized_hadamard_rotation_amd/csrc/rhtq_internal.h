@@ -47,7 +47,7 @@ hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
 
 // fp32 input on the single-stage register-resident kernels (widths 16 .. 8192, 3072, 6144), the
-// 12288 kernel and the 172 x 2^k kernels: each value is split into three exact bf16 terms for the
+// 16384, 12288 and 172 x 2^k kernels: each value is split into three exact bf16 terms for the
 // stage-1 products.  Returns
 // hipErrorNotSupported where that kernel has no variant; the caller then uses the generic one.
 hipError_t launch_fast_f32(int op, const KernelArgs& a, hipStream_t s);
@@ -76,6 +76,8 @@ hipError_t launch_fast2(int op, const KernelArgs& a, hipStream_t s, bool f16in =
 // 8192- and 16384-wide rows, 2 or 4 waves per row with the top index bits exchanged through LDS
 // (called by launch_fast).
 hipError_t launch_fastw(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
+// Its fp32-input form at 16384 (called by launch_fast_f32; 8192 has the single-stage kernel's).
+hipError_t launch_fastw_f32(int op, const KernelArgs& a, hipStream_t s);
 
 // Integer matrix-core inverse for KV-cache rows (64, 128, 256) with one INT4 scale per row.
 // Returns hipErrorNotSupported for other cases (the generic kernel then runs).

@@ -289,10 +289,11 @@ def test_quantise_every_width(R, n):
             check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n,tokens", [(4096, 3000), (128, 40000), (3072, 2500), (8192, 1100), (12288, 1100)])
+@pytest.mark.parametrize("n,tokens", [(4096, 3000), (128, 40000), (3072, 2500), (8192, 1100), (12288, 1100),
+                                      (16384, 600)])
 def test_fp32_input_many_rows_per_wave(R, n, tokens):
-    """fp32 input on the single-stage and 12288 kernels (three exact bf16 terms per value for stage 1, no
-    prefetch): more rows than the persistent grid, so waves take several units; INT4 g128 and
+    """fp32 input on the single-stage, 12288 and 16384 kernels (three exact bf16 terms per value for
+    stage 1, no prefetch): more rows than the persistent grid, so waves take several units; INT4 g128 and
     per-token, dynamic NVFP4 (its tensor scale over all rows) and MXFP4 on sampled rows, the
     rotation of the same rows."""
     import dataclasses
@@ -570,7 +571,7 @@ def test_special_inputs(R, kind):
         check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n", [128, 4096, 12288])
+@pytest.mark.parametrize("n", [128, 4096, 12288, 16384])
 def test_fp32_rows_near_the_normal_floor(R, n):
     """fp32 rows of magnitude 1e-35 .. 3e-38 (just above the fp32 denormal range) through the fp32
     fast paths: the three bf16 terms of each value must stay normal numbers (the matrix cores flush
