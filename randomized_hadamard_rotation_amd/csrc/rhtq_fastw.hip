@@ -38,7 +38,58 @@ struct WideShared {
   uint4 xch[W][8][64];   // [wave][quad][lane]: the half a wave sends in the current round
   float xs[W];           // [wave]: split scale S in the current round
   float rmax[W];         // [wave]: row maximum (per-token INT4) or running maximum (tensor amax)
+  float gmax[16];        // INT4 groups of whole 1024-element groups: the maximum of each (16384 only)
 };
+
+// INT4 groups of 2^(9 + BIG) elements (BIG = 1 .. 4: 1024 .. 8192) in 16384-wide rows.  After the
+// exchange rounds wave K holds the 1024-element groups j = 4 s + gfix (s = 0 .. 3, chunks 2 s and
+// 2 s + 1), so a group of 1024 is the wave's own and larger ones span two or four waves: each
+// wave reduces its 1024-groups over its lanes, they meet in LDS behind one barrier (as the
+// per-token maximum does), and every wave takes the maxima of its groups from there.
+template <int BIG, int K, typename ValF, typename BaseF>
+__device__ __forceinline__ void wide_big_groups(const KernelArgs& a, WideShared<4>& sh, const int64_t row,
+                                                const int64_t ebase, const float invS, const float cnorm,
+                                                const int lane, const int lc, ValF val, BaseF cbase) {
+  constexpr int gfix = ((K & 1) << 1) | ((K >> 1) & 1);
+  constexpr int LG = BIG - 1;          // log2 of the group in 1024-element groups
+  float m1k[4];                        // this wave's 1024-groups, true units
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 2 * st; q < 2 * st + 2; ++q)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(val(q, r)));
+    m1k[st] = group_max(m, 64) * invS;
+  }
+  if constexpr (LG > 0) {
+    if (lane == 0) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) sh.gmax[4 * st + gfix] = m1k[st];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int j0 = ((4 * st + gfix) >> LG) << LG;   // the group's first 1024-group
+      float m = sh.gmax[j0];
+#pragma unroll
+      for (int j = 1; j < (1 << LG); ++j) m = fmaxf(m, sh.gmax[j0 + j]);
+      m1k[st] = m;
+    }
+  }
+  float inv[8];
+  bool clamp = false;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const Int4Scale sc = int4_scale(m1k[st], cnorm, a.scale_dtype);
+    clamp |= sc.clamp;
+    inv[2 * st] = inv[2 * st + 1] = sc.inv * invS;
+    // the wave holding the group's first 1024-group stores its scale
+    const int j = 4 * st + gfix;
+    if (lane == 0 && (j & ((1 << LG) - 1)) == 0) store_int4_scale(a.scales, a.scale_dtype, row * (16 >> LG) + (j >> LG), sc.s);
+  }
+  int4_codes<8>(a.packed + (ebase >> 1), inv, clamp, lc, val, cbase);
+}
 
 // values: v[slot][t][t2][i].  Before round r a slot is (h << (2 - r)) | c: h holds index bits
 // 12 .. 11 + r, c the group bits of g not yet split (bits 0 .. 1 - r of g).
@@ -123,8 +174,9 @@ __device__ __forceinline__ void exchange_round(Slots& v, float& S, float& invS, 
 // Rows of the workgroup as seen by wave K (a template parameter, so that every register array
 // is indexed by constants).  All waves of the workgroup take the same rows and barriers.
 // H16: fp16 input (stage 1 on the f16 matrix-core instruction).  F32: fp32 input, each value split
-// into three exact bf16 terms for stage 1 (split3_bf16, stage1_f32).
-template <int B, int OP, int K, bool H16, bool F32>
+// into three exact bf16 terms for stage 1 (split3_bf16, stage1_f32).  BIG > 0: INT4 groups of
+// 2^(9 + BIG) elements at 16384 (wide_big_groups; a separate instantiation).
+template <int B, int OP, int K, bool H16, bool F32, int BIG>
 __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B>& sh) {
   constexpr int W = 1 << B, N = kSub << B;
   const int lane = threadIdx.x & 63;
@@ -284,6 +336,9 @@ __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B
         st_stream(p, o[0], o[1], o[2], o[3]);
         st_stream(p + 4, o[4], o[5], o[6], o[7]);
       }
+    } else if constexpr (BIG > 0) {
+      static_assert(B == 2 && OP == OP_INT4, "large groups: INT4 at 16384");
+      wide_big_groups<BIG, K>(a, sh, row, ebase, invS, cnorm, lane, lc, val, cbase);
     } else {
       quant_epilogue<OP, 8>(a, row, ebase, G, invS, cnorm, gts, inv6g, lane, lane == 0 && K == 0, val, cbase,
                             [&](float m) {
@@ -312,21 +367,30 @@ __device__ __forceinline__ void wide_rows(const KernelArgs& a, WideShared<1 << B
   }
 }
 
-template <int B, int OP, bool H16 = false, bool F32 = false>
+template <int B, int OP, bool H16 = false, bool F32 = false, int BIG = 0>
 __global__ __launch_bounds__(64 << B) void fastw_kernel(KernelArgs a) {
   __shared__ WideShared<1 << B> sh;
   const int wave = threadIdx.x >> 6;
   if constexpr (B == 1) {
-    if (wave == 0) wide_rows<B, OP, 0, H16, F32>(a, sh);
-    else wide_rows<B, OP, 1, H16, F32>(a, sh);
+    if (wave == 0) wide_rows<B, OP, 0, H16, F32, BIG>(a, sh);
+    else wide_rows<B, OP, 1, H16, F32, BIG>(a, sh);
   } else {
     switch (wave) {
-      case 0: wide_rows<B, OP, 0, H16, F32>(a, sh); break;
-      case 1: wide_rows<B, OP, 1, H16, F32>(a, sh); break;
-      case 2: wide_rows<B, OP, 2, H16, F32>(a, sh); break;
-      default: wide_rows<B, OP, 3, H16, F32>(a, sh); break;
+      case 0: wide_rows<B, OP, 0, H16, F32, BIG>(a, sh); break;
+      case 1: wide_rows<B, OP, 1, H16, F32, BIG>(a, sh); break;
+      case 2: wide_rows<B, OP, 2, H16, F32, BIG>(a, sh); break;
+      default: wide_rows<B, OP, 3, H16, F32, BIG>(a, sh); break;
     }
   }
+}
+
+template <int B, int OP, int IN, int BIG>
+hipError_t launchwk(const KernelArgs& a, hipStream_t s) {
+  auto kern = fastw_kernel<B, OP, IN == RHTQ_IN_F16, IN == RHTQ_IN_F32, BIG>;
+  static const int max_blocks = resident_blocks((const void*)kern, 64 << B, 0);
+  const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 << B), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int B, int OP, int IN>
@@ -335,13 +399,15 @@ hipError_t launchw(const KernelArgs& a, hipStream_t s) {
   if (a.sign_period != N) return hipErrorNotSupported;   // block-diagonal calls: the other kernels
   if (reinterpret_cast<uintptr_t>(a.x) & 15) return hipErrorNotSupported;
   if constexpr (OP == OP_INT4) {
+    if constexpr (B == 2) {   // groups of 1024 .. 8192 (8192: the single-stage kernel takes them)
+      if (a.group == 1024) return launchwk<B, OP, IN, 1>(a, s);
+      if (a.group == 2048) return launchwk<B, OP, IN, 2>(a, s);
+      if (a.group == 4096) return launchwk<B, OP, IN, 3>(a, s);
+      if (a.group == 8192) return launchwk<B, OP, IN, 4>(a, s);
+    }
     if (!(a.group == N || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-  auto kern = fastw_kernel<B, OP, IN == RHTQ_IN_F16, IN == RHTQ_IN_F32>;
-  static const int max_blocks = resident_blocks((const void*)kern, 64 << B, 0);
-  const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 << B), 0, s, a);
-  return hipGetLastError();
+  return launchwk<B, OP, IN, 0>(a, s);
 }
 
 template <int OP, int IN>

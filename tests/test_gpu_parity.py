@@ -413,6 +413,31 @@ def test_12288_whole_subrow_groups_many_rows(R):
         print(check_forward(R, x, s, "int4", group, "f16", y_ref=y_ref))
 
 
+def test_16384_large_groups_many_rows(R):
+    """INT4 groups of 1024 .. 8192 at width 16384 (one wave's own 1024-groups, and groups spanning
+    two or four waves, met in LDS) on more rows than the persistent grid has workgroups, with two
+    rows of magnitude 1e30 whose fp16 scales saturate; bf16, fp16 and fp32 input; fp32 and fp16
+    scales."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(WORKLOADS["llama_4096_int4"], n=16384, tokens=700)
+    xb, s = generate(w, dev())
+    xb[5] = special_rows("huge", 16384, 1, device=dev())[0]
+    xb[690] = special_rows("huge", 16384, 1, seed=8, device=dev())[0]
+    torch.cuda.synchronize()
+    for dt in ("bf16", "f16", "f32"):
+        if dt == "bf16":
+            x = xb
+        elif dt == "f16":
+            x = (xb.float() * 0.25).clamp(-6e4, 6e4).to(torch.float16)   # the 1e30 rows saturate fp16
+        else:
+            x = xb.float() * (1.0 + 2.0 ** -12)
+        y_ref = O.rotate(x.cpu(), s)
+        for group, sd in ((1024, "f16"), (2048, "f32"), (4096, "f16"), (8192, "f32")):
+            say(f"16384 int4 group={group} scale={sd} rows=700 input={dt}")
+            print(check_forward(R, x, s, "int4", group, sd, y_ref=y_ref))
+
+
 @pytest.mark.parametrize("n", [16, 32, 64])
 def test_narrow_rows_ragged_units(R, n):
     """16-, 32- and 64-wide rows share a 512-element wave unit (32, 16 or 8 rows); 4099 rows
