@@ -55,7 +55,52 @@ struct Shared24 {
   float4 xb[2][kW][kOwn][2][64];   // [slot][receiving wave][jl][half of the run][lane]
   float m1[kW];                    // stage-1 maximum of each wave
   float rmax[kW];                  // per-token row maximum of each wave
+  float cmax[kW][kSub];            // INT4 groups above 512: each wave's chunk maxima
 };
+
+// INT4 groups of 2^(9 + BIG) elements (BIG = 1 .. 4: 1024 .. 8192).  Wave H holds chunk q =
+// 2048 q + 512 H + [0, 512) of every sub-row q, so every such group spans two or four waves (and
+// from 4096 on, several sub-rows): each wave reduces its chunks over its lanes, the maxima meet
+// in LDS behind one barrier, and every wave takes its groups' maxima from there; the chunk that
+// starts a group stores its scale.  val and cbase as for quant_epilogue.
+template <int BIG, int H, typename ValF, typename BaseF>
+__device__ __forceinline__ void fast24_big_groups(const KernelArgs& a, Shared24& sh, const int64_t row,
+                                                  const int64_t relem0, const float invS, const float cnorm,
+                                                  const int lane, const int lc, ValF val, BaseF cbase) {
+  constexpr int G = 9 + BIG;
+  float cm[kSub];
+#pragma unroll
+  for (int q = 0; q < kSub; ++q) {
+    float m = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(val(q, r)));
+    cm[q] = group_max(m, 64) * invS;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < kSub; ++q) sh.cmax[H][q] = cm[q];
+  }
+  __syncthreads();
+  float inv[kSub];
+  bool clamp = false;
+#pragma unroll
+  for (int q = 0; q < kSub; ++q) {
+    // the group's chunks: sub-rows q0 .. q0 + nq - 1, waves h0 .. h0 + nh - 1
+    constexpr int nq = G <= 11 ? 1 : 1 << (G - 11), nh = G == 10 ? 2 : 4;
+    const int q0 = q & ~(nq - 1), h0 = G == 10 ? (H & 2) : 0;
+    float m = 0.0f;
+#pragma unroll
+    for (int dq = 0; dq < nq; ++dq)
+#pragma unroll
+      for (int dh = 0; dh < nh; ++dh) m = fmaxf(m, sh.cmax[h0 + dh][q0 + dq]);
+    const Int4Scale sc = int4_scale(m, cnorm, a.scale_dtype);
+    clamp |= sc.clamp;
+    inv[q] = sc.inv * invS;
+    const int e = kM * q + 512 * H;   // the chunk's first element
+    if (lane == 0 && (e & ((1 << G) - 1)) == 0) store_int4_scale(a.scales, a.scale_dtype, (relem0 + e) >> G, sc.s);
+  }
+  int4_codes<kSub>(a.packed + (relem0 >> 1), inv, clamp, lc, val, cbase);
+}
 
 // Sign bits of one own sub-row, one word per lane: the value the lane loads as element e of
 // fragment f (dword k = e >> 1 of the 16-byte load) has its bit at 4 f + k, plus 16 for the
@@ -98,7 +143,7 @@ __device__ __forceinline__ f32x4 stage1(const uint4& r, const bf16x8& hbt) {
 
 // Rows of the workgroup as seen by wave H (a template parameter, so that every register
 // array is indexed by constants).  All four waves pass the same barriers in the same order.
-template <int OP, int H, bool H16>
+template <int OP, int H, bool H16, int BIG>
 __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, const bf16x8 (&hb)[2],
                                             const f16x8 (&hc)[2], const uint32_t (&sb)[kOwn], const int lane,
                                             const float gts, const float inv6g, const int G) {
@@ -277,6 +322,8 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
         st_stream(p, o[0], o[1], o[2], o[3]);
         st_stream(p + 4, o[4], o[5], o[6], o[7]);
       }
+    } else if constexpr (BIG > 0) {
+      fast24_big_groups<BIG, H>(a, sh, row, relem0, invS, cnorm, lane, lc, val, cbase);
     } else {
       // per-token INT4: maximum of the whole row across the four waves (uniform branch)
       auto rowmax = [&](float m) -> float {
@@ -302,7 +349,8 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
 }
 
 // H16: fp16 input (stage 1 on the f16 matrix-core instruction).
-template <int OP, bool H16 = false>
+// BIG > 0: INT4 groups of 2^(9 + BIG) elements (a separate instantiation).
+template <int OP, bool H16 = false, int BIG = 0>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fast24_kernel(KernelArgs a) {
   __shared__ Shared24 sh;
   const int lane = threadIdx.x & 63;
@@ -324,24 +372,33 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fa
   if constexpr (OP == OP_NVFP4) G = 4;
   if constexpr (OP == OP_MXFP4) G = 5;
   switch (h) {
-    case 0: fast24_rows<OP, 0, H16>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    case 1: fast24_rows<OP, 1, H16>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    case 2: fast24_rows<OP, 2, H16>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    default: fast24_rows<OP, 3, H16>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 0: fast24_rows<OP, 0, H16, BIG>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 1: fast24_rows<OP, 1, H16, BIG>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 2: fast24_rows<OP, 2, H16, BIG>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    default: fast24_rows<OP, 3, H16, BIG>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
   }
+}
+
+template <int OP, bool H16, int BIG>
+hipError_t launch24k(const KernelArgs& a, hipStream_t s) {
+  auto kern = fast24_kernel<OP, H16, BIG>;
+  static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
+  const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int OP, bool H16>
 hipError_t launch24(const KernelArgs& a, hipStream_t s) {
   if (a.sign_period != kN) return hipErrorNotSupported;
   if constexpr (OP == OP_INT4) {
+    if (a.group == 1024) return launch24k<OP, H16, 1>(a, s);
+    if (a.group == 2048) return launch24k<OP, H16, 2>(a, s);
+    if (a.group == 4096) return launch24k<OP, H16, 3>(a, s);
+    if (a.group == 8192) return launch24k<OP, H16, 4>(a, s);
     if (!(a.group == kN || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-  auto kern = fast24_kernel<OP, H16>;
-  static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
-  const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
-  return hipGetLastError();
+  return launch24k<OP, H16, 0>(a, s);
 }
 
 template <bool H16>

@@ -438,6 +438,24 @@ def test_16384_large_groups_many_rows(R):
             print(check_forward(R, x, s, "int4", group, sd, y_ref=y_ref))
 
 
+def test_24576_large_groups_many_rows(R):
+    """INT4 groups of 1024 .. 8192 at width 24576 (each spans two or four waves, met in LDS) on more
+    rows than the persistent grid has workgroups, with a row of magnitude 1e30 whose fp16 scales
+    saturate; bf16 and fp16 input; fp32 and fp16 scales."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(WORKLOADS["llama_4096_int4"], n=24576, tokens=600)
+    xb, s = generate(w, dev())
+    xb[591] = special_rows("huge", 24576, 1, device=dev())[0]
+    torch.cuda.synchronize()
+    for dt in ("bf16", "f16"):
+        x = xb if dt == "bf16" else (xb.float() * 0.25).clamp(-6e4, 6e4).to(torch.float16)
+        y_ref = O.rotate(x.cpu(), s)
+        for group, sd in ((1024, "f32"), (2048, "f16"), (4096, "f32"), (8192, "f16")):
+            say(f"24576 int4 group={group} scale={sd} rows=600 input={dt}")
+            print(check_forward(R, x, s, "int4", group, sd, y_ref=y_ref))
+
+
 @pytest.mark.parametrize("n", [16, 32, 64])
 def test_narrow_rows_ragged_units(R, n):
     """16-, 32- and 64-wide rows share a 512-element wave unit (32, 16 or 8 rows); 4099 rows
