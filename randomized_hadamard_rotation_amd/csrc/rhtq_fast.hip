@@ -577,6 +577,7 @@ hipError_t launch_fast_f32(int op, const KernelArgs& a, hipStream_t s) {
   if (a.n == 12288) return launch_fast12_f32(op, a, s);
   if (a.n == 22016 || a.n == 11008 || a.n == 5504 || a.n == 2752) return launch_fast172_f32(op, a, s);
   if (a.n == 16384) return launch_fastw_f32(op, a, s);
+  if (a.n == 24576) return launch_fast24_f32(op, a, s);
   return dispatch_op<RHTQ_IN_F32>(op, a, s);
 }
 

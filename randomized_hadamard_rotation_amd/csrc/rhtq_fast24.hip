@@ -143,7 +143,10 @@ __device__ __forceinline__ f32x4 stage1(const uint4& r, const bf16x8& hbt) {
 
 // Rows of the workgroup as seen by wave H (a template parameter, so that every register
 // array is indexed by constants).  All four waves pass the same barriers in the same order.
-template <int OP, int H, bool H16, int BIG>
+// F32: fp32 input.  Each value is split into three exact bf16 terms for stage 1 (split3_bf16,
+// stage1_f32); the registers cannot hold the fp32 sub-rows between the two stage-1 passes, so
+// each pass loads its sub-row when it needs it (no prefetch).
+template <int OP, int H, bool H16, int BIG, bool F32>
 __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, const bf16x8 (&hb)[2],
                                             const f16x8 (&hc)[2], const uint32_t (&sb)[kOwn], const int lane,
                                             const float gts, const float inv6g, const int G) {
@@ -167,29 +170,71 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
         }
     }
   };
-  load(blockIdx.x, 0, kPf);
+  if constexpr (!F32) load(blockIdx.x, 0, kPf);
+  const float* xf = static_cast<const float*>(a.x);
+  // fp32 input: stage 1 of own sub-row jl of row r, loaded here
+  auto stage1_f32_sub = [&](int64_t r, int jl, float (&d)[kNF][2][4]) {
+    uint4 r32[kNF][2];
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) {
+      const float* p = xf + r * kN + load_off(h, jl, f, lane);
+      r32[f][0] = ld_stream(p);
+      r32[f][1] = ld_stream(p + 4);
+    }
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) {
+      uint32_t th[4], tm[4], tl[4];
+      split3_bf16(r32[f][0], r32[f][1], th, tm, tl);
+      const uint4 mk = sign_masks(sb[jl], f);   // the signs flip every term
+      const uint32_t m4[4] = {mk.x, mk.y, mk.z, mk.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { th[k] ^= m4[k]; tm[k] ^= m4[k]; tl[k] ^= m4[k]; }
+      bf16x8 ah, am, al;
+      __builtin_memcpy(&ah, th, 16);
+      __builtin_memcpy(&am, tm, 16);
+      __builtin_memcpy(&al, tl, 16);
+      const f32x4 p0 = stage1_f32(ah, am, al, hb[0]);
+      const f32x4 p1 = stage1_f32(ah, am, al, hb[1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { d[f][0][i] = p0[i]; d[f][1][i] = p1[i]; }
+    }
+  };
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const int64_t relem0 = row * kN;
-    load(row, kPf, kOwn);
+    if constexpr (!F32) load(row, kPf, kOwn);
     // ---------------- stage 1: bits 0-4 ----------------
     // A first pass only takes the maximum: the split scale must exist before the first split,
     // and holding all 96 stage-1 values until then would leave room for one wave per SIMD.
     // The signed inputs stay in raw, and each sub-row's stage 1 is recomputed just before its
     // split (24 more matrix-core operations per row, on a unit with time to spare).
     float m1 = 0.0f;
+    if constexpr (F32) {
 #pragma unroll
-    for (int jl = 0; jl < kOwn; ++jl)
+      for (int jl = 0; jl < kOwn; ++jl) {
+        float d[kNF][2][4];
+        stage1_f32_sub(row, jl, d);
 #pragma unroll
-      for (int f = 0; f < kNF; ++f) {
-        uint4& r = raw[jl][f];
-        const uint4 mk = sign_masks(sb[jl], f);
-        r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
-        const f32x4 p0 = stage1<H16>(r, hb[0]);
-        const f32x4 p1 = stage1<H16>(r, hb[1]);
+        for (int f = 0; f < kNF; ++f)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fmaxf(fabsf(p0[i]), fabsf(p1[i])));
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fabsf(d[f][t][i]));
       }
+    } else {
+#pragma unroll
+      for (int jl = 0; jl < kOwn; ++jl)
+#pragma unroll
+        for (int f = 0; f < kNF; ++f) {
+          uint4& r = raw[jl][f];
+          const uint4 mk = sign_masks(sb[jl], f);
+          r.x ^= mk.x; r.y ^= mk.y; r.z ^= mk.z; r.w ^= mk.w;
+          const f32x4 p0 = stage1<H16>(r, hb[0]);
+          const f32x4 p1 = stage1<H16>(r, hb[1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m1 = fmaxf(m1, fmaxf(fabsf(p0[i]), fabsf(p1[i])));
+        }
+    }
     m1 = group_max(m1, 64);
     if (lane == 0) sh.m1[h] = m1;
     __syncthreads();   // every wave's maximum is in; the previous row's exchange reads are done
@@ -202,12 +247,16 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
 #pragma unroll
     for (int jl = 0; jl < kOwn; ++jl) {
       float d1[kNF][2][4];   // [f][t][i]: stage 1 of this sub-row again
+      if constexpr (F32) {
+        stage1_f32_sub(row, jl, d1);
+      } else {
 #pragma unroll
-      for (int f = 0; f < kNF; ++f) {
-        const f32x4 p0 = stage1<H16>(raw[jl][f], hb[0]);
-        const f32x4 p1 = stage1<H16>(raw[jl][f], hb[1]);
+        for (int f = 0; f < kNF; ++f) {
+          const f32x4 p0 = stage1<H16>(raw[jl][f], hb[0]);
+          const f32x4 p1 = stage1<H16>(raw[jl][f], hb[1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { d1[f][0][i] = p0[i]; d1[f][1][i] = p1[i]; }
+          for (int i = 0; i < 4; ++i) { d1[f][0][i] = p0[i]; d1[f][1][i] = p1[i]; }
+        }
       }
       // ---------------- stage 2: bits 5-9 of each 1024-half ----------------
       // d2[hf][t][t2][i2]: element 1024 hf + 512 t2 + 8 lc + t + 2 i2 of the sub-row
@@ -265,7 +314,7 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
     }
     // the next row's loads go out once stage 1's values are consumed (registers allow no
     // earlier start) and run during the exchange, the order-12 factor and the epilogue
-    load(row + gridDim.x, 0, kPf);
+    if constexpr (!F32) load(row + gridDim.x, 0, kPf);
     auto take = [&](int slot, int j1, int jl) {
       const float4 u = sh.xb[slot][h][jl][0][lane];
       const float4 v = sh.xb[slot][h][jl][1][lane];
@@ -349,8 +398,8 @@ __device__ __forceinline__ void fast24_rows(const KernelArgs& a, Shared24& sh, c
 }
 
 // H16: fp16 input (stage 1 on the f16 matrix-core instruction).
-// BIG > 0: INT4 groups of 2^(9 + BIG) elements (a separate instantiation).
-template <int OP, bool H16 = false, int BIG = 0>
+// BIG > 0: INT4 groups of 2^(9 + BIG) elements (a separate instantiation).  F32: fp32 input.
+template <int OP, bool H16 = false, int BIG = 0, bool F32 = false>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fast24_kernel(KernelArgs a) {
   __shared__ Shared24 sh;
   const int lane = threadIdx.x & 63;
@@ -372,43 +421,43 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2))) void fa
   if constexpr (OP == OP_NVFP4) G = 4;
   if constexpr (OP == OP_MXFP4) G = 5;
   switch (h) {
-    case 0: fast24_rows<OP, 0, H16, BIG>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    case 1: fast24_rows<OP, 1, H16, BIG>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    case 2: fast24_rows<OP, 2, H16, BIG>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
-    default: fast24_rows<OP, 3, H16, BIG>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 0: fast24_rows<OP, 0, H16, BIG, F32>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 1: fast24_rows<OP, 1, H16, BIG, F32>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    case 2: fast24_rows<OP, 2, H16, BIG, F32>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
+    default: fast24_rows<OP, 3, H16, BIG, F32>(a, sh, hb, hc, sb, lane, gts, inv6g, G); break;
   }
 }
 
-template <int OP, bool H16, int BIG>
+template <int OP, int IN, int BIG>
 hipError_t launch24k(const KernelArgs& a, hipStream_t s) {
-  auto kern = fast24_kernel<OP, H16, BIG>;
+  auto kern = fast24_kernel<OP, IN == RHTQ_IN_F16, BIG, IN == RHTQ_IN_F32>;
   static const int max_blocks = resident_blocks((const void*)kern, kT, 0);
   const int grid = (int)(a.rows < max_blocks ? a.rows : max_blocks);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int OP, bool H16>
+template <int OP, int IN>
 hipError_t launch24(const KernelArgs& a, hipStream_t s) {
   if (a.sign_period != kN) return hipErrorNotSupported;
   if constexpr (OP == OP_INT4) {
-    if (a.group == 1024) return launch24k<OP, H16, 1>(a, s);
-    if (a.group == 2048) return launch24k<OP, H16, 2>(a, s);
-    if (a.group == 4096) return launch24k<OP, H16, 3>(a, s);
-    if (a.group == 8192) return launch24k<OP, H16, 4>(a, s);
+    if (a.group == 1024) return launch24k<OP, IN, 1>(a, s);
+    if (a.group == 2048) return launch24k<OP, IN, 2>(a, s);
+    if (a.group == 4096) return launch24k<OP, IN, 3>(a, s);
+    if (a.group == 8192) return launch24k<OP, IN, 4>(a, s);
     if (!(a.group == kN || (a.group >= 16 && a.group <= 512))) return hipErrorNotSupported;
   }
-  return launch24k<OP, H16, 0>(a, s);
+  return launch24k<OP, IN, 0>(a, s);
 }
 
-template <bool H16>
+template <int IN>
 hipError_t launch24_op(int op, const KernelArgs& a, hipStream_t s) {
   switch (op) {
-    case OP_ROTATE: return launch24<OP_ROTATE, H16>(a, s);
-    case OP_INT4: return launch24<OP_INT4, H16>(a, s);
-    case OP_NVFP4: return launch24<OP_NVFP4, H16>(a, s);
-    case OP_MXFP4: return launch24<OP_MXFP4, H16>(a, s);
-    case OP_AMAX: return launch24<OP_AMAX, H16>(a, s);
+    case OP_ROTATE: return launch24<OP_ROTATE, IN>(a, s);
+    case OP_INT4: return launch24<OP_INT4, IN>(a, s);
+    case OP_NVFP4: return launch24<OP_NVFP4, IN>(a, s);
+    case OP_MXFP4: return launch24<OP_MXFP4, IN>(a, s);
+    case OP_AMAX: return launch24<OP_AMAX, IN>(a, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -416,7 +465,11 @@ hipError_t launch24_op(int op, const KernelArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fast24(int op, const KernelArgs& a, hipStream_t s, bool f16in) {
-  return f16in ? launch24_op<true>(op, a, s) : launch24_op<false>(op, a, s);
+  return f16in ? launch24_op<RHTQ_IN_F16>(op, a, s) : launch24_op<RHTQ_IN_BF16>(op, a, s);
+}
+
+hipError_t launch_fast24_f32(int op, const KernelArgs& a, hipStream_t s) {
+  return launch24_op<RHTQ_IN_F32>(op, a, s);
 }
 
 }  // namespace rhtq

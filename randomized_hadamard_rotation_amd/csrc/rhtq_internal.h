@@ -47,7 +47,7 @@ hipError_t launch_generic(int op, int in_dtype, const KernelArgs& a, hipStream_t
 hipError_t launch_fast(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
 
 // fp32 input on the single-stage register-resident kernels (widths 16 .. 8192, 3072, 6144), the
-// 16384, 12288 and 172 x 2^k kernels: each value is split into three exact bf16 terms for the
+// 16384, 12288, 24576 and 172 x 2^k kernels: each value is split into three exact bf16 terms for the
 // stage-1 products.  Returns
 // hipErrorNotSupported where that kernel has no variant; the caller then uses the generic one.
 hipError_t launch_fast_f32(int op, const KernelArgs& a, hipStream_t s);
@@ -63,6 +63,7 @@ int64_t fast12_grid(int64_t rows);
 
 // Four-wave kernel for 24576-wide rows, H12 (x) H2048 (called by launch_fast).
 hipError_t launch_fast24(int op, const KernelArgs& a, hipStream_t s, bool f16in = false);
+hipError_t launch_fast24_f32(int op, const KernelArgs& a, hipStream_t s);   // fp32 input
 
 // Matrix-core kernel for 11008-wide rows, H172 (x) H64, and 5504, 2752, 22016 (called by
 // launch_fast), and its fp32-input form (called by launch_fast_f32: three exact bf16 terms per

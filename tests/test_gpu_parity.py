@@ -290,10 +290,10 @@ def test_quantise_every_width(R, n):
 
 
 @pytest.mark.parametrize("n,tokens", [(4096, 3000), (128, 40000), (3072, 2500), (8192, 1100), (12288, 1100),
-                                      (16384, 600)])
+                                      (16384, 600), (24576, 600)])
 def test_fp32_input_many_rows_per_wave(R, n, tokens):
-    """fp32 input on the single-stage, 12288 and 16384 kernels (three exact bf16 terms per value for
-    stage 1, no prefetch): more rows than the persistent grid, so waves take several units; INT4 g128 and
+    """fp32 input on the single-stage, 12288, 16384 and 24576 kernels (three exact bf16 terms per value
+    for stage 1, no prefetch): more rows than the persistent grid, so waves take several units; INT4 g128 and
     per-token, dynamic NVFP4 (its tensor scale over all rows) and MXFP4 on sampled rows, the
     rotation of the same rows."""
     import dataclasses
@@ -441,15 +441,20 @@ def test_16384_large_groups_many_rows(R):
 def test_24576_large_groups_many_rows(R):
     """INT4 groups of 1024 .. 8192 at width 24576 (each spans two or four waves, met in LDS) on more
     rows than the persistent grid has workgroups, with a row of magnitude 1e30 whose fp16 scales
-    saturate; bf16 and fp16 input; fp32 and fp16 scales."""
+    saturate; bf16, fp16 and fp32 input; fp32 and fp16 scales."""
     import dataclasses
     import torch
     w = dataclasses.replace(WORKLOADS["llama_4096_int4"], n=24576, tokens=600)
     xb, s = generate(w, dev())
     xb[591] = special_rows("huge", 24576, 1, device=dev())[0]
     torch.cuda.synchronize()
-    for dt in ("bf16", "f16"):
-        x = xb if dt == "bf16" else (xb.float() * 0.25).clamp(-6e4, 6e4).to(torch.float16)
+    for dt in ("bf16", "f16", "f32"):
+        if dt == "bf16":
+            x = xb
+        elif dt == "f16":
+            x = (xb.float() * 0.25).clamp(-6e4, 6e4).to(torch.float16)
+        else:
+            x = xb.float() * (1.0 + 2.0 ** -12)
         y_ref = O.rotate(x.cpu(), s)
         for group, sd in ((1024, "f32"), (2048, "f16"), (4096, "f32"), (8192, "f16")):
             say(f"24576 int4 group={group} scale={sd} rows=600 input={dt}")
@@ -614,7 +619,7 @@ def test_special_inputs(R, kind):
         check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
-@pytest.mark.parametrize("n", [128, 4096, 12288, 16384])
+@pytest.mark.parametrize("n", [128, 4096, 12288, 16384, 24576])
 def test_fp32_rows_near_the_normal_floor(R, n):
     """fp32 rows of magnitude 1e-35 .. 3e-38 (just above the fp32 denormal range) through the fp32
     fast paths: the three bf16 terms of each value must stay normal numbers (the matrix cores flush
