@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 CACHE_DEFEAT_BYTES = 512 << 20
 HEADLINE = "llama_4096_int4"
 OTHERS = ["downproj_12288_int4g128", "kv_128_int4g128", "nvfp4_4096", "mxfp4_4096", "blockh128_4096_int4g128",
-          "downproj7b_11008_int4g128", "wide172_22016_int4g128", "llama_4096_int4_f16"]
+          "downproj7b_11008_int4g128", "wide172_22016_int4g128", "llama_4096_int4_f16", "llama_4096_int4_f32"]
 KERNEL_SOURCES = ["randomized_hadamard_rotation_amd/csrc/rhtq_fast.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast12.hip",
                   "randomized_hadamard_rotation_amd/csrc/rhtq_fast24.hip",

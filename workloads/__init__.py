@@ -81,6 +81,10 @@ WORKLOADS = {
     "llama_4096_int4_f16": Workload(
         "llama_4096_int4_f16", 2048, 4096, "f16", "llama_like", 2, 0, "int4", 0, "f32",
         description="2048 x 4096 fp16, the llama-like recipe x 1/4; per-token INT4, fp32 scale"),
+    # the headline shape with fp32 input: each value split into three exact bf16 terms for stage 1
+    "llama_4096_int4_f32": Workload(
+        "llama_4096_int4_f32", 2048, 4096, "f32", "llama_like", 2, 0, "int4", 0, "f32",
+        description="2048 x 4096 fp32, the llama-like recipe; per-token INT4, fp32 scale"),
     "downproj_12288_int4g128": Workload(
         "downproj_12288_int4g128", 8192, 12288, "bf16", "llama_like", 3, 0, "int4", 128, "f16",
         description="8192 x 12288 bf16 (H12 x H1024), same value recipe; INT4 group 128, fp16 scales"),
