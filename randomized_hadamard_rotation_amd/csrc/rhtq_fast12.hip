@@ -85,6 +85,41 @@ __device__ __forceinline__ void fast12_whole_subrow_groups(const KernelArgs& a, 
   int4_codes<kSub>(a.packed + (relem0 >> 1), inv, clamp, lc, val, cbase);
 }
 
+// The order-12 factor (h12_forward) on values of which the other wave's six sub-rows are still in
+// that wave's units: their factor rho (a power of two) enters the column sums once and otherwise
+// rides on additions the array already needs, as fused multiply-adds, instead of one multiply per
+// received value.  Scaling by a power of two is exact, so the results equal h12_forward of the
+// rescaled values (each rounding step is the same one on a scaled operand).  Wave 0 owns blocks 0-1 (j1 < 6) and receives blocks 2-3, wave 1 the reverse.
+template <int H>
+__device__ __forceinline__ void h12_forward_rho(float* w, const float rho) {
+  float s1 = w[0] + w[1] + w[2];
+  float s2 = w[3] + w[4] + w[5];
+  float s3 = w[6] + w[7] + w[8];
+  float s4 = w[9] + w[10] + w[11];
+  if constexpr (H == 0) { s3 *= rho; s4 *= rho; } else { s1 *= rho; s2 *= rho; }
+  const float pa = s1 + s3, pb = s2 + s4, pc = s2 - s4, pd = s3 - s1;
+  const float t1 = pa + pb, t2 = pb - pa, t3 = pc + pd, t4 = pd - pc;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const float v1 = w[k], v2 = w[3 + k], v3 = w[6 + k], v4 = w[9 + k];
+    if constexpr (H == 0) {   // v3, v4 received
+      const float s34 = v3 + v4, d34 = v3 - v4, s12 = v1 + v2;
+      const float d24 = __builtin_fmaf(-rho, v4, v2);
+      w[k] = __builtin_fmaf(-2.0f, __builtin_fmaf(rho, s34, v2), t1);     // -2 (v2 + v3 + v4)
+      w[3 + k] = __builtin_fmaf(2.0f, __builtin_fmaf(rho, d34, v1), t2);  // +2 (v1 + v3 - v4)
+      w[6 + k] = __builtin_fmaf(2.0f, v1 - d24, t3);                      // +2 (v1 - v2 + v4)
+      w[9 + k] = __builtin_fmaf(2.0f, __builtin_fmaf(-rho, v3, s12), t4); // +2 (v1 + v2 - v3)
+    } else {                  // v1, v2 received
+      const float s34 = v3 + v4, d34 = v3 - v4, s12 = v1 + v2;
+      const float d24 = __builtin_fmaf(rho, v2, -v4);
+      w[k] = __builtin_fmaf(-2.0f, __builtin_fmaf(rho, v2, s34), t1);
+      w[3 + k] = __builtin_fmaf(2.0f, __builtin_fmaf(rho, v1, d34), t2);
+      w[6 + k] = __builtin_fmaf(2.0f, __builtin_fmaf(rho, v1, -d24), t3);
+      w[9 + k] = __builtin_fmaf(2.0f, __builtin_fmaf(rho, s12, -v3), t4);
+    }
+  }
+}
+
 // Rows of the workgroup as seen by wave H (a template parameter, so that every register
 // array is indexed by constants).  Both waves pass the same barriers in the same order.
 template <int OP, int H, int PER, bool F32, bool H16>
@@ -218,10 +253,13 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
 #pragma unroll
       for (int jl = 0; jl < kOwn; ++jl)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[kOwn * other + jl][t][i] = sh.xbuf[other][jl * 4 + i][lane] * rho;
+        for (int i = 0; i < 4; ++i) w[kOwn * other + jl][t][i] = sh.xbuf[other][jl * 4 + i][lane];
     }
+    // keep the order-12 factor after both exchange steps: scheduled between them it lengthens the
+    // stretch between barriers that the other wave waits on
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---------------- order-12 factor ----------------
+    // ---------------- order-12 factor (the received half rescaled by rho on the way) ----------------
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -229,7 +267,7 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
         float v[kSub];
 #pragma unroll
         for (int j1 = 0; j1 < kSub; ++j1) v[j1] = w[j1][t][i];
-        h12_forward(v);
+        h12_forward_rho<H>(v, rho);
 #pragma unroll
         for (int j1 = 0; j1 < kSub; ++j1) w[j1][t][i] = v[j1];
       }
