@@ -65,7 +65,7 @@ def _host(t):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", list(CASES))
-def test_workload_every_row(R, pool, name):
+def test_workload_every_row(R, pool, name, request):
     import torch
     w = WORKLOADS[name]
     say(f"{name} every row: {w.tokens} x {w.n} {w.fmt} group={w.group} scale={w.scale_dtype}"
@@ -114,3 +114,12 @@ def test_workload_every_row(R, pool, name):
         tot[k]["mismatch_fraction"] = tot[k]["code_mismatches"] / tot["codes"]
     assert tot["rot_max_rel_err"] <= C.ROT_REL
     print(f"[fullsize] {name}: {tot}", flush=True)
+    parts = [f"{name} {w.tokens}x{w.n}: {tot['codes']} codes"]
+    for k in outs:
+        parts.append(f"{k} mismatches {tot[k]['code_mismatches']} ({tot[k]['mismatch_fraction']:.1e}), "
+                     f"scale boundary cases {tot[k]['scale_boundary_cases']}")
+    parts.append(f"worst R1 {tot['rot_max_rel_err']:.2e}")
+    if "tensor_scale" in tot:
+        ts = tot["tensor_scale"]
+        parts.append(f"g rel diff {abs(ts['device'] - ts['oracle']) / ts['oracle']:.1e}")
+    request.config.fullsize_lines.append("; ".join(parts))
