@@ -239,7 +239,7 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[kOwn * h + jl][t][i] = d2[jl][t][h][i];
-    float rho = 1.0f;
+    float rho = 1.0f, xso = 1.0f;   // xso: the other wave's inverse split scale
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       __syncthreads();   // the other wave has read the previous contents of xbuf
@@ -249,11 +249,30 @@ __device__ __forceinline__ void fast12_rows(const KernelArgs& a, Shared12& sh, c
         for (int i = 0; i < 4; ++i) sh.xbuf[h][jl * 4 + i][lane] = d2[jl][t][other][i];
       if (t == 0 && lane == 0) sh.xs[h] = invS;
       __syncthreads();
-      if (t == 0) rho = S * sh.xs[other];   // ratio of two powers of two: exact
+      if (t == 0) {
+        xso = sh.xs[other];
+        rho = S * xso;   // ratio of two powers of two: exact (or out of range, handled below)
+      }
 #pragma unroll
       for (int jl = 0; jl < kOwn; ++jl)
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[kOwn * other + jl][t][i] = sh.xbuf[other][jl * 4 + i][lane];
+    }
+    // rho takes the received half into this wave's units.  Where that half is far larger (rho
+    // above 2^40; a dynamic range above about 2^108 between the halves would take it past fp32's
+    // range), this wave works in the other wave's units instead: its own values go down by 1/rho
+    // (a power of two, or to zero below fp32's range, far under the received half's rounding).
+    // The branch is uniform.
+    if (rho > 0x1p40f) {
+      const float down = __builtin_amdgcn_rcpf(rho);
+#pragma unroll
+      for (int jl = 0; jl < kOwn; ++jl)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[kOwn * h + jl][t][i] *= down;
+      rho = 1.0f;
+      invS = xso;
     }
     // keep the order-12 factor after both exchange steps: scheduled between them it lengthens the
     // stretch between barriers that the other wave waits on

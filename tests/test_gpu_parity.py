@@ -619,6 +619,31 @@ def test_special_inputs(R, kind):
         check_forward(R, x, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
 
 
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+def test_12288_halves_far_apart(R, in_dtype):
+    """12288-wide rows whose halves (sub-rows 0-5 and 6-11, the shares of the kernel's two waves)
+    differ in magnitude by about 2^116 or 2^60, in both orders, plus an ordinary row: taking the
+    larger half into the smaller half's units must not leave fp32's range, and the rotation and
+    codes must match the oracle (which keeps the tiny half's negligible contribution exactly)."""
+    import torch
+    n = 12288
+    s = splitmix64_signs(12, n)
+    g = torch.Generator().manual_seed(121)
+    x = torch.randn(5, n, generator=g, dtype=torch.float64)
+    for r, (lo, hi) in enumerate([(1e-20, 1e15), (1e15, 1e-20), (1e-9, 1e9), (1e9, 1e-9)]):
+        x[r, : n // 2] *= lo
+        x[r, n // 2:] *= hi
+    x = x.to(torch.bfloat16 if in_dtype == "bf16" else torch.float32)
+    say(f"12288 halves far apart, {in_dtype}")
+    y_ref = O.rotate(x, s)
+    xd = x.to(dev())
+    C.check_rotation(to_np(R.rhtq_rotate(xd, s)), y_ref)
+    check_forward(R, xd, s, "int4", 128, "f32", y_ref=y_ref)
+    check_forward(R, xd, s, "int4", 0, "f32", y_ref=y_ref)
+    check_forward(R, xd, s, "mxfp4", 32, "e8m0", y_ref=y_ref)
+    check_forward(R, xd, s, "nvfp4", 16, "e4m3", y_ref=y_ref)
+
+
 @pytest.mark.parametrize("n", [128, 4096, 12288, 16384, 24576])
 def test_fp32_rows_near_the_normal_floor(R, n):
     """fp32 rows of magnitude 1e-35 .. 3e-38 (just above the fp32 denormal range) through the fp32
