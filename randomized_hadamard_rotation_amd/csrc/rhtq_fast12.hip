@@ -14,8 +14,10 @@
 //     per sub-row and per half t2 = j2 bit 9, eight consecutive outputs.
 //  3. Exchange through LDS: wave h keeps the half t2 = h of every sub-row, so it sends
 //     its other half (48 values per lane, in two steps) and receives the other wave's
-//     half t2 = h of the six sub-rows it lacks, rescaled to its own S.
-//  4. The order-12 Williamson factor in registers across the twelve sub-rows.
+//     half t2 = h of the six sub-rows it lacks, in the other wave's units.
+//  4. The order-12 Williamson factor in registers across the twelve sub-rows, taking the
+//     received half into this wave's units on the way (or, where that half is far larger,
+//     this wave's own half into the other wave's units, so that nothing is scaled up).
 //  5. Epilogue on the twelve 512-element chunks 1024 j1 + 512 h + [0, 512): group
 //     maxima, scales, INT4 or E2M1 codes, packed stores straight from registers.
 #include <hip/hip_fp16.h>
